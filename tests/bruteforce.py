@@ -1,0 +1,107 @@
+"""Independent numpy brute force of MSA, for pinning the oracle on tiny inputs.
+
+Written from the definition in a different form than the oracle: the paged
+cache is first gathered into logical per-sequence arrays, token scores are one
+matrix product, block pooling is a reshape + max, TopK is a full sort by
+(score descending, block ascending), and attention is a vectorised softmax.
+It shares no code with ``oracle/`` and must not import it.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+def logical(case, s: int, length: int):
+    """Gather sequence s's first ``length`` tokens: K,V [Hkv][L][D], IK [L][d_i]."""
+    sh, cache = case.shape, case.cache
+    B = sh.block_size
+    nb = (length + B - 1) // B
+    pages = cache.block_table[s, :nb].cpu().numpy().astype(np.int64)
+    k = f64(cache.k)[pages]                      # [nb][Hkv][B][D]
+    v = f64(cache.v)[pages]                      # [nb][Hkv][D][B]
+    ik = f64(cache.idx_k)[pages]                 # [nb][B][d_i]
+    K = k.transpose(1, 0, 2, 3).reshape(sh.num_kv_heads, nb * B, sh.head_dim)[:, :length]
+    V = v.transpose(1, 0, 3, 2).reshape(sh.num_kv_heads, nb * B, sh.head_dim)[:, :length]
+    IK = ik.reshape(nb * B, sh.idx_dim)[:length]
+    return K, V, IK
+
+
+def topk_sorted(scores: np.ndarray, own: int, k: int) -> np.ndarray:
+    order = sorted(range(own), key=lambda b: (-scores[b], b))
+    keep = sorted(order[:min(k - 1, own)] + [own])
+    return np.array(keep + [-1] * (k - len(keep)), dtype=np.int32)
+
+
+def pool_blocks(tok_scores: np.ndarray, own: int, B: int) -> np.ndarray:
+    """tok_scores [rows][L] -> per-block max over rows and tokens, blocks < own."""
+    if own == 0:
+        return np.zeros(0)
+    return tok_scores[:, :own * B].reshape(tok_scores.shape[0], own, B).max(axis=(0, 2))
+
+
+def softmax_attend(qv: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    z = scale * (K @ qv)
+    w = np.exp(z - z.max())
+    return (w / w.sum()) @ V
+
+
+def tokens_of(sel: np.ndarray, B: int, last_pos: int) -> np.ndarray:
+    toks = [np.arange(b * B, (b + 1) * B) for b in sel if b >= 0]
+    t = np.concatenate(toks)
+    return t[t <= last_pos]
+
+
+def decode(case):
+    sh = case.shape
+    B, H, G, k = sh.block_size, sh.num_kv_heads, sh.group_size, sh.top_k
+    outs, sels, pools = [], [], []
+    for s, L in enumerate(case.lengths):
+        K, V, IK = logical(case, s, L)
+        own = (L - 1) // B
+        qi = f64(case.idx_q[s])                          # [Hkv][n_i][d_i]
+        sc = qi @ IK.T                                   # [Hkv][n_i][L]
+        pooled = [pool_blocks(sc[g], own, B) for g in range(H)]
+        sel = np.stack([topk_sorted(pooled[g], own, k) for g in range(H)])
+        q = f64(case.q[s])
+        out = np.stack([softmax_attend(q[j], K[j // G][tokens_of(sel[j // G], B, L - 1)],
+                                       V[j // G][tokens_of(sel[j // G], B, L - 1)],
+                                       sh.softmax_scale)
+                        for j in range(sh.num_q_heads)])
+        outs.append(out)
+        sels.append(sel)
+        pools.append(pooled)
+    return {"out": np.stack(outs), "sel": np.stack(sels), "pooled": pools}
+
+
+def prefill(case):
+    sh = case.shape
+    B, H, G, k = sh.block_size, sh.num_kv_heads, sh.group_size, sh.top_k
+    P, C = case.prior_len, case.chunk_len
+    K, V, IK = logical(case, 0, P + C)
+    qi = f64(case.idx_q)                                 # [C][Hkv][n_i][d_i]
+    q = f64(case.q)
+    first = P // B
+    out = np.zeros((C, sh.num_q_heads, sh.head_dim))
+    sels, pools = [], []
+    for tau in range(case.num_tiles):
+        own = first + tau
+        q0, q1 = max(0, own * B - P), min(C, (own + 1) * B - P)
+        sel_t, pool_t = [], []
+        for g in range(H):
+            rows = qi[q0:q1, g].reshape(-1, sh.idx_dim)  # tile queries x heads
+            pooled = pool_blocks(rows @ IK.T, own, B)
+            sel_t.append(topk_sorted(pooled, own, k))
+            pool_t.append(pooled)
+        sel_t = np.stack(sel_t)
+        for i in range(q0, q1):
+            for j in range(sh.num_q_heads):
+                t = tokens_of(sel_t[j // G], B, P + i)
+                out[i, j] = softmax_attend(q[i, j], K[j // G][t], V[j // G][t], sh.softmax_scale)
+        sels.append(sel_t)
+        pools.append(pool_t)
+    return {"out": out, "sel": np.stack(sels), "pooled": pools}

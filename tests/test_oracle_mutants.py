@@ -1,0 +1,102 @@
+"""Plant plausible mistakes in a copy of the oracle and check that the pins
+catch every one of them (CPU only; the copies are compiled into a temporary
+directory and never replace the real oracle)."""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from msa_inputs import make_decode_case, make_prefill_case
+from tests import bruteforce
+from tests.test_oracle_pins import TINY, TINY1, _by_sort
+from tests.test_oracle_pins import test_handworked_golden as _golden
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "msa_oracle.c")
+
+# (name, text in msa_oracle.c, replacement, replace every occurrence)
+MUTANTS = [
+    ("index heads not pooled", "for (int64_t row = 0; row < nrows; row++)",
+     "for (int64_t row = 0; row < nrows; row += ni)", False),
+    ("own block scored", "if (b < own)\n", "if (b <= own)\n", False),
+    ("ties keep the higher index", "score[b] > score[best]", "score[b] >= score[best]", False),
+    ("values read untransposed", "return bf(c->v[((pg * H + g) * D + d) * B + t % B]);",
+     "return bf(c->v[((pg * H + g) * B + t % B) * D + d]);", False),
+    ("softmax scale dropped", "z[i] = p->softmax_scale * dot;", "z[i] = dot;", False),
+    ("heads mapped to groups round-robin", "int32_t g = j / G;", "int32_t g = j % H;", True),
+    ("one block too few", "int32_t kk = (k - 1 < own) ? k - 1 : own;",
+     "int32_t kk = (k - 2 < own) ? k - 2 : own;", False),
+    ("current token excluded", "if (hi > last_pos + 1) hi = last_pos + 1;",
+     "if (hi > last_pos) hi = last_pos;", True),
+    ("block table ignored for index keys",
+     "  int64_t pg = page_of(c, seq, t, B);\n  return bf(c->idx_k",
+     "  int64_t pg = t / B;\n  return bf(c->idx_k", False),
+    ("tile queries not pooled", "block_score(p, c, 0, idx_q, q0, q1, g, b)",
+     "block_score(p, c, 0, idx_q, q0, q0 + 1, g, b)", False),
+    ("softmax not normalised", "out[d] = acc / den;", "out[d] = acc;", False),
+    ("index key dims swapped with query", "dot += qry[row * di + d] * key[r * di + d];",
+     "dot += qry[row * di + d] * key[d * B + r];", False),
+]
+
+
+def _pins_pass() -> bool:
+    """A compact run of the brute-force, TopK and golden pins."""
+    try:
+        for shape, lengths, seed, kw in [
+                (TINY, [37, 9, 1, 4, 5, 17], 11, {}),
+                (TINY, [41, 7, 28, 13], 21, dict(shuffle_pages=True, poison_frac=0.3)),
+                (TINY1, [300, 16, 17], 13, {})]:
+            case = make_decode_case(shape, lengths, seed, **kw)
+            o, r = oracle.decode(case), bruteforce.decode(case)
+            np.testing.assert_array_equal(o["sel"], r["sel"])
+            for s, L in enumerate(case.lengths):
+                own = (L - 1) // shape.block_size
+                for g in range(shape.num_kv_heads):
+                    np.testing.assert_array_equal(o["pooled"][s, g, :own], r["pooled"][s][g])
+                    assert np.all(np.isneginf(o["pooled"][s, g, own:]))
+            np.testing.assert_allclose(o["out"], r["out"], rtol=1e-12, atol=1e-12)
+        for P, C, seed in [(13, 22, 32), (37, 40, 35)]:
+            case = make_prefill_case(TINY, P, C, seed, shuffle_pages=True, poison_frac=0.2)
+            o, r = oracle.prefill(case), bruteforce.prefill(case)
+            np.testing.assert_array_equal(o["sel"], r["sel"])
+            np.testing.assert_allclose(o["out"], r["out"], rtol=1e-12, atol=1e-12)
+        rng = np.random.default_rng(5)
+        for _ in range(100):
+            own, k = int(rng.integers(0, 30)), int(rng.integers(1, 10))
+            sc = rng.integers(-3, 4, size=max(own, 1)).astype(np.float64)
+            assert oracle.select(sc[:own], own, k).tolist() == _by_sort(sc, own, k)
+        _golden()
+    except AssertionError:
+        return False
+    return True
+
+
+def test_unmutated_copy_passes(tmp_path):
+    lib = tmp_path / "liboracle_copy.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-shared", "-fPIC", SRC,
+                           "-o", str(lib), "-lm"])
+    oracle.use_library(str(lib))
+    try:
+        assert _pins_pass()
+    finally:
+        oracle.use_library(None)
+
+
+@pytest.mark.parametrize("name,old,new,every", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(tmp_path, name, old, new, every):
+    text = open(SRC).read()
+    assert text.count(old) >= 1, name
+    if not every:
+        assert text.count(old) == 1, name
+    mutated = text.replace(old, new) if every else text.replace(old, new, 1)
+    src = tmp_path / "mutant.c"
+    src.write_text(mutated)
+    lib = tmp_path / ("libmutant_%d.so" % abs(hash(name)))
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-shared", "-fPIC", str(src),
+                           "-o", str(lib), "-lm"])
+    oracle.use_library(str(lib))
+    try:
+        assert not _pins_pass(), "pins did not catch: " + name
+    finally:
+        oracle.use_library(None)
