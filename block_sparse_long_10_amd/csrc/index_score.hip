@@ -1,0 +1,291 @@
+// Index branch of MSA: token scores Q_idx . K_idx^T against the single shared
+// index-key head, max-pooled per KV block ("Block Max Pool"), following
+// "MiniMax wird dünn", section 1, Schritt 1.
+//
+// Decode (msa_index_score_decode): one pass over every cached index key of
+// every sequence.  The keys are streamed from HBM exactly once with 16-byte
+// loads straight into MFMA operand registers; all Hkv*n_i index-query rows of a
+// sequence (32 at 8 groups x 4 heads) are the M side of a
+// v_mfma_f32_16x16x32_bf16 so the 64-term dots run on the matrix cores and the
+// kernel stays bound by HBM.  Each wave owns a run of blocks, double-buffers
+// one block (B tokens x 128 B) in registers, and folds the 16x16 score tiles
+// into per-row running maxima; a DPP row reduction then gives the block max.
+//
+// Prefill (msa_index_score_prefill): per (tile, group) the tile's queries x
+// index heads (up to 512 rows) are held in registers as the A side of
+// v_mfma_f32_32x32x16_bf16 and every eligible key block is staged through LDS
+// (XOR-swizzled 16-byte chunks, double-buffered) as the B side.  The 32x32
+// accumulators are folded with v_max into one running max per lane and
+// reduced across the workgroup once per block.
+#include "msa_device.h"
+#include "msa_launch.h"
+
+namespace msa {
+
+// ---------------------------------------------------------------- decode
+template <int B, int NI, int MT>
+__global__ __launch_bounds__(256) void index_score_decode_kernel(
+    const uint16_t* __restrict__ idx_k, const int32_t* __restrict__ block_table,
+    int32_t max_blocks, const uint16_t* __restrict__ idx_q, const int32_t* __restrict__ seq_lens,
+    int32_t num_kv_heads, int32_t blocks_per_wave, float* __restrict__ pooled,
+    uint32_t* __restrict__ zero_counters) {
+  constexpr int NT = B / 16;  // 16-token MFMA tiles per block
+  const int s = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  if (zero_counters != nullptr && blockIdx.x == 0 && tid < num_kv_heads)
+    zero_counters[s * num_kv_heads + tid] = 0u;
+  const int own = (seq_lens[s] - 1) / B;
+  const int b_begin = (blockIdx.x * (256 / kWave) + wave) * blocks_per_wave;
+  const int b_end = min(b_begin + blocks_per_wave, own);
+  if (b_begin >= b_end) return;
+
+  const int R = num_kv_heads * NI;
+  const int r16 = lane & 15, q4 = lane >> 4;
+  // A operand: index-query rows (row = group*NI + head), two 32-wide K steps.
+  bf16x8 a[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int row = mt * 16 + r16;
+    const uint16_t* p = idx_q + ((size_t)s * R + row) * 64 + q4 * 8;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) a[mt][ks] = row < R ? load_bf16x8(p + ks * 32) : zero_bf16x8();
+  }
+  const int32_t* bt = block_table + (size_t)s * max_blocks;
+  float* out = pooled + (size_t)s * num_kv_heads * max_blocks;
+
+  // B operand: token nt*16 + r16 of the block, same K split as A.
+  bf16x8 kb[NT][2];
+  auto load_block = [&](int b) {
+    const uint16_t* base = idx_k + (size_t)bt[b] * (B * 64) + r16 * 64 + q4 * 8;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      kb[nt][0] = load_bf16x8(base + nt * 16 * 64);
+      kb[nt][1] = load_bf16x8(base + nt * 16 * 64 + 32);
+    }
+  };
+  load_block(b_begin);
+  for (int b = b_begin; b < b_end; ++b) {
+    bf16x8 cur[NT][2];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      cur[nt][0] = kb[nt][0];
+      cur[nt][1] = kb[nt][1];
+    }
+    if (b + 1 < b_end) load_block(b + 1);
+    f32x4 rmax[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) rmax[mt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma16(a[mt][0], cur[nt][0], acc);
+        acc = mfma16(a[mt][1], cur[nt][1], acc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rmax[mt][j] = fmaxf(rmax[mt][j], acc[j]);
+      }
+    }
+    // lane holds rows mt*16 + 4*q4 + j; reduce over the 16 token lanes, then
+    // over the rows of each group.
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row0 = mt * 16 + q4 * 4;
+      if constexpr (NI >= 4) {
+        float v = row16_max(max4(rmax[mt]));
+        if constexpr (NI >= 8) v = fmaxf(v, xor_lane(v, 16));
+        if constexpr (NI >= 16) v = fmaxf(v, xor_lane(v, 32));
+        const int g = row0 / NI;
+        if (r16 == 0 && (row0 % NI) == 0 && g < num_kv_heads) out[(size_t)g * max_blocks + b] = v;
+      } else {
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = row16_max(rmax[mt][j]);
+        if (r16 == 0) {
+          if constexpr (NI == 2) {
+            const int g = row0 / 2;
+            if (g < num_kv_heads) out[(size_t)g * max_blocks + b] = fmaxf(v[0], v[1]);
+            if (g + 1 < num_kv_heads) out[(size_t)(g + 1) * max_blocks + b] = fmaxf(v[2], v[3]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (row0 + j < num_kv_heads) out[(size_t)(row0 + j) * max_blocks + b] = v[j];
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int B, int NI>
+static hipError_t launch_decode_ni(int mt, dim3 grid, hipStream_t st, const uint16_t* idx_k,
+                                   const int32_t* bt, int32_t mb, const uint16_t* idx_q,
+                                   const int32_t* sl, int32_t hkv, int32_t bpw, float* pooled,
+                                   uint32_t* zc) {
+  switch (mt) {
+    case 1: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 1>), grid, dim3(256), 0, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled, zc); break;
+    case 2: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 2>), grid, dim3(256), 0, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled, zc); break;
+    case 3: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 3>), grid, dim3(256), 0, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled, zc); break;
+    default: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 4>), grid, dim3(256), 0, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled, zc); break;
+  }
+  return hipGetLastError();
+}
+
+template <int B>
+static hipError_t launch_decode_b(int ni, int mt, dim3 grid, hipStream_t st, const uint16_t* idx_k,
+                                  const int32_t* bt, int32_t mb, const uint16_t* idx_q,
+                                  const int32_t* sl, int32_t hkv, int32_t bpw, float* pooled,
+                                  uint32_t* zc) {
+  switch (ni) {
+    case 1: return launch_decode_ni<B, 1>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled, zc);
+    case 2: return launch_decode_ni<B, 2>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled, zc);
+    case 4: return launch_decode_ni<B, 4>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled, zc);
+    case 8: return launch_decode_ni<B, 8>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled, zc);
+    default: return launch_decode_ni<B, 16>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled, zc);
+  }
+}
+
+hipError_t launch_index_score_decode(const Dims& d, const Cache& c, const uint16_t* idx_q,
+                                     const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                     float* pooled, uint32_t* zero_counters, hipStream_t stream) {
+  const int B = d.block_size;
+  const int max_own = (max_seq_len - 1) / B;
+  const int bpw = 2;
+  const int per_wg = bpw * (256 / kWave);
+  const int gx = max_own > 0 ? (max_own + per_wg - 1) / per_wg : 1;
+  const int mt = (d.num_kv_heads * d.num_idx_heads + 15) / 16;
+  dim3 grid(gx, batch);
+  if (B == 64)
+    return launch_decode_b<64>(d.num_idx_heads, mt, grid, stream, c.idx_k, c.block_table,
+                               c.max_blocks, idx_q, seq_lens, d.num_kv_heads, bpw, pooled,
+                               zero_counters);
+  return launch_decode_b<128>(d.num_idx_heads, mt, grid, stream, c.idx_k, c.block_table,
+                              c.max_blocks, idx_q, seq_lens, d.num_kv_heads, bpw, pooled,
+                              zero_counters);
+}
+
+// --------------------------------------------------------------- prefill
+// Workgroup: 4 waves x 128 row slots (4 M tiles of 32) = 512 rows of one
+// (tile, group); rows are (query, index head) pairs, padding rows repeat row 0.
+// Keys: blocks [b_lo, b_hi) of the tile's eligible range, one block per step.
+template <int B>
+__global__ __launch_bounds__(256) void index_score_prefill_kernel(
+    const uint16_t* __restrict__ idx_k, const int32_t* __restrict__ block_table,
+    const uint16_t* __restrict__ idx_q, int32_t prior_len, int32_t chunk_len, int32_t num_kv_heads,
+    int32_t num_idx_heads, int32_t max_blocks, int32_t blocks_per_split,
+    float* __restrict__ pooled) {
+  constexpr int NT = B / 32;                 // 32-token N tiles per block
+  constexpr int BLOCK_BYTES = B * 128;       // B tokens x 64 bf16
+  constexpr int LOADS = BLOCK_BYTES / (16 * 256);  // 16-byte loads per thread per block
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][BLOCK_BYTES];
+  __shared__ float wmax[2][4];
+
+  const int tile = blockIdx.x, g = blockIdx.y, split = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int own = prior_len / B + tile;
+  const int b_lo = split * blocks_per_split;
+  const int b_hi = min(b_lo + blocks_per_split, own);
+  if (b_lo >= b_hi) return;
+  const int q0 = max(0, own * B - prior_len);
+  const int q1 = min(chunk_len, (own + 1) * B - prior_len);
+  const int nrows = (q1 - q0) * num_idx_heads;
+
+  // A operand: row slot = wave*128 + mt*32 + (lane & 31); K = 64 in 4 steps of 16.
+  bf16x8 a[4][4];
+  const int half = lane >> 5;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    int r = wave * 128 + mt * 32 + (lane & 31);
+    if (r >= nrows) r = 0;
+    const int qi = q0 + r / num_idx_heads, h = r % num_idx_heads;
+    const uint16_t* p =
+        idx_q + (((size_t)qi * num_kv_heads + g) * num_idx_heads + h) * 64 + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) a[mt][ks] = load_bf16x8(p + ks * 16);
+  }
+
+  const int32_t* bt = block_table;  // one sequence
+  u32x4 pre[LOADS];
+  auto gload = [&](int b) {
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(idx_k) + (size_t)bt[b] * BLOCK_BYTES;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      pre[i] = *reinterpret_cast<const u32x4*>(src + (size_t)(i * 256 + tid) * 16);
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int chunk = i * 256 + tid;        // 16-byte chunk id within the block
+      const int t = chunk >> 3, c = chunk & 7;  // token, chunk within the 128-byte row
+      *reinterpret_cast<u32x4*>(&kbuf[buf][t * 128 + ((c ^ (t & 7)) << 4)]) = pre[i];
+    }
+  };
+
+  gload(b_lo);
+  lstore(0);
+  __syncthreads();
+  for (int b = b_lo; b < b_hi; ++b) {
+    const int buf = (b - b_lo) & 1;
+    const bool more = b + 1 < b_hi;
+    if (more) gload(b + 1);
+    f32x16 run;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) run[v] = -INFINITY;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int t = nt * 32 + (lane & 31);
+      bf16x8 bf[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int c = ks * 2 + half;
+        bf[ks] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(&kbuf[buf][t * 128 + ((c ^ (t & 7)) << 4)]));
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = mfma32(a[mt][ks], bf[ks], acc);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) run[v] = fmaxf(run[v], acc[v]);
+      }
+    }
+    float m = run[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) m = fmaxf(m, run[v]);
+    m = wave_max(m);
+    if (lane == 0) wmax[buf][wave] = m;
+    if (more) lstore(buf ^ 1);
+    __syncthreads();
+    if (tid == 0) {
+      const float r = fmaxf(fmaxf(wmax[buf][0], wmax[buf][1]), fmaxf(wmax[buf][2], wmax[buf][3]));
+      pooled[((size_t)tile * num_kv_heads + g) * max_blocks + b] = r;
+    }
+  }
+}
+
+hipError_t launch_index_score_prefill(const Dims& d, const Cache& c, const uint16_t* idx_q,
+                                      int32_t prior_len, int32_t chunk_len, float* pooled,
+                                      hipStream_t stream) {
+  const int B = d.block_size;
+  const int first = prior_len / B;
+  const int num_tiles = (prior_len + chunk_len + B - 1) / B - first;
+  const int max_own = first + num_tiles - 1;
+  // split the key range so that the grid holds several workgroups per CU
+  const int units = num_tiles * d.num_kv_heads;
+  int splits = (2048 + units - 1) / units;
+  if (splits > max_own) splits = max_own > 0 ? max_own : 1;
+  const int per = max_own > 0 ? (max_own + splits - 1) / splits : 1;
+  dim3 grid(num_tiles, d.num_kv_heads, splits);
+  if (B == 64)
+    hipLaunchKernelGGL(index_score_prefill_kernel<64>, grid, dim3(256), 0, stream, c.idx_k,
+                       c.block_table, idx_q, prior_len, chunk_len, d.num_kv_heads,
+                       d.num_idx_heads, c.max_blocks, per, pooled);
+  else
+    hipLaunchKernelGGL(index_score_prefill_kernel<128>, grid, dim3(256), 0, stream, c.idx_k,
+                       c.block_table, idx_q, prior_len, chunk_len, d.num_kv_heads,
+                       d.num_idx_heads, c.max_blocks, per, pooled);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,281 @@
+// Host side of libmsa.so: argument validation, workspace layout and the
+// launch sequence of each entry point declared in include/msa.h.
+//
+// Validation is pure host code and runs before any HIP call, so a rejected
+// call touches no device state.  Nothing here allocates, copies or
+// synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+#include "msa.h"
+#include "msa_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+msa_status fail(msa_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool is_pow2_idx_heads(int n) { return n == 1 || n == 2 || n == 4 || n == 8 || n == 16; }
+
+msa_status check_params(const msa_params* p) {
+  if (p == nullptr) return fail(MSA_ERR_INVALID_ARGUMENT, "params is NULL");
+  if (p->num_q_heads < 1 || p->num_kv_heads < 1 || p->head_dim < 1 || p->num_idx_heads < 1 ||
+      p->idx_dim < 1 || p->block_size < 1 || p->top_k < 1)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "head counts, dims, block_size and top_k must be >= 1");
+  if (p->num_q_heads % p->num_kv_heads != 0)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "num_q_heads must be a multiple of num_kv_heads");
+  if (!std::isfinite(p->softmax_scale))
+    return fail(MSA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
+  if (p->head_dim != 128) return fail(MSA_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (p->idx_dim != 64) return fail(MSA_ERR_UNSUPPORTED, "idx_dim must be 64");
+  if (p->block_size != 64 && p->block_size != 128)
+    return fail(MSA_ERR_UNSUPPORTED, "block_size must be 64 or 128");
+  if (p->top_k > 64) return fail(MSA_ERR_UNSUPPORTED, "top_k must be <= 64");
+  if (!is_pow2_idx_heads(p->num_idx_heads))
+    return fail(MSA_ERR_UNSUPPORTED, "num_idx_heads must be 1, 2, 4, 8 or 16");
+  if (p->num_kv_heads * p->num_idx_heads > 64)
+    return fail(MSA_ERR_UNSUPPORTED, "num_kv_heads * num_idx_heads must be <= 64");
+  if (p->num_q_heads / p->num_kv_heads > 16)
+    return fail(MSA_ERR_UNSUPPORTED, "group size num_q_heads/num_kv_heads must be <= 16");
+  return MSA_OK;
+}
+
+msa_status check_kv(const msa_paged_kv* kv) {
+  if (kv == nullptr) return fail(MSA_ERR_INVALID_ARGUMENT, "kv is NULL");
+  if (kv->k == nullptr || kv->v == nullptr || kv->idx_k == nullptr || kv->block_table == nullptr)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "kv cache pointer is NULL");
+  if (kv->num_pages < 1 || kv->max_blocks_per_seq < 1)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "num_pages and max_blocks_per_seq must be >= 1");
+  return MSA_OK;
+}
+
+msa::Dims dims_of(const msa_params* p) {
+  return msa::Dims{p->num_q_heads, p->num_kv_heads, p->head_dim, p->num_idx_heads,
+                   p->idx_dim,     p->block_size,   p->top_k,    p->softmax_scale};
+}
+
+msa::Cache cache_of(const msa_paged_kv* kv) {
+  return msa::Cache{static_cast<const uint16_t*>(kv->k), static_cast<const uint16_t*>(kv->v),
+                    static_cast<const uint16_t*>(kv->idx_k), kv->block_table, kv->num_pages,
+                    kv->max_blocks_per_seq};
+}
+
+msa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MSA_OK;
+  return fail(MSA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// decode workspace layout
+struct DecodeWs {
+  size_t pooled, part_o, part_ml, counters, sel, total;
+};
+DecodeWs decode_layout(const msa_params* p, int32_t batch, int32_t max_blocks) {
+  const size_t G = (size_t)(p->num_q_heads / p->num_kv_heads);
+  const size_t sg = (size_t)batch * p->num_kv_heads;
+  DecodeWs w{};
+  size_t off = 0;
+  w.pooled = off;
+  off += align_up(sg * (size_t)max_blocks * sizeof(float));
+  w.part_o = off;
+  off += align_up(sg * p->top_k * G * p->head_dim * sizeof(float));
+  w.part_ml = off;
+  off += align_up(sg * p->top_k * G * 2 * sizeof(float));
+  w.counters = off;
+  off += align_up(sg * sizeof(uint32_t));
+  w.sel = off;
+  off += align_up(sg * p->top_k * sizeof(int32_t));
+  w.total = off;
+  return w;
+}
+
+int32_t num_tiles_of(int32_t prior_len, int32_t chunk_len, int32_t B) {
+  return (int32_t)(((int64_t)prior_len + chunk_len + B - 1) / B - prior_len / B);
+}
+
+struct PrefillWs {
+  size_t pooled, sel, total;
+};
+PrefillWs prefill_layout(const msa_params* p, int32_t prior_len, int32_t chunk_len,
+                         int32_t max_blocks) {
+  const size_t rows = (size_t)num_tiles_of(prior_len, chunk_len, p->block_size) * p->num_kv_heads;
+  PrefillWs w{};
+  w.pooled = 0;
+  w.sel = align_up(rows * (size_t)max_blocks * sizeof(float));
+  w.total = w.sel + align_up(rows * p->top_k * sizeof(int32_t));
+  return w;
+}
+
+msa_status check_prefill_sizes(const msa_params* p, const msa_paged_kv* kv, int32_t prior_len,
+                               int32_t chunk_len) {
+  if (prior_len < 0 || chunk_len < 1)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "prior_len must be >= 0 and chunk_len >= 1");
+  if ((int64_t)prior_len + chunk_len > (int64_t)kv->max_blocks_per_seq * p->block_size)
+    return fail(MSA_ERR_INVALID_ARGUMENT,
+                "prior_len + chunk_len exceeds max_blocks_per_seq * block_size");
+  if (p->block_size * p->num_idx_heads > 512)
+    return fail(MSA_ERR_UNSUPPORTED, "prefill needs block_size * num_idx_heads <= 512");
+  return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* msa_last_error(void) { return g_last_error.c_str(); }
+
+const char* msa_version(void) { return "msa-mi355x 0.1.0 (gfx950)"; }
+
+size_t msa_decode_workspace_bytes(const msa_params* params, int32_t batch,
+                                  int32_t max_blocks_per_seq) {
+  if (check_params(params) != MSA_OK || batch < 1 || max_blocks_per_seq < 1) return 0;
+  return decode_layout(params, batch, max_blocks_per_seq).total;
+}
+
+msa_status msa_index_score_decode(const msa_params* params, const msa_paged_kv* kv,
+                                  const void* idx_q, const int32_t* seq_lens, int32_t batch,
+                                  int32_t max_seq_len, float* pooled, void* stream) {
+  msa_status st = check_params(params);
+  if (st != MSA_OK) return st;
+  if ((st = check_kv(kv)) != MSA_OK) return st;
+  if (idx_q == nullptr || seq_lens == nullptr || pooled == nullptr)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "idx_q, seq_lens and pooled must not be NULL");
+  if (batch < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "batch must be >= 1");
+  if (max_seq_len < 1 || (int64_t)max_seq_len > (int64_t)kv->max_blocks_per_seq * params->block_size)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "max_seq_len must be in [1, max_blocks_per_seq*block_size]");
+  return hip_status(msa::launch_index_score_decode(dims_of(params), cache_of(kv),
+                                                   static_cast<const uint16_t*>(idx_q), seq_lens,
+                                                   batch, max_seq_len, pooled, nullptr,
+                                                   static_cast<hipStream_t>(stream)),
+                    "index score launch");
+}
+
+msa_status msa_decode(const msa_params* params, const msa_paged_kv* kv, const void* q,
+                      const void* idx_q, const int32_t* seq_lens, int32_t batch,
+                      int32_t max_seq_len, float* out, int32_t* sel, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  msa_status st = check_params(params);
+  if (st != MSA_OK) return st;
+  if ((st = check_kv(kv)) != MSA_OK) return st;
+  if (q == nullptr || idx_q == nullptr || seq_lens == nullptr || out == nullptr)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "q, idx_q, seq_lens and out must not be NULL");
+  if (batch < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "batch must be >= 1");
+  if (batch > 65535) return fail(MSA_ERR_UNSUPPORTED, "batch must be <= 65535");
+  if (max_seq_len < 1 || (int64_t)max_seq_len > (int64_t)kv->max_blocks_per_seq * params->block_size)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "max_seq_len must be in [1, max_blocks_per_seq*block_size]");
+  const DecodeWs w = decode_layout(params, batch, kv->max_blocks_per_seq);
+  if (workspace == nullptr || workspace_bytes < w.total)
+    return fail(MSA_ERR_WORKSPACE, "workspace missing or smaller than msa_decode_workspace_bytes()");
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* pooled = reinterpret_cast<float*>(ws + w.pooled);
+  uint32_t* counters = reinterpret_cast<uint32_t*>(ws + w.counters);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const msa::Dims d = dims_of(params);
+  const msa::Cache c = cache_of(kv);
+  st = hip_status(msa::launch_index_score_decode(d, c, static_cast<const uint16_t*>(idx_q),
+                                                 seq_lens, batch, max_seq_len, pooled, counters, s),
+                  "index score launch");
+  if (st != MSA_OK) return st;
+  return hip_status(
+      msa::launch_decode_attn(d, c, static_cast<const uint16_t*>(q), seq_lens, batch, pooled,
+                              reinterpret_cast<float*>(ws + w.part_o),
+                              reinterpret_cast<float*>(ws + w.part_ml), counters,
+                              sel != nullptr ? sel : reinterpret_cast<int32_t*>(ws + w.sel), out, s),
+      "sparse attention launch");
+}
+
+size_t msa_prefill_workspace_bytes(const msa_params* params, int32_t prior_len, int32_t chunk_len,
+                                   int32_t max_blocks_per_seq) {
+  if (check_params(params) != MSA_OK || prior_len < 0 || chunk_len < 1 || max_blocks_per_seq < 1)
+    return 0;
+  return prefill_layout(params, prior_len, chunk_len, max_blocks_per_seq).total;
+}
+
+msa_status msa_index_score_prefill(const msa_params* params, const msa_paged_kv* kv,
+                                   const void* idx_q, int32_t prior_len, int32_t chunk_len,
+                                   float* pooled, void* stream) {
+  msa_status st = check_params(params);
+  if (st != MSA_OK) return st;
+  if ((st = check_kv(kv)) != MSA_OK) return st;
+  if (idx_q == nullptr || pooled == nullptr)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "idx_q and pooled must not be NULL");
+  if ((st = check_prefill_sizes(params, kv, prior_len, chunk_len)) != MSA_OK) return st;
+  return hip_status(msa::launch_index_score_prefill(dims_of(params), cache_of(kv),
+                                                    static_cast<const uint16_t*>(idx_q), prior_len,
+                                                    chunk_len, pooled,
+                                                    static_cast<hipStream_t>(stream)),
+                    "prefill index score launch");
+}
+
+msa_status msa_block_topk_prefill(const msa_params* params, int32_t prior_len, int32_t chunk_len,
+                                  int32_t max_blocks_per_seq, const float* pooled, int32_t* sel,
+                                  void* stream) {
+  msa_status st = check_params(params);
+  if (st != MSA_OK) return st;
+  if (pooled == nullptr || sel == nullptr)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "pooled and sel must not be NULL");
+  if (prior_len < 0 || chunk_len < 1 || max_blocks_per_seq < 1 ||
+      (int64_t)prior_len + chunk_len > (int64_t)max_blocks_per_seq * params->block_size)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "inconsistent prior_len, chunk_len, max_blocks_per_seq");
+  return hip_status(msa::launch_block_topk_prefill(dims_of(params), prior_len, chunk_len,
+                                                   max_blocks_per_seq, pooled, sel,
+                                                   static_cast<hipStream_t>(stream)),
+                    "prefill topk launch");
+}
+
+msa_status msa_sparse_attn_prefill(const msa_params* params, const msa_paged_kv* kv, const void* q,
+                                   int32_t prior_len, int32_t chunk_len, const int32_t* sel,
+                                   float* out, void* stream) {
+  msa_status st = check_params(params);
+  if (st != MSA_OK) return st;
+  if ((st = check_kv(kv)) != MSA_OK) return st;
+  if (q == nullptr || sel == nullptr || out == nullptr)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "q, sel and out must not be NULL");
+  if ((st = check_prefill_sizes(params, kv, prior_len, chunk_len)) != MSA_OK) return st;
+  return hip_status(msa::launch_sparse_attn_prefill(dims_of(params), cache_of(kv),
+                                                    static_cast<const uint16_t*>(q), prior_len,
+                                                    chunk_len, sel, out,
+                                                    static_cast<hipStream_t>(stream)),
+                    "prefill sparse attention launch");
+}
+
+msa_status msa_prefill_chunk(const msa_params* params, const msa_paged_kv* kv, const void* q,
+                             const void* idx_q, int32_t prior_len, int32_t chunk_len, float* out,
+                             int32_t* sel, void* workspace, size_t workspace_bytes, void* stream) {
+  msa_status st = check_params(params);
+  if (st != MSA_OK) return st;
+  if ((st = check_kv(kv)) != MSA_OK) return st;
+  if (q == nullptr || idx_q == nullptr || out == nullptr)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "q, idx_q and out must not be NULL");
+  if ((st = check_prefill_sizes(params, kv, prior_len, chunk_len)) != MSA_OK) return st;
+  const PrefillWs w = prefill_layout(params, prior_len, chunk_len, kv->max_blocks_per_seq);
+  if (workspace == nullptr || workspace_bytes < w.total)
+    return fail(MSA_ERR_WORKSPACE, "workspace missing or smaller than msa_prefill_workspace_bytes()");
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* pooled = reinterpret_cast<float*>(ws + w.pooled);
+  int32_t* sel_buf = sel != nullptr ? sel : reinterpret_cast<int32_t*>(ws + w.sel);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const msa::Dims d = dims_of(params);
+  const msa::Cache c = cache_of(kv);
+  st = hip_status(msa::launch_index_score_prefill(d, c, static_cast<const uint16_t*>(idx_q),
+                                                  prior_len, chunk_len, pooled, s),
+                  "prefill index score launch");
+  if (st != MSA_OK) return st;
+  st = hip_status(msa::launch_block_topk_prefill(d, prior_len, chunk_len, kv->max_blocks_per_seq,
+                                                 pooled, sel_buf, s),
+                  "prefill topk launch");
+  if (st != MSA_OK) return st;
+  return hip_status(msa::launch_sparse_attn_prefill(d, c, static_cast<const uint16_t*>(q),
+                                                    prior_len, chunk_len, sel_buf, out, s),
+                    "prefill sparse attention launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Device-side helpers shared by the MSA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8*(l/16)+j], B[8*(l/16)+j][l%16]
+// (j = 0..7) and D[4*(l/16)+j][l%16] (j = 0..3).
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// v_mfma_f32_32x32x16_bf16: lane l holds A[l%32][8*(l/32)+j], B[8*(l/32)+j][l%32]
+// and D[8*(v/4)+4*(l/32)+v%4][l%32] (v = 0..15).
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+}
+__device__ __forceinline__ bf16x8 join_bf16x4(u32x2 lo, u32x2 hi) {
+  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// Round-to-nearest-even float -> bfloat16 bits (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __builtin_bit_cast(float, h << 16);
+}
+
+// Split x into hi + lo, both bfloat16, with hi = bf16(x) and lo = bf16(x - hi):
+// x - (hi + lo) is below 2^-16 |x|.
+__device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
+  hi = f32_to_bf16_bits(x);
+  lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+}
+__device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) {
+  return lo16 | (hi16 << 16);
+}
+
+// DPP row rotate within 16-lane rows (row_ror:n has control 0x120 + n).
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + N, 0xF, 0xF, false));
+}
+// Max over the 16 lanes of each DPP row; every lane receives the result.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, row_ror<8>(v));
+  v = fmaxf(v, row_ror<4>(v));
+  v = fmaxf(v, row_ror<2>(v));
+  v = fmaxf(v, row_ror<1>(v));
+  return v;
+}
+__device__ __forceinline__ float row16_min(float v) {
+  v = fminf(v, row_ror<8>(v));
+  v = fminf(v, row_ror<4>(v));
+  v = fminf(v, row_ror<2>(v));
+  v = fminf(v, row_ror<1>(v));
+  return v;
+}
+__device__ __forceinline__ float xor_lane(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  v = fmaxf(v, xor_lane(v, 16));
+  return fmaxf(v, xor_lane(v, 32));
+}
+__device__ __forceinline__ float wave_min(float v) {
+  v = row16_min(v);
+  v = fminf(v, xor_lane(v, 16));
+  return fminf(v, xor_lane(v, 32));
+}
+
+__device__ __forceinline__ float max4(f32x4 v) { return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])); }
+
+// Device-scope release/acquire fences around the "last workgroup" hand-off.
+__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+}  // namespace msa

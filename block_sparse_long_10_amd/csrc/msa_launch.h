@@ -1,0 +1,52 @@
+// Internal launch interface between the host dispatch (msa_api.cpp) and the
+// HIP kernels.  Every launcher enqueues on `stream` and returns the
+// hipGetLastError() of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+struct Dims {
+  int32_t num_q_heads, num_kv_heads, head_dim, num_idx_heads, idx_dim, block_size, top_k;
+  float softmax_scale;
+};
+
+struct Cache {
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* idx_k;
+  const int32_t* block_table;
+  int32_t num_pages, max_blocks;
+};
+
+// Step 1, decode: pooled[s][g][b] for b < own(s).  When zero_counters is not
+// null, counters [batch][Hkv] are cleared for the attention launch that follows.
+hipError_t launch_index_score_decode(const Dims& d, const Cache& c, const uint16_t* idx_q,
+                                     const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                     float* pooled, uint32_t* zero_counters, hipStream_t stream);
+
+// TopK + Step 2, decode, with the cross-block merge done by the last workgroup
+// of each (sequence, group).
+hipError_t launch_decode_attn(const Dims& d, const Cache& c, const uint16_t* q,
+                              const int32_t* seq_lens, int32_t batch, const float* pooled,
+                              float* part_o, float* part_ml, uint32_t* counters, int32_t* sel,
+                              float* out, hipStream_t stream);
+
+// Step 1, prefill: pooled[t][g][b] for b < prior_len/B + t.
+hipError_t launch_index_score_prefill(const Dims& d, const Cache& c, const uint16_t* idx_q,
+                                      int32_t prior_len, int32_t chunk_len, float* pooled,
+                                      hipStream_t stream);
+
+// TopK, prefill: sel[t][g][k].
+hipError_t launch_block_topk_prefill(const Dims& d, int32_t prior_len, int32_t chunk_len,
+                                     int32_t max_blocks, const float* pooled, int32_t* sel,
+                                     hipStream_t stream);
+
+// Step 2, prefill, for a given selection.
+hipError_t launch_sparse_attn_prefill(const Dims& d, const Cache& c, const uint16_t* q,
+                                      int32_t prior_len, int32_t chunk_len, const int32_t* sel,
+                                      float* out, hipStream_t stream);
+
+}  // namespace msa

@@ -1,0 +1,371 @@
+// Sparse branch of MSA: exact softmax attention of every query head of a GQA
+// group over the real keys/values of the group's kept blocks only
+// ("MiniMax wird dünn", section 1, Schritt 2; all heads of a group share one
+// selection, Q1-Q3 -> I_1, Q4-Q6 -> I_2).
+//
+// Both kernels compute S^T = K Q^T (keys on the MFMA M side, query rows on the
+// N side) so that a query row's softmax statistics live in one lane pair, and
+// O^T = V^T P^T with V^T read straight from the page layout [D][B] (8
+// consecutive tokens of one dimension = one 16-byte operand).  Probabilities
+// enter the bf16 PV contraction as hi + lo bf16 parts (P - hi - lo < 2^-16 P),
+// so the only rounding left is fp32 accumulation.
+//
+// Decode: one workgroup per (sequence, group, kept-block slot).  Every
+// workgroup first re-derives its group's selection from the pooled scores
+// (block_topk, identical in all slots), then attends to its one block
+// (4 waves x 32 tokens, v_mfma_f32_16x16x32_bf16, heads padded to 16) and
+// writes a partial (max, sum, unnormalised output).  The last workgroup of a
+// (sequence, group) to finish -- detected with a device-scope counter that the
+// preceding index launch cleared -- merges the partials by log-sum-exp.
+//
+// Prefill: one workgroup per (tile, group, 128 query rows); rows are
+// (query, head) pairs of the group.  Kept blocks are staged whole through LDS
+// (K token-major, V^T dimension-major, XOR-swizzled 16-byte chunks) and
+// consumed 32 keys at a time with v_mfma_f32_32x32x16_bf16 and an online
+// softmax; the causal mask applies inside the tile's diagonal block only.
+#include "block_topk.h"
+#include "msa_device.h"
+#include "msa_launch.h"
+
+namespace msa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- decode
+template <int B>
+__global__ __launch_bounds__(256) void decode_attn_kernel(
+    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ block_table, int32_t max_blocks, const uint16_t* __restrict__ q,
+    const int32_t* __restrict__ seq_lens, const float* __restrict__ pooled, int32_t num_kv_heads,
+    int32_t group, int32_t top_k, float scale_log2, float* __restrict__ part_o,
+    float* __restrict__ part_ml, uint32_t* __restrict__ counters, int32_t* __restrict__ sel_out,
+    float* __restrict__ out) {
+  __shared__ TopkShared tsh;
+  __shared__ int sel_s[kMaxTopK];
+  __shared__ float w_m[4][16], w_l[4][16];
+  __shared__ float w_o[4][16][128 + 4];
+  __shared__ int is_last;
+
+  const int slot = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int L = seq_lens[s];
+  const int own = (L - 1) / B;
+  const int Hq = num_kv_heads * group;
+  const size_t sg = (size_t)s * num_kv_heads + g;
+
+  block_topk(pooled + sg * max_blocks, own, top_k, sel_s, tsh);
+  if (slot == 0 && sel_out != nullptr)
+    for (int i = tid; i < top_k; i += 256) sel_out[sg * top_k + i] = sel_s[i];
+  const int blk = sel_s[slot];
+  const size_t pbase = sg * top_k + slot;
+
+  if (blk < 0) {
+    for (int h = tid; h < group; h += 256) {
+      part_ml[(pbase * group + h) * 2 + 0] = -INFINITY;
+      part_ml[(pbase * group + h) * 2 + 1] = 0.f;
+    }
+  } else {
+    const int n_valid = min(B, L - blk * B);
+    const size_t page = (size_t)block_table[(size_t)s * max_blocks + blk];
+    const int t0 = wave * 32;
+    const int r16 = lane & 15, q4 = lane >> 4;
+    float m_w = -INFINITY, l_w = 0.f;
+    f32x4 o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (t0 < n_valid) {
+      // Q^T as the B operand: lane -> head r16, dims ks*32 + 8*q4 .. +7
+      bf16x8 qf[4];
+      const uint16_t* qp = q + ((size_t)s * Hq + (size_t)g * group + r16) * 128 + q4 * 8;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qf[ks] = r16 < group ? load_bf16x8(qp + ks * 32) : zero_bf16x8();
+      // S^T tiles: M row r of tile mt is token t0 + 8*(r>>2) + 4*mt + (r&3), so
+      // that lane (r16, q4) ends up with tokens t0 + 8*q4 + 0..7 of head r16.
+      const uint16_t* kp = kc + (page * num_kv_heads + g) * (size_t)(B * 128);
+      f32x4 st[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int tok = t0 + 8 * (r16 >> 2) + 4 * mt + (r16 & 3);
+        const uint16_t* kr = kp + (size_t)tok * 128 + q4 * 8;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = mfma16(load_bf16x8(kr + ks * 32), qf[ks], acc);
+        st[mt] = acc;
+      }
+      float z[8];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int tok = t0 + 8 * q4 + 4 * mt + j;
+          z[mt * 4 + j] = tok < n_valid ? st[mt][j] * scale_log2 : -INFINITY;
+        }
+      float mx = z[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
+      mx = fmaxf(mx, xor_lane(mx, 16));
+      mx = fmaxf(mx, xor_lane(mx, 32));
+      float p[8], sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p[i] = z[i] == -INFINITY ? 0.f : exp2f(z[i] - mx);
+        sum += p[i];
+      }
+      sum += xor_lane(sum, 16);
+      sum += xor_lane(sum, 32);
+      m_w = mx;
+      l_w = sum;
+      // P^T as the B operand (keys 8*q4 + j of head r16), hi + lo bf16 parts
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) split_bf16(p[i], hi[i], lo[i]);
+      const bf16x8 phi = __builtin_bit_cast(
+          bf16x8, u32x4{pack2(hi[0], hi[1]), pack2(hi[2], hi[3]), pack2(hi[4], hi[5]), pack2(hi[6], hi[7])});
+      const bf16x8 plo = __builtin_bit_cast(
+          bf16x8, u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(lo[4], lo[5]), pack2(lo[6], lo[7])});
+      // V^T as the A operand: dimension 16*mt + r16, tokens t0 + 8*q4 .. +7
+      const uint16_t* vp = vc + (page * num_kv_heads + g) * (size_t)(128 * B) + t0 + 8 * q4;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const bf16x8 vf = load_bf16x8(vp + (size_t)(16 * mt + r16) * B);
+        o[mt] = mfma16(vf, phi, o[mt]);
+        o[mt] = mfma16(vf, plo, o[mt]);
+      }
+    }
+    // o[mt][j] = O^T[dim 16*mt + 4*q4 + j][head r16]
+    if (lane < 16) {
+      w_m[wave][lane] = m_w;
+      w_l[wave][lane] = l_w;
+    }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w_o[wave][r16][16 * mt + 4 * q4 + j] = o[mt][j];
+    __syncthreads();
+    for (int idx = tid; idx < group * 128; idx += 256) {
+      const int h = idx >> 7, d = idx & 127;
+      float M = w_m[0][h];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) M = fmaxf(M, w_m[w][h]);
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        if (w_m[w][h] != -INFINITY) acc += exp2f(w_m[w][h] - M) * w_o[w][h][d];
+      part_o[(pbase * group + h) * 128 + d] = acc;
+      if (d == 0) {
+        float l = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          if (w_m[w][h] != -INFINITY) l += exp2f(w_m[w][h] - M) * w_l[w][h];
+        part_ml[(pbase * group + h) * 2 + 0] = M;
+        part_ml[(pbase * group + h) * 2 + 1] = l;
+      }
+    }
+  }
+
+  // the last workgroup of this (sequence, group) merges all slots
+  fence_release();
+  __syncthreads();
+  if (tid == 0) is_last = atomicAdd(&counters[sg], 1u) == (unsigned)(top_k - 1);
+  __syncthreads();
+  if (!is_last) return;
+  fence_acquire();
+  for (int idx = tid; idx < group * 128; idx += 256) {
+    const int h = idx >> 7, d = idx & 127;
+    float M = -INFINITY;
+    for (int k = 0; k < top_k; ++k) M = fmaxf(M, part_ml[((sg * top_k + k) * group + h) * 2]);
+    float num = 0.f, den = 0.f;
+    for (int k = 0; k < top_k; ++k) {
+      const size_t pk = (sg * top_k + k) * group + h;
+      const float m = part_ml[pk * 2];
+      if (m == -INFINITY) continue;
+      const float w = exp2f(m - M);
+      num += w * part_o[pk * 128 + d];
+      den += w * part_ml[pk * 2 + 1];
+    }
+    out[((size_t)s * Hq + (size_t)g * group + h) * 128 + d] = num / den;
+  }
+}
+
+hipError_t launch_decode_attn(const Dims& d, const Cache& c, const uint16_t* q,
+                              const int32_t* seq_lens, int32_t batch, const float* pooled,
+                              float* part_o, float* part_ml, uint32_t* counters, int32_t* sel,
+                              float* out, hipStream_t stream) {
+  const int G = d.num_q_heads / d.num_kv_heads;
+  const float sl2 = d.softmax_scale * kLog2e;
+  dim3 grid(d.top_k, d.num_kv_heads, batch);
+  if (d.block_size == 64)
+    hipLaunchKernelGGL(decode_attn_kernel<64>, grid, dim3(256), 0, stream, c.k, c.v,
+                       c.block_table, c.max_blocks, q, seq_lens, pooled, d.num_kv_heads, G,
+                       d.top_k, sl2, part_o, part_ml, counters, sel, out);
+  else
+    hipLaunchKernelGGL(decode_attn_kernel<128>, grid, dim3(256), 0, stream, c.k, c.v,
+                       c.block_table, c.max_blocks, q, seq_lens, pooled, d.num_kv_heads, G,
+                       d.top_k, sl2, part_o, part_ml, counters, sel, out);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------- prefill
+template <int B>
+__global__ __launch_bounds__(256) void prefill_attn_kernel(
+    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ block_table, const uint16_t* __restrict__ q,
+    const int32_t* __restrict__ sel, int32_t prior_len, int32_t chunk_len, int32_t num_kv_heads,
+    int32_t group, int32_t top_k, float scale_log2, float* __restrict__ out) {
+  constexpr int KROW = 256;            // bytes per key row (128 bf16)
+  constexpr int VROW = 2 * B;          // bytes per value^T row (B bf16)
+  constexpr int VCH = B / 8;           // 16-byte chunks per value^T row
+  constexpr int LOADS = B * 256 / (16 * 256);  // per thread, per K (and per V) block
+  __shared__ __attribute__((aligned(16))) uint8_t ks_[B * KROW];
+  __shared__ __attribute__((aligned(16))) uint8_t vs_[128 * VROW];
+
+  const int tile = blockIdx.x, g = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int own = prior_len / B + tile;
+  const int q0 = max(0, own * B - prior_len);
+  const int q1 = min(chunk_len, (own + 1) * B - prior_len);
+  const int nq = q1 - q0;
+  const int nrows = nq * group;
+  const int row0 = blockIdx.z * 128;
+  if (row0 >= nrows) return;
+  const int Hq = num_kv_heads * group;
+
+  // this lane's query row (N side): (query, head) = (q0 + r % nq, r / nq)
+  const int half = lane >> 5;
+  int r = row0 + wave * 32 + (lane & 31);
+  const bool row_ok = r < nrows;
+  if (!row_ok) r = 0;
+  const int qi = q0 + r % nq, hh = r / nq;
+  const int pos = prior_len + qi;
+  bf16x8 qf[8];
+  {
+    const uint16_t* qp = q + ((size_t)qi * Hq + (size_t)g * group + hh) * 128 + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = load_bf16x8(qp + ks * 16);
+  }
+  f32x16 o[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) o[mt] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int32_t* srow = sel + ((size_t)tile * num_kv_heads + g) * top_k;
+  for (int si = 0; si < top_k; ++si) {
+    const int blk = srow[si];
+    if (blk < 0) break;
+    const size_t page = (size_t)block_table[blk];
+    // stage K (token-major) and V^T (dimension-major) of this block
+    const uint8_t* kg = reinterpret_cast<const uint8_t*>(kc) + (page * num_kv_heads + g) * (size_t)(B * KROW);
+    const uint8_t* vg = reinterpret_cast<const uint8_t*>(vc) + (page * num_kv_heads + g) * (size_t)(128 * VROW);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int ch = i * 256 + tid;
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(kg + (size_t)ch * 16);
+      const u32x4 vv = *reinterpret_cast<const u32x4*>(vg + (size_t)ch * 16);
+      const int kt = ch >> 4, kcn = ch & 15;
+      *reinterpret_cast<u32x4*>(&ks_[kt * KROW + ((kcn ^ (kt & 15)) << 4)]) = kv;
+      const int vd = ch / VCH, vcn = ch % VCH;
+      *reinterpret_cast<u32x4*>(&vs_[vd * VROW + ((vcn ^ (vd & (VCH - 1))) << 4)]) = vv;
+    }
+    __syncthreads();
+    const bool diag = blk == own;
+#pragma unroll 1
+    for (int kt = 0; kt < B / 32; ++kt) {
+      // S^T: A = K rows; M row m of the tile is key kmap(m) so that value v of
+      // lane half h is key 16*(v/8) + 8*h + v%8.
+      const int m = lane & 31;
+      const int key = kt * 32 + 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
+      f32x16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int c = ks * 2 + half;
+        const bf16x8 kf = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(&ks_[key * KROW + ((c ^ (key & 15)) << 4)]));
+        acc = mfma32(kf, qf[ks], acc);
+      }
+      float z[16];
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int kk = kt * 32 + 16 * (v >> 3) + 8 * half + (v & 7);
+        const bool ok = !diag || (blk * B + kk) <= pos;
+        z[v] = ok ? acc[v] * scale_log2 : -INFINITY;
+        mloc = fmaxf(mloc, z[v]);
+      }
+      mloc = fmaxf(mloc, xor_lane(mloc, 32));
+      // control flow stays wave-uniform around the MFMAs: a row that sees no
+      // key yet keeps alpha = 1 and p = 0
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha =
+          m_new == -INFINITY ? 1.f : (m_run == -INFINITY ? 0.f : exp2f(m_run - m_new));
+      float p[16], psum = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        p[v] = z[v] == -INFINITY ? 0.f : exp2f(z[v] - m_new);
+        psum += p[v];
+      }
+      psum += xor_lane(psum, 32);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[mt][v] *= alpha;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        uint32_t hi[8], lo[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) split_bf16(p[8 * s2 + j], hi[j], lo[j]);
+        const bf16x8 phi = __builtin_bit_cast(
+            bf16x8, u32x4{pack2(hi[0], hi[1]), pack2(hi[2], hi[3]), pack2(hi[4], hi[5]), pack2(hi[6], hi[7])});
+        const bf16x8 plo = __builtin_bit_cast(
+            bf16x8, u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(lo[4], lo[5]), pack2(lo[6], lo[7])});
+        const int vch = kt * 4 + 2 * s2 + half;  // chunk of keys kt*32 + 16*s2 + 8*half
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int dd = mt * 32 + (lane & 31);
+          const bf16x8 vf = __builtin_bit_cast(
+              bf16x8,
+              *reinterpret_cast<const u32x4*>(&vs_[dd * VROW + ((vch ^ (dd & (VCH - 1))) << 4)]));
+          o[mt] = mfma32(vf, phi, o[mt]);
+          o[mt] = mfma32(vf, plo, o[mt]);
+        }
+      }
+    }
+  }
+  if (!row_ok) return;
+  const float inv = 1.f / l_run;
+  float* op = out + ((size_t)qi * Hq + (size_t)g * group + hh) * 128;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const int d0 = mt * 32 + 8 * v4 + 4 * half;
+      *reinterpret_cast<f32x4*>(op + d0) =
+          f32x4{o[mt][4 * v4] * inv, o[mt][4 * v4 + 1] * inv, o[mt][4 * v4 + 2] * inv,
+                o[mt][4 * v4 + 3] * inv};
+    }
+}
+
+hipError_t launch_sparse_attn_prefill(const Dims& d, const Cache& c, const uint16_t* q,
+                                      int32_t prior_len, int32_t chunk_len, const int32_t* sel,
+                                      float* out, hipStream_t stream) {
+  const int B = d.block_size;
+  const int G = d.num_q_heads / d.num_kv_heads;
+  const int first = prior_len / B;
+  const int num_tiles = (prior_len + chunk_len + B - 1) / B - first;
+  const int zr = (B * G + 127) / 128;
+  const float sl2 = d.softmax_scale * kLog2e;
+  dim3 grid(num_tiles, d.num_kv_heads, zr);
+  if (B == 64)
+    hipLaunchKernelGGL(prefill_attn_kernel<64>, grid, dim3(256), 0, stream, c.k, c.v,
+                       c.block_table, q, sel, prior_len, chunk_len, d.num_kv_heads, G, d.top_k,
+                       sl2, out);
+  else
+    hipLaunchKernelGGL(prefill_attn_kernel<128>, grid, dim3(256), 0, stream, c.k, c.v,
+                       c.block_table, q, sel, prior_len, chunk_len, d.num_kv_heads, G, d.top_k,
+                       sl2, out);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,178 @@
+/*
+ * msa.h -- C ABI of libmsa.so: MiniMax Sparse Attention (MSA) decode and
+ * chunked prefill on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the attention block of "MiniMax wird dünn:
+ * M3-Attention anhand eines einzigen Diagramms entschlüsselt"
+ * (atlascloud.ai), section 1 "Was das Diagramm zeigt":
+ *   Step 1 (index branch): each GQA group has index queries; a single index-key
+ *     head is shared by every group; token scores are Q_idx . K_idx^T; "Block
+ *     Max Pool" keeps the largest score of each fixed-size block; TopK keeps
+ *     the k best blocks per group (index lists I_1, I_2, ...).
+ *   Step 2 (sparse branch): every query head of a group runs plain softmax
+ *     attention over the real, uncompressed keys/values of its group's kept
+ *     blocks only (traeai.com summary of the M3 live session, highlight 1).
+ * Parameters the page leaves open are fixed as follows: the index score is the
+ * raw dot product; the index heads of a group (and, in prefill, the queries of
+ * a tile) are pooled by max together with the block's tokens; k counts the
+ * current block, which is always kept and never scored; only blocks before it
+ * are eligible; ranking is by (score descending, block index ascending); query
+ * head j belongs to group j / (num_q_heads / num_kv_heads).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller; nothing is
+ *   copied between host and device, nothing is allocated, the library keeps
+ *   no pointer after returning, and no call synchronises.  Work is enqueued
+ *   on `stream` (a hipStream_t; NULL = the default stream) in order.
+ * - bf16 = IEEE bfloat16 stored as uint16; f32 = IEEE binary32.
+ * - Arguments are validated on the host before anything is launched; a
+ *   rejected call launches nothing and returns a negative msa_status;
+ *   msa_last_error() then describes it (thread-local).  A failed launch
+ *   returns MSA_ERR_HIP.  No C++ exception crosses this interface.
+ * - Device-side data errors (a block-table entry outside [0, num_pages), a
+ *   seq_len larger than max_blocks_per_seq * block_size) are not detected
+ *   and give undefined results.
+ * - Supported set: head_dim 128, idx_dim 64, block_size 64 or 128,
+ *   1 <= top_k <= 64, num_idx_heads in {1, 2, 4, 8, 16},
+ *   num_kv_heads * num_idx_heads <= 64, group size num_q_heads/num_kv_heads
+ *   in 1..16.  Other values return MSA_ERR_UNSUPPORTED.
+ *
+ * Paged KV cache (one page holds one KV block of block_size tokens)
+ * -----------------------------------------------------------------
+ *   k      bf16 [num_pages][Hkv][B][D]   keys, token-major within a page
+ *   v      bf16 [num_pages][Hkv][D][B]   values, transposed within a page
+ *   idx_k  bf16 [num_pages][B][d_i]      the single shared index-key head
+ *   block_table int32 [batch][max_blocks_per_seq]: logical block b of
+ *          sequence s lives in page block_table[s*max_blocks_per_seq + b]
+ * The caller has already written the current token's (decode) or the
+ * chunk's (prefill) keys, values and index keys into the cache.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARGUMENT = -1, /* null pointer, inconsistent sizes      */
+  MSA_ERR_UNSUPPORTED = -2,      /* valid but outside the supported set    */
+  MSA_ERR_WORKSPACE = -3,        /* workspace missing or too small         */
+  MSA_ERR_HIP = -4               /* a HIP launch or runtime call failed    */
+} msa_status;
+
+typedef struct {
+  int32_t num_q_heads;   /* Hq                                            */
+  int32_t num_kv_heads;  /* Hkv = number of GQA groups                    */
+  int32_t head_dim;      /* D                                             */
+  int32_t num_idx_heads; /* n_i index queries per group                   */
+  int32_t idx_dim;       /* d_i                                           */
+  int32_t block_size;    /* B tokens per block (= page)                   */
+  int32_t top_k;         /* k kept blocks per group, own block included   */
+  float softmax_scale;   /* applied to attention scores only, e.g. 1/sqrt(D) */
+} msa_params;
+
+typedef struct {
+  const void *k;              /* bf16 [num_pages][Hkv][B][D]  */
+  const void *v;              /* bf16 [num_pages][Hkv][D][B]  */
+  const void *idx_k;          /* bf16 [num_pages][B][d_i]     */
+  const int32_t *block_table; /* int32 [batch][max_blocks_per_seq] */
+  int32_t num_pages;
+  int32_t max_blocks_per_seq;
+} msa_paged_kv;
+
+/* ------------------------------------------------------------------ decode
+ * One decode step for a batch of sequences (Step 1 + TopK + Step 2).
+ * Sequence s holds seq_lens[s] >= 1 tokens, the last being the current one;
+ * its own block is c = (seq_lens[s]-1)/B; blocks 0..c-1 are scored.
+ *   q        bf16 [batch][Hq][D]
+ *   idx_q    bf16 [batch][Hkv][n_i][d_i]
+ *   seq_lens int32 [batch]            (device)
+ *   max_seq_len  host upper bound of seq_lens (sizes the launch grid; a
+ *                smaller bound than a real length gives wrong results)
+ *   out      f32 [batch][Hq][D]
+ *   sel      int32 [batch][Hkv][top_k] or NULL: kept blocks, ascending,
+ *            padded with -1
+ *   workspace  device memory of at least msa_decode_workspace_bytes(); its
+ *              contents on entry do not matter.
+ */
+size_t msa_decode_workspace_bytes(const msa_params *params, int32_t batch,
+                                  int32_t max_blocks_per_seq);
+
+msa_status msa_decode(const msa_params *params, const msa_paged_kv *kv,
+                      const void *q, const void *idx_q, const int32_t *seq_lens,
+                      int32_t batch, int32_t max_seq_len, float *out,
+                      int32_t *sel, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* Step 1 of decode alone (index scores + block max pool):
+ *   pooled f32 [batch][Hkv][max_blocks_per_seq]; entries b < c are written,
+ *   the others are left untouched. */
+msa_status msa_index_score_decode(const msa_params *params,
+                                  const msa_paged_kv *kv, const void *idx_q,
+                                  const int32_t *seq_lens, int32_t batch,
+                                  int32_t max_seq_len, float *pooled,
+                                  void *stream);
+
+/* ----------------------------------------------------------------- prefill
+ * One chunk of a single sequence: chunk_len >= 1 new queries at positions
+ * prior_len .. prior_len+chunk_len-1 (their K/V/index keys already cached).
+ * Tile t is the set of chunk queries inside absolute block
+ * c_t = prior_len/B + t, for t in [0, num_tiles) with
+ * num_tiles = ceil((prior_len+chunk_len)/B) - prior_len/B.  A tile is scored
+ * as one unit (its queries pooled like index heads) with c_t as its own
+ * block; query i attends to tokens <= prior_len + i of its tile's kept blocks.
+ *   q      bf16 [chunk_len][Hq][D]
+ *   idx_q  bf16 [chunk_len][Hkv][n_i][d_i]
+ *   out    f32 [chunk_len][Hq][D]
+ *   sel    int32 [num_tiles][Hkv][top_k] or NULL (ascending, -1 padded)
+ * block_table row 0 is used; it must cover prior_len+chunk_len tokens. */
+size_t msa_prefill_workspace_bytes(const msa_params *params, int32_t prior_len,
+                                   int32_t chunk_len,
+                                   int32_t max_blocks_per_seq);
+
+msa_status msa_prefill_chunk(const msa_params *params, const msa_paged_kv *kv,
+                             const void *q, const void *idx_q,
+                             int32_t prior_len, int32_t chunk_len, float *out,
+                             int32_t *sel, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/* Step 1 of prefill alone: pooled f32 [num_tiles][Hkv][max_blocks_per_seq];
+ * entries b < c_t are written, the others are left untouched. */
+msa_status msa_index_score_prefill(const msa_params *params,
+                                   const msa_paged_kv *kv, const void *idx_q,
+                                   int32_t prior_len, int32_t chunk_len,
+                                   float *pooled, void *stream);
+
+/* TopK of prefill alone, from pooled scores as written by
+ * msa_index_score_prefill: sel int32 [num_tiles][Hkv][top_k]. */
+msa_status msa_block_topk_prefill(const msa_params *params,
+                                  int32_t prior_len, int32_t chunk_len,
+                                  int32_t max_blocks_per_seq,
+                                  const float *pooled, int32_t *sel,
+                                  void *stream);
+
+/* Step 2 of prefill alone, for a given selection sel [num_tiles][Hkv][top_k]
+ * (ascending, -1 padded, every entry <= its tile's own block). */
+msa_status msa_sparse_attn_prefill(const msa_params *params,
+                                   const msa_paged_kv *kv, const void *q,
+                                   int32_t prior_len, int32_t chunk_len,
+                                   const int32_t *sel, float *out,
+                                   void *stream);
+
+/* Text of the last non-OK status returned on this thread. */
+const char *msa_last_error(void);
+
+/* Library version string. */
+const char *msa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H_ */

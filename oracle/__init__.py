@@ -72,8 +72,10 @@ def lib():
         L.msa_oracle_prefill.argtypes = [P, C, vp, vp, i32, i32, vp, i32, vp, vp, vp]
         L.msa_oracle_attend_prefill.argtypes = [P, C, vp, i32, i32, vp, i32, vp, vp]
         L.msa_oracle_select.argtypes = [vp, i32, i32, vp]
+        L.msa_oracle_block_scores.argtypes = [P, C, i32, vp, i32, i32, i32, vp, i32, vp]
         for f in ("msa_oracle_decode", "msa_oracle_attend_decode", "msa_oracle_prefill",
-                  "msa_oracle_attend_prefill", "msa_oracle_select", "msa_oracle_max_threads"):
+                  "msa_oracle_attend_prefill", "msa_oracle_select", "msa_oracle_max_threads",
+                  "msa_oracle_block_scores"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -99,14 +101,23 @@ def _ptr(a: Optional[np.ndarray]):
 
 
 class _Prepared:
-    """Host copies of a case's cache, kept alive for the C calls."""
+    """Host copies of a case's cache, kept alive for the C calls.
 
-    def __init__(self, case):
+    With ``kv_pages`` given, only those pages of K and V are copied; the other
+    pages of the host arrays stay zero (and, being calloc'ed, take no memory),
+    which lets very long contexts be checked for the blocks actually used."""
+
+    def __init__(self, case, kv_pages=None):
         sh, cache = case.shape, case.cache
         self.params = _Params(sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.num_idx_heads,
                               sh.idx_dim, sh.block_size, sh.top_k, sh.softmax_scale)
-        self.k = _host_u16(cache.k)
-        self.v = _host_u16(cache.v)
+        if kv_pages is None:
+            self.k = _host_u16(cache.k)
+            self.v = _host_u16(cache.v)
+        else:
+            self.k = np.zeros(tuple(cache.k.shape), dtype=np.int16)
+            self.v = np.zeros(tuple(cache.v.shape), dtype=np.int16)
+            self.fill_pages(case, kv_pages)
         self.idx_k = _host_u16(cache.idx_k)
         self.bt = _host_i32(cache.block_table)
         self.cache = _Cache(_ptr(self.k), _ptr(self.v), _ptr(self.idx_k), _ptr(self.bt),
@@ -115,8 +126,18 @@ class _Prepared:
         self.idx_q = _host_u16(case.idx_q)
 
 
-def prepare(case) -> _Prepared:
-    return _Prepared(case)
+    def fill_pages(self, case, pages):
+        """Copy the listed pages of K and V into the host arrays."""
+        idx = torch.as_tensor(sorted(set(int(p) for p in pages)), dtype=torch.long)
+        if idx.numel() == 0:
+            return
+        dev = case.cache.k.device
+        self.k[idx.numpy()] = case.cache.k[idx.to(dev)].cpu().view(torch.int16).numpy()
+        self.v[idx.numpy()] = case.cache.v[idx.to(dev)].cpu().view(torch.int16).numpy()
+
+
+def prepare(case, kv_pages=None) -> _Prepared:
+    return _Prepared(case, kv_pages)
 
 
 def decode(case, prepared: Optional[_Prepared] = None, want_pooled: bool = True) -> dict:
@@ -209,3 +230,27 @@ def select(scores: np.ndarray, own: int, k: int) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle select rejected its arguments")
     return sel
+
+
+def block_scores(case, group: int, blocks: Sequence[int], seq: int = 0, tile: Optional[int] = None,
+                 prepared: Optional[_Prepared] = None) -> np.ndarray:
+    """Pooled index scores of the listed blocks, for decode sequence ``seq`` or,
+    when ``tile`` is given, for that prefill tile."""
+    P = prepared or _Prepared(case, kv_pages=[])
+    bl = _host_i32(list(blocks))
+    out = np.zeros(len(bl), dtype=np.float64)
+    if tile is None:
+        sh = case.shape
+        row = sh.num_kv_heads * sh.num_idx_heads * sh.idx_dim
+        iq = P.idx_q.reshape(case.batch, -1)[seq]
+        iq = np.ascontiguousarray(iq[:row])
+        q0, q1, s = 0, 1, seq
+    else:
+        iq = P.idx_q
+        q0, q1 = tile_rows(case, tile)
+        s = 0
+    rc = lib().msa_oracle_block_scores(ctypes.byref(P.params), ctypes.byref(P.cache), s, _ptr(iq),
+                                       q0, q1, group, _ptr(bl), len(bl), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle block_scores rejected its arguments")
+    return out

@@ -390,3 +390,23 @@ int msa_oracle_attend_prefill(const oracle_params *p, const oracle_cache *c,
   return prefill_impl(p, c, q, NULL, prior_len, chunk_len, tiles, n_tiles, out,
                       NULL, sel, NULL);
 }
+
+/*
+ * Step 1 for listed blocks only: out[i] = block score of blocks[i] for group g
+ * of sequence seq, pooled over the query rows [q0, q1) of idx_q
+ * ([query][Hkv][n_i][d_i]; decode: the sequence's own row, q0 = 0, q1 = 1).
+ * Lets tests check single pooled scores of very long contexts.
+ */
+int msa_oracle_block_scores(const oracle_params *p, const oracle_cache *c, int32_t seq,
+                            const uint16_t *idx_q, int32_t q0, int32_t q1, int32_t g,
+                            const int32_t *blocks, int32_t n, double *out) {
+  if (check(p, c) || !idx_q || !blocks || !out || q0 < 0 || q1 <= q0 || g < 0 ||
+      g >= p->num_kv_heads || n < 0)
+    return -1;
+  for (int32_t i = 0; i < n; i++)
+    if (blocks[i] < 0 || blocks[i] >= c->max_blocks) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int32_t i = 0; i < n; i++)
+    out[i] = block_score(p, c, seq, idx_q, q0, q1, g, blocks[i]);
+  return 0;
+}

@@ -1,0 +1,142 @@
+"""The C ABI library on the CPU: it loads, exports every entry point that
+include/msa.h declares, and rejects bad arguments on the host before anything
+is launched (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import block_sparse_long_10_amd as msa
+from block_sparse_long_10_amd import Params, PagedKV
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+FAKE = 0x10000  # a non-null address; never dereferenced by a rejected call
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["msa_decode", "msa_prefill_chunk", "msa_decode_workspace_bytes",
+              "msa_prefill_workspace_bytes", "msa_last_error", "msa_index_score_decode",
+              "msa_index_score_prefill", "msa_block_topk_prefill", "msa_sparse_attn_prefill"]:
+        assert n in names
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = ctypes.CDLL(msa.library_path())
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert msa.msa_version().startswith("msa-mi355x")
+
+
+def good_params(**kw):
+    p = dict(num_q_heads=64, num_kv_heads=8, head_dim=128, num_idx_heads=4, idx_dim=64,
+             block_size=128, top_k=16, softmax_scale=128 ** -0.5)
+    p.update(kw)
+    return Params(**p)
+
+
+def fake_kv(num_pages=100, max_blocks=50):
+    return PagedKV(FAKE, FAKE, FAKE, FAKE, num_pages, max_blocks)
+
+
+def decode_status(p, kv, batch=2, max_seq_len=1000, ws_bytes=None, **null):
+    L = msa.lib()
+    if ws_bytes is None:
+        ws_bytes = L.msa_decode_workspace_bytes(ctypes.byref(p), batch, kv.max_blocks_per_seq) \
+            if p is not None and kv is not None else 0
+    args = dict(q=FAKE, idx_q=FAKE, seq_lens=FAKE, out=FAKE, ws=FAKE)
+    args.update(null)
+    return L.msa_decode(ctypes.byref(p) if p is not None else None,
+                        ctypes.byref(kv) if kv is not None else None, args["q"], args["idx_q"],
+                        args["seq_lens"], batch, max_seq_len, args["out"], None, args["ws"],
+                        ws_bytes, None)
+
+
+@pytest.mark.parametrize("change,status,msg", [
+    (dict(num_q_heads=60), INVALID, "multiple"),
+    (dict(top_k=0), INVALID, ">= 1"),
+    (dict(head_dim=64), UNSUPPORTED, "head_dim"),
+    (dict(idx_dim=128), UNSUPPORTED, "idx_dim"),
+    (dict(block_size=32), UNSUPPORTED, "block_size"),
+    (dict(top_k=65), UNSUPPORTED, "top_k"),
+    (dict(num_idx_heads=3), UNSUPPORTED, "num_idx_heads"),
+    (dict(num_idx_heads=16), UNSUPPORTED, "num_kv_heads * num_idx_heads"),
+    (dict(num_q_heads=256), UNSUPPORTED, "group size"),
+    (dict(softmax_scale=float("inf")), INVALID, "finite"),
+])
+def test_decode_rejects_bad_params(change, status, msg):
+    assert decode_status(good_params(**change), fake_kv()) == status
+    assert msg in msa.msa_last_error()
+
+
+def test_decode_rejects_bad_arguments():
+    p = good_params()
+    assert decode_status(None, fake_kv()) == INVALID
+    assert decode_status(p, None) == INVALID
+    assert decode_status(p, PagedKV(FAKE, None, FAKE, FAKE, 10, 10)) == INVALID
+    assert decode_status(p, fake_kv(num_pages=0)) == INVALID
+    assert decode_status(p, fake_kv(), q=None) == INVALID
+    assert decode_status(p, fake_kv(), out=None) == INVALID
+    assert decode_status(p, fake_kv(), batch=0) == INVALID
+    assert decode_status(p, fake_kv(), max_seq_len=0) == INVALID
+    assert decode_status(p, fake_kv(max_blocks=4), max_seq_len=513) == INVALID
+    assert "max_seq_len" in msa.msa_last_error()
+    need = msa.lib().msa_decode_workspace_bytes(ctypes.byref(p), 2, 50)
+    assert decode_status(p, fake_kv(), ws_bytes=need - 1) == WORKSPACE
+    assert decode_status(p, fake_kv(), ws=None) == WORKSPACE
+
+
+def test_workspace_sizes():
+    L = msa.lib()
+    p = good_params()
+    a = L.msa_decode_workspace_bytes(ctypes.byref(p), 1, 8192)
+    b = L.msa_decode_workspace_bytes(ctypes.byref(p), 8, 8192)
+    assert 0 < a < b
+    assert a >= 8 * 8192 * 4  # pooled scores alone
+    assert L.msa_decode_workspace_bytes(ctypes.byref(good_params(head_dim=64)), 1, 10) == 0
+    pf = L.msa_prefill_workspace_bytes(ctypes.byref(p), 1048576, 8192, 8256)
+    assert pf >= 64 * 8 * 8256 * 4
+    assert L.msa_prefill_workspace_bytes(ctypes.byref(p), 0, 0, 10) == 0
+
+
+def test_prefill_rejects_bad_arguments():
+    L = msa.lib()
+    p = good_params()
+    kv = fake_kv(num_pages=100, max_blocks=40)
+    ws = L.msa_prefill_workspace_bytes(ctypes.byref(p), 1000, 100, 40)
+
+    def st(prior, chunk, params=p, kvv=kv, wsb=ws, q=FAKE):
+        return L.msa_prefill_chunk(ctypes.byref(params), ctypes.byref(kvv), q, FAKE, prior, chunk,
+                                   FAKE, None, FAKE, wsb, None)
+
+    assert st(1000, 0) == INVALID
+    assert st(-1, 10) == INVALID
+    assert st(5000, 200) == INVALID       # beyond max_blocks * block_size
+    assert st(1000, 100, q=None) == INVALID
+    assert st(1000, 100, wsb=ws - 1) == WORKSPACE
+    big = good_params(num_kv_heads=4, num_q_heads=32, num_idx_heads=8)
+    assert st(1000, 100, params=big) == UNSUPPORTED   # block_size * num_idx_heads > 512
+    assert L.msa_index_score_prefill(ctypes.byref(p), ctypes.byref(kv), None, 10, 10, FAKE,
+                                     None) == INVALID
+    assert L.msa_block_topk_prefill(ctypes.byref(p), 10, 10, 40, FAKE, None, None) == INVALID
+    assert L.msa_sparse_attn_prefill(ctypes.byref(p), ctypes.byref(kv), FAKE, 10, 10, None, FAKE,
+                                     None) == INVALID
+
+
+def test_binding_has_no_cpu_path():
+    p = msa.make_params(8, 1, block_size=64, top_k=8)
+    k = torch.zeros(4, 1, 64, 128, dtype=torch.bfloat16)
+    with pytest.raises(TypeError, match="GPU tensor"):
+        msa.make_kv(k, k, torch.zeros(4, 64, 64, dtype=torch.bfloat16),
+                    torch.zeros(1, 4, dtype=torch.int32))

@@ -1,0 +1,155 @@
+"""GPU parity of MSA decode (index score + pooling, TopK, sparse attention)
+against the oracle, through the C ABI.  Marked gpu."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from msa_inputs import Shape, GQA64, make_decode_case, make_workload
+from tests.gpu_util import (check_out, check_pooled, check_selection, run_decode)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _announce(what):
+    print("\n[gpu decode] " + what, flush=True)
+    sys.stdout.flush()
+
+
+def _full_check(case, exact_sel=False):
+    """Oracle on the whole cache (small cases)."""
+    g = run_decode(case)
+    P = oracle.prepare(case)
+    ref = oracle.decode(case, prepared=P)
+    sh = case.shape
+    kinds = []
+    for s, L in enumerate(case.lengths):
+        own = (L - 1) // sh.block_size
+        for gi in range(sh.num_kv_heads):
+            check_pooled(g["pooled"][s, gi, :own], ref["pooled"][s, gi, :own], "s%d g%d" % (s, gi))
+            kinds.append(check_selection(g["sel"][s, gi], ref["pooled"][s, gi], own, sh.top_k,
+                                         exact_only=exact_sel))
+    ref_out = oracle.attend_decode(case, g["sel"], prepared=P)
+    worst = check_out(g["out"], ref_out)
+    return g, ref, worst, kinds
+
+
+def _big_check(case):
+    """Oracle with only the needed K/V pages on the host (long contexts)."""
+    g = run_decode(case)
+    P = oracle.prepare(case, kv_pages=[])
+    ref = oracle.decode(case, prepared=P)        # scores + selection (K/V unused here)
+    sh = case.shape
+    bt = case.cache.block_table.cpu().numpy()
+    kinds, pages = [], set()
+    for s, L in enumerate(case.lengths):
+        own = (L - 1) // sh.block_size
+        for gi in range(sh.num_kv_heads):
+            check_pooled(g["pooled"][s, gi, :own], ref["pooled"][s, gi, :own], "s%d g%d" % (s, gi))
+            kinds.append(check_selection(g["sel"][s, gi], ref["pooled"][s, gi], own, sh.top_k))
+            pages.update(int(bt[s, b]) for b in g["sel"][s, gi] if b >= 0)
+    P.fill_pages(case, pages)
+    ref_out = oracle.attend_decode(case, g["sel"], prepared=P)
+    worst = check_out(g["out"], ref_out)
+    return g, worst, kinds
+
+
+SMALL = Shape(num_q_heads=16, num_kv_heads=2, num_idx_heads=4, block_size=64, top_k=8)
+
+
+@pytest.mark.parametrize("lengths,seed", [
+    ([1, 63, 64, 65, 1000, 4097, 130, 448, 449], 101),
+    ([5000, 12345, 777], 102),
+])
+def test_decode_small_ragged(lengths, seed):
+    _announce("small ragged %s" % lengths)
+    case = make_decode_case(SMALL, lengths, seed, device=DEV, shuffle_pages=True, poison_frac=0.05)
+    _, _, worst, kinds = _full_check(case)
+    print("worst row err %.3g, selections %s" % (worst, {k: kinds.count(k) for k in set(kinds)}))
+
+
+@pytest.mark.parametrize("shape", [
+    Shape(num_q_heads=8, num_kv_heads=8, num_idx_heads=1, block_size=128, top_k=16),
+    Shape(num_q_heads=12, num_kv_heads=4, num_idx_heads=2, block_size=128, top_k=5),
+    Shape(num_q_heads=64, num_kv_heads=4, num_idx_heads=8, block_size=64, top_k=64),
+    Shape(num_q_heads=16, num_kv_heads=4, num_idx_heads=16, block_size=128, top_k=1),
+    Shape(num_q_heads=3, num_kv_heads=3, num_idx_heads=4, block_size=64, top_k=2),
+    Shape(num_q_heads=48, num_kv_heads=16, num_idx_heads=4, block_size=128, top_k=9),
+])
+def test_decode_shape_variants(shape):
+    _announce("shape %s" % (shape,))
+    case = make_decode_case(shape, [9000, 257, 128, 3333], 103, device=DEV, shuffle_pages=True)
+    _, _, worst, _ = _full_check(case)
+    print("worst row err %.3g" % worst)
+
+
+def test_decode_workload_b1_L4k():
+    _announce("decode_b1_L4k")
+    case = make_workload("decode_b1_L4k", DEV)
+    _, _, worst, kinds = _full_check(case)
+    print("worst row err %.3g, selections %s" % (worst, kinds))
+
+
+@pytest.mark.parametrize("name", ["decode_b8_L128k", "decode_b1_L1M", "decode_paged_b32"])
+def test_decode_workload_full_size(name):
+    _announce(name)
+    case = make_workload(name, DEV)
+    g, worst, kinds = _big_check(case)
+    print("worst row err %.3g, selections %s" % (worst, {k: kinds.count(k) for k in set(kinds)}))
+    if case.shifted:
+        # the shifted blocks rank above the plain ones: most of them are kept
+        hit = sum(len(set(v) & set(g["sel"][s, gi].tolist()))
+                  for (s, gi), v in case.shifted.items())
+        tot = sum(len(v) for v in case.shifted.values())
+        print("shifted blocks kept: %d of %d" % (hit, tot))
+        assert hit >= 0.5 * tot
+
+
+def test_decode_constructed_exact_ties():
+    _announce("exact ties")
+    case = make_decode_case(SMALL, [3000, 2000], 104, device=DEV)
+    ik = case.cache.idx_k
+    bt = case.cache.block_table
+    # make blocks 3, 9, 20, 31 bit-identical and the clear best of sequence 0;
+    # blocks 5 and 6 identical in sequence 1
+    src = int(bt[0, 3])
+    ik[src] = (ik[src].float() * 0.5 + 1.5).to(torch.bfloat16)
+    for b in (9, 20, 31):
+        ik[int(bt[0, b])] = ik[src]
+    ik[int(bt[1, 6])] = ik[int(bt[1, 5])]
+    case.idx_q[:] = case.idx_q.abs()
+    g, ref, _, _ = _full_check(case, exact_sel=True)
+    for gi in range(SMALL.num_kv_heads):
+        row = g["sel"][0, gi].tolist()
+        assert {3, 9, 20, 31} <= set(row)
+    np.testing.assert_array_equal(g["sel"], ref["sel"])
+
+
+def test_decode_tie_fallback_paths():
+    _announce("all-equal and heavily tied scores")
+    # every pooled score equal: the lowest indices win
+    case = make_decode_case(SMALL, [6000, 3001], 105, device=DEV)
+    case.cache.idx_k.zero_()
+    g, ref, _, _ = _full_check(case, exact_sel=True)
+    for s, L in enumerate(case.lengths):
+        own = (L - 1) // SMALL.block_size
+        assert g["sel"][s, 0].tolist() == list(range(SMALL.top_k - 1)) + [own]
+    # few distinct values, hundreds of blocks per value: histogram refinement
+    case = make_decode_case(SMALL, [40000, 20000], 106, device=DEV)
+    q = case.cache.idx_k.float()
+    case.cache.idx_k.copy_((torch.round(q * 2) / 2).clamp(-1, 1).to(torch.bfloat16))
+    case.idx_q.fill_(0.25)
+    _full_check(case, exact_sel=True)
+
+
+def test_decode_deterministic():
+    _announce("determinism")
+    case = make_decode_case(GQA64, [70000, 9999, 131072], 107, device=DEV, shuffle_pages=True)
+    a = run_decode(case, with_pooled=False)
+    b = run_decode(case, with_pooled=False)
+    np.testing.assert_array_equal(a["sel"], b["sel"])
+    assert np.array_equal(a["out"], b["out"])
