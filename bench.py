@@ -1,0 +1,334 @@
+#!/usr/bin/env python3
+"""Benchmark of the MSA hot path on one MI355X.
+
+Headline: MSA decode latency per step at a 1,048,576-token context
+(decode_b1_L1M: batch 1, 64 query / 8 KV heads, head dim 128, 4 index heads x
+64 per group, block 128, top-k 16), one attention layer.  One step is one
+msa_decode call: index scores + block max pool, TopK, sparse attention and
+the partial merge.  The line also carries the chunked-prefill throughput
+(prefill_P1M_C8k: 8192 queries after 1,048,576 tokens) with the MFMA use of
+its kernels, the roofline of the dominant decode kernel, and the oracle timed
+on the host cores.
+
+Inputs are synthetic and seeded (msa_inputs), generated on the GPU and
+resident in HBM before timing.  Decode rotates over several independent
+buffer sets (as consecutive layers of a model would) so the 128 MiB of index
+keys are never served from the 256 MB Infinity Cache.
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, datasheet
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, datasheet
+DECODE_WORKLOAD = "decode_b1_L1M"
+PREFILL_WORKLOAD = "prefill_P1M_C8k"
+KERNEL_SOURCES = ["block_sparse_long_10_amd/csrc/index_score.hip",
+                  "block_sparse_long_10_amd/csrc/msa_device.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_index_score_decode_L1M.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the decode index kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def clone_decode_case(case):
+    import copy
+    c = copy.copy(case)
+    c.cache = copy.copy(case.cache)
+    c.cache.k = case.cache.k.clone()
+    c.cache.v = case.cache.v.clone()
+    c.cache.idx_k = case.cache.idx_k.clone()
+    c.cache.block_table = case.cache.block_table.clone()
+    c.q = case.q.clone()
+    c.idx_q = case.idx_q.clone()
+    c.seq_lens = case.seq_lens.clone()
+    return c
+
+
+def decode_algorithmic_bytes(case):
+    """Bytes a decode step must move at least (per the definition): every
+    index key of every eligible block, the K/V of the kept blocks, the
+    queries, index queries, block table and the output."""
+    sh = case.shape
+    B, D, di = sh.block_size, sh.head_dim, sh.idx_dim
+    idx_keys = kept_kv = 0
+    for L in case.lengths:
+        own = (L - 1) // B
+        idx_keys += own * B * di * 2
+        kept_tokens = min(sh.top_k - 1, own) * B + (L - own * B)
+        kept_kv += kept_tokens * D * 2 * 2 * sh.num_kv_heads
+    small = (case.q.numel() * 2 + case.idx_q.numel() * 2 + case.cache.block_table.numel() * 4
+             + case.batch * sh.num_q_heads * D * 4)
+    return idx_keys, kept_kv, small
+
+
+class _Binding:
+    """Parameter and cache descriptors of a seeded case for the C ABI."""
+
+    def __init__(self, msa):
+        self.msa = msa
+
+    def params_of(self, sh):
+        return self.msa.make_params(sh.num_q_heads, sh.num_kv_heads, sh.head_dim,
+                                    sh.num_idx_heads, sh.idx_dim, sh.block_size, sh.top_k,
+                                    sh.softmax_scale)
+
+    def kv_of(self, case):
+        c = case.cache
+        return self.msa.make_kv(c.k, c.v, c.idx_k, c.block_table)
+
+
+def run_decode_bench(args, torch, msa, mi, gu):
+    log("[bench] generating %s x%d buffer sets" % (DECODE_WORKLOAD, args.rotate))
+    base = mi.make_workload(DECODE_WORKLOAD, "cuda")
+    sets = [base] + [clone_decode_case(base) for _ in range(args.rotate - 1)]
+    sh = base.shape
+    p = gu.params_of(sh)
+    kvs = [gu.kv_of(c) for c in sets]
+    batch, maxL, mb = base.batch, max(base.lengths), base.cache.max_blocks
+    out = torch.empty(batch, sh.num_q_heads, sh.head_dim, device="cuda")
+    sel = torch.empty(batch, sh.num_kv_heads, sh.top_k, dtype=torch.int32, device="cuda")
+    ws = torch.empty(msa.msa_decode_workspace_bytes(p, batch, mb), dtype=torch.uint8,
+                     device="cuda")
+    pooled = torch.empty(batch, sh.num_kv_heads, mb, device="cuda")
+
+    def step(i):
+        c = sets[i % len(sets)]
+        msa.msa_decode(p, kvs[i % len(sets)], c.q, c.idx_q, c.seq_lens, batch, maxL, out, sel, ws)
+
+    def index_only(i):
+        c = sets[i % len(sets)]
+        msa.msa_index_score_decode(p, kvs[i % len(sets)], c.idx_q, c.seq_lens, batch, maxL,
+                                   pooled)
+
+    def timed(fn, n, warm):
+        for i in range(warm):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n  # ms
+
+    log("[bench] decode: %d warmup + %d timed steps" % (args.warmup, args.steps))
+    ms_step = timed(step, args.steps, args.warmup)
+    log("[bench] decode index kernel alone")
+    ms_index = timed(index_only, args.steps, args.warmup)
+    idx_bytes, kv_bytes, small = decode_algorithmic_bytes(base)
+    own = (maxL - 1) // sh.block_size
+    index_bytes = idx_bytes + base.idx_q.numel() * 2 + base.cache.block_table.numel() * 4 \
+        + batch * sh.num_kv_heads * own * 4
+    step_bytes = idx_bytes + kv_bytes + small
+    return {
+        "ms_step": ms_step, "ms_index": ms_index, "index_bytes": index_bytes,
+        "step_bytes": step_bytes, "case": base, "sets": sets, "p": p, "kvs": kvs,
+    }
+
+
+def run_prefill_bench(args, torch, msa, mi, gu):
+    log("[bench] generating %s" % PREFILL_WORKLOAD)
+    case = mi.make_workload(PREFILL_WORKLOAD, "cuda")
+    sh = case.shape
+    p, kv = gu.params_of(sh), gu.kv_of(case)
+    P, C, mb, nt = case.prior_len, case.chunk_len, case.cache.max_blocks, case.num_tiles
+    out = torch.empty(C, sh.num_q_heads, sh.head_dim, device="cuda")
+    sel = torch.empty(nt, sh.num_kv_heads, sh.top_k, dtype=torch.int32, device="cuda")
+    ws = torch.empty(msa.msa_prefill_workspace_bytes(p, P, C, mb), dtype=torch.uint8,
+                     device="cuda")
+    pooled = torch.empty(nt, sh.num_kv_heads, mb, device="cuda")
+
+    def timed(fn, n, warm):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    n, w = args.prefill_steps, args.prefill_warmup
+    log("[bench] prefill: %d warmup + %d timed chunks" % (w, n))
+    ms_chunk = timed(lambda: msa.msa_prefill_chunk(p, kv, case.q, case.idx_q, P, C, out, sel, ws),
+                     n, w)
+    ms_index = timed(lambda: msa.msa_index_score_prefill(p, kv, case.idx_q, P, C, pooled), n, w)
+    ms_topk = timed(lambda: msa.msa_block_topk_prefill(p, P, C, mb, pooled, sel), n, w)
+    ms_attn = timed(lambda: msa.msa_sparse_attn_prefill(p, kv, case.q, P, C, sel, out), n, w)
+    # algorithmic flops: every (query, eligible key) pair x all index rows x d_i
+    # multiply-adds; attention over the kept tokens visible to each query
+    B, rows = sh.block_size, sh.num_kv_heads * sh.num_idx_heads
+    pairs = 0
+    attn_pairs = 0
+    for t in range(nt):
+        own = P // B + t
+        q0, q1 = max(0, own * B - P), min(C, (own + 1) * B - P)
+        pairs += (q1 - q0) * own * B
+        kept = min(sh.top_k - 1, own) * B
+        for i in range(q0, q1):
+            attn_pairs += kept + (P + i - own * B + 1)
+    index_flops = pairs * rows * sh.idx_dim * 2
+    attn_flops = attn_pairs * sh.num_q_heads * sh.head_dim * 4
+    return {"case": case, "ms_chunk": ms_chunk, "ms_index": ms_index, "ms_topk": ms_topk,
+            "ms_attn": ms_attn, "index_flops": index_flops, "attn_flops": attn_flops}
+
+
+def cpu_baseline(case, budget_s):
+    """The oracle on the host cores: whole decode steps of the same workload
+    (index scores of every block, TopK, attention), repeated for about
+    budget_s seconds; K/V pages are copied to the host for the kept blocks."""
+    import oracle
+    oracle.build()
+    log("[bench] cpu baseline: oracle decode on the host")
+    P = oracle.prepare(case, kv_pages=[])
+    first = oracle.decode(case, prepared=P)
+    bt = case.cache.block_table.cpu().numpy()
+    pages = {int(bt[s, b]) for s in range(case.batch) for g in range(case.shape.num_kv_heads)
+             for b in first["sel"][s, g] if b >= 0}
+    P.fill_pages(case, pages)
+    times = []
+    t_end = time.time() + budget_s
+    while time.time() < t_end or not times:
+        t0 = time.time()
+        oracle.decode(case, prepared=P, want_pooled=False)
+        times.append(time.time() - t0)
+        if len(times) >= 50:
+            break
+    times.sort()
+    med = times[len(times) // 2]
+    return {"value": med * 1e6, "unit": "us/step", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": "%d full decode steps of %s (median), fp64 C oracle with OpenMP"
+                      % (len(times), DECODE_WORKLOAD)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotate", type=int, default=4, help="decode buffer sets")
+    ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--prefill-warmup", type=int, default=2)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle time for the CPU baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_long_10_amd as msa
+    import msa_inputs as mi
+    gu = _Binding(msa)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    msa.lib()
+
+    dec = run_decode_bench(args, torch, msa, mi, gu)
+    pre = None if args.no_prefill else run_prefill_bench(args, torch, msa, mi, gu)
+
+    case = dec["case"]
+    sh = case.shape
+    us_step = dec["ms_step"] * 1e3
+    index_gbps = dec["index_bytes"] / (dec["ms_index"] * 1e-3) / 1e9
+    step_gbps = dec["step_bytes"] / (dec["ms_step"] * 1e-3) / 1e9
+    traffic = measured_traffic()
+    result = {
+        "metric": "MSA decode latency per step at 1M-token context (one attention layer)",
+        "value": round(us_step, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_step"], 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, generated on the GPU)",
+        "config": {"workload": DECODE_WORKLOAD, "batch": case.batch, "seq_len": case.lengths[0],
+                   "num_q_heads": sh.num_q_heads, "num_kv_heads": sh.num_kv_heads,
+                   "head_dim": sh.head_dim, "num_idx_heads": sh.num_idx_heads,
+                   "idx_dim": sh.idx_dim, "block_size": sh.block_size, "top_k": sh.top_k,
+                   "rotated_buffer_sets": args.rotate},
+        "decode_step_gbps": round(step_gbps, 1),
+        "decode_step_bytes": dec["step_bytes"],
+        "roofline": {
+            "kernel": "index_score_decode",
+            "bound": "hbm",
+            "achieved": round(index_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(index_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": dec["index_bytes"],
+            "avg_launch_us": round(dec["ms_index"] * 1e3, 3),
+        },
+    }
+    if pre is not None:
+        pc = pre["case"]
+        result["prefill"] = {
+            "workload": PREFILL_WORKLOAD,
+            "prior_len": pc.prior_len, "chunk_len": pc.chunk_len,
+            "tokens_per_s": round(pc.chunk_len / (pre["ms_chunk"] * 1e-3), 1),
+            "ms_per_chunk": round(pre["ms_chunk"], 4),
+            "index_kernel_ms": round(pre["ms_index"], 4),
+            "index_tflops": round(pre["index_flops"] / (pre["ms_index"] * 1e-3) / 1e12, 1),
+            "index_mfma_frac": round(pre["index_flops"] / (pre["ms_index"] * 1e-3) / 1e12
+                                     / BF16_PEAK_TFLOPS, 4),
+            "topk_kernel_ms": round(pre["ms_topk"], 4),
+            "attn_kernel_ms": round(pre["ms_attn"], 4),
+            "attn_tflops": round(pre["attn_flops"] / (pre["ms_attn"] * 1e-3) / 1e12, 1),
+            "attn_mfma_frac": round(pre["attn_flops"] / (pre["ms_attn"] * 1e-3) / 1e12
+                                    / BF16_PEAK_TFLOPS, 4),
+            "index_flops": pre["index_flops"], "attn_flops": pre["attn_flops"],
+            "peak_tflops": BF16_PEAK_TFLOPS,
+        }
+    if args.cpu_budget > 0:
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
