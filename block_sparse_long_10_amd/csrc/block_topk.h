@@ -3,16 +3,27 @@
 // own block always kept ("TopK" of the index branch in "MiniMax wird dünn",
 // section 1, Schritt 1).
 //
-// One 256-thread workgroup selects from scores[0 .. own) in global memory:
-//   1. range [lo, hi] of the scores (wave DPP reductions + LDS);
-//   2. LDS histogram of 256 value bins over [lo, hi]; bin(v) is monotone
-//      non-increasing in v, so every item of a lower bin outranks every item
-//      of a higher bin;
+// One 256-thread workgroup selects from scores[0 .. own).  Every score
+// becomes an order-preserving 32-bit key (-0.0 folded into +0.0), held in
+// registers when own <= 256*MAXV (all loads issued at once; empty slots hold
+// key 0, below every finite score), otherwise re-read from global memory.
+//
+// Fast path (registers, k' = k-1 <= 16): each thread takes the max of its
+// keys; wave-wide DPP bitonic sorts give T, the k'-th largest of the 256
+// thread maxima, which k' distinct scores reach, so it bounds the k'-th best
+// score from below; the few keys >= T are gathered to LDS (prefix-sum
+// offsets) and one more bitonic sort on (key, ~index) picks the winners, a
+// last one orders them by block index.  If more than 64 keys reach T (heavy
+// ties), the general path below runs instead:
+//   1. key range [lo, hi] (DPP/shuffle wave reductions + LDS);
+//   2. LDS histogram of bin = (hi - key) >> shift, at most 256 bins; the bin
+//      is monotone in the key, so every item of a lower bin outranks every
+//      item of a higher bin;
 //   3. a wave scan finds the bin b* holding the last needed item; items of
-//      lower bins are kept, the items of b* are ranked exactly (score, index)
-//      when they fit in LDS, otherwise [lo, hi] narrows to b*'s range and the
-//      histogram repeats;
-//   4. when the live range holds a single value, the lowest indices win
+//      lower bins are kept; the items of b* are ranked exactly by
+//      (key, index) when they fit in LDS, otherwise [lo, hi] narrows to b*'s
+//      range (at least 2^7 times smaller) and the histogram repeats;
+//   4. when the live range holds a single key, the lowest indices win
 //      (ballot prefix counts in index order).
 // The result (sorted ascending, own block included, -1 padded) lands in LDS.
 #pragma once
@@ -28,11 +39,11 @@ constexpr int kMaxTopK = 64;
 
 struct TopkShared {
   unsigned hist[kTopkBins];
-  float cand_v[kTopkCap];
+  uint32_t cand_k[kTopkCap];
   int cand_i[kTopkCap];
   int chosen[kMaxTopK];
-  float red_a[kTopkThreads / kWave];
-  float red_b[kTopkThreads / kWave];
+  uint32_t red_a[kTopkThreads / kWave];
+  uint32_t red_b[kTopkThreads / kWave];
   int wave_cnt[kTopkThreads / kWave];
   int n_chosen;
   int n_cand;
@@ -41,33 +52,116 @@ struct TopkShared {
   int c_eq;
 };
 
+// Order-preserving map float -> uint32 (larger score, larger key).
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  if ((u << 1) == 0u) u = 0u;  // -0.0 == +0.0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint32_t umax_(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t umin_(uint32_t a, uint32_t b) { return a < b ? a : b; }
+
+template <int N>
+__device__ __forceinline__ uint32_t row_ror_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x120 + N, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = umax_(v, row_ror_u<8>(v));
+  v = umax_(v, row_ror_u<4>(v));
+  v = umax_(v, row_ror_u<2>(v));
+  v = umax_(v, row_ror_u<1>(v));
+  v = umax_(v, (uint32_t)__shfl_xor((int)v, 16, kWave));
+  return umax_(v, (uint32_t)__shfl_xor((int)v, 32, kWave));
+}
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+  v = umin_(v, row_ror_u<8>(v));
+  v = umin_(v, row_ror_u<4>(v));
+  v = umin_(v, row_ror_u<2>(v));
+  v = umin_(v, row_ror_u<1>(v));
+  v = umin_(v, (uint32_t)__shfl_xor((int)v, 16, kWave));
+  return umin_(v, (uint32_t)__shfl_xor((int)v, 32, kWave));
+}
+
+// Keys held in registers: item i = j*256 + tid lives in key[j].
+template <int MAXV>
+struct RegKeys {
+  static constexpr int kChunks = MAXV;
+  uint32_t key[MAXV];
+  int n;
+  __device__ __forceinline__ void load(const float* __restrict__ s, int n_) {
+    n = n_;
+    const int tid = threadIdx.x;
+    float v[MAXV];
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j) {
+      const int i = j * kTopkThreads + tid;
+      v[j] = i < n ? s[i] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j) key[j] = j * kTopkThreads + tid < n ? order_key(v[j]) : 0u;
+  }
+  template <class F>
+  __device__ __forceinline__ void each(F&& f) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j) {
+      const int i = j * kTopkThreads + tid;
+      if (i < n) f(i, key[j]);
+    }
+  }
+  // f(i, key, valid) for chunks of 256 consecutive items in index order,
+  // called by all threads; stops when f returns false (a uniform decision).
+  template <class F>
+  __device__ __forceinline__ void chunks_in_order(F&& f) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j) {
+      const int i = j * kTopkThreads + tid;
+      if (!f(i, key[j], i < n)) break;
+    }
+  }
+};
+
+// Keys re-read from global memory (very long contexts).
+struct GlobalKeys {
+  const float* __restrict__ s;
+  int n;
+  template <class F>
+  __device__ __forceinline__ void each(F&& f) const {
+    for (int i = threadIdx.x; i < n; i += kTopkThreads) f(i, order_key(s[i]));
+  }
+  template <class F>
+  __device__ __forceinline__ void chunks_in_order(F&& f) const {
+    for (int c0 = 0; c0 < n; c0 += kTopkThreads) {
+      const int i = c0 + (int)threadIdx.x;
+      if (!f(i, i < n ? order_key(s[i]) : 0u, i < n)) break;
+    }
+  }
+};
+
 __device__ __forceinline__ void push_chosen(TopkShared& sh, int i) {
   const int p = atomicAdd(&sh.n_chosen, 1);
   if (p < kMaxTopK) sh.chosen[p] = i;
 }
 
-__device__ __forceinline__ int topk_bin(float v, double hi, double scale) {
-  double d = (hi - (double)v) * scale;
-  return d >= (double)(kTopkBins - 1) ? kTopkBins - 1 : (int)d;
-}
-
-// Range of the live items (lo <= v <= hi, optionally restricted to one bin).
-__device__ __forceinline__ void topk_range(const float* __restrict__ scores, int n, float lo,
-                                           float hi, bool use_bin, double dhi, double scale,
-                                           int bin, TopkShared& sh, float& out_lo, float& out_hi) {
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  float mx = -INFINITY, mn = INFINITY;
-  for (int i = tid; i < n; i += kTopkThreads) {
-    float v = scores[i];
-    bool live = v >= lo && v <= hi;
-    if (use_bin && live) live = topk_bin(v, dhi, scale) == bin;
+// Range [lo, hi] of the live keys (lo <= key <= hi, and bin == b when b >= 0).
+template <class Src>
+__device__ __forceinline__ void topk_range(const Src& src, uint32_t lo, uint32_t hi, int shift,
+                                           int b, TopkShared& sh, uint32_t& out_lo,
+                                           uint32_t& out_hi) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  uint32_t mx = 0u, mn = 0xFFFFFFFFu;
+  src.each([&](int, uint32_t key) {
+    bool live = key >= lo && key <= hi;
+    if (b >= 0) live = live && (int)((hi - key) >> shift) == b;
     if (live) {
-      mx = fmaxf(mx, v);
-      mn = fminf(mn, v);
+      mx = umax_(mx, key);
+      mn = umin_(mn, key);
     }
-  }
-  mx = wave_max(mx);
-  mn = wave_min(mn);
+  });
+  mx = wave_umax(mx);
+  mn = wave_umin(mn);
   if (lane == 0) {
     sh.red_a[wave] = mx;
     sh.red_b[wave] = mn;
@@ -77,22 +171,23 @@ __device__ __forceinline__ void topk_range(const float* __restrict__ scores, int
   mn = sh.red_b[0];
 #pragma unroll
   for (int w = 1; w < kTopkThreads / kWave; ++w) {
-    mx = fmaxf(mx, sh.red_a[w]);
-    mn = fminf(mn, sh.red_b[w]);
+    mx = umax_(mx, sh.red_a[w]);
+    mn = umin_(mn, sh.red_b[w]);
   }
   __syncthreads();
   out_lo = mn;
   out_hi = mx;
 }
 
-// Keep the `need` lowest indices among items equal to `val`.
-__device__ __forceinline__ void topk_lowest_equal(const float* __restrict__ scores, int n,
-                                                  float val, int need, TopkShared& sh) {
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+// Keep the `need` lowest indices among the items whose key equals val.
+template <class Src>
+__device__ __forceinline__ void topk_lowest_equal(const Src& src, uint32_t val, int need,
+                                                  TopkShared& sh) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   int done = 0;
-  for (int c0 = 0; c0 < n && done < need; c0 += kTopkThreads) {
-    const int i = c0 + tid;
-    const bool f = i < n && scores[i] == val;
+  src.chunks_in_order([&](int i, uint32_t key, bool valid) -> bool {
+    if (done >= need) return false;
+    const bool f = valid && key == val;
     const unsigned long long m = __ballot(f);
     const int in_wave = __popcll(m & ((1ull << lane) - 1ull));
     if (lane == 0) sh.wave_cnt[wave] = __popcll(m);
@@ -107,13 +202,159 @@ __device__ __forceinline__ void topk_lowest_equal(const float* __restrict__ scor
     if (f && before + in_wave < need) push_chosen(sh, i);
     __syncthreads();
     done += total;
+    return true;
+  });
+}
+
+// Lane exchange with lane ^ M across the wave (DPP for M <= 8, swizzle for
+// 16, bpermute for 32).  row_ror:n reads lane i-n within a row of 16.
+template <int M>
+__device__ __forceinline__ uint32_t xor_exchange(uint32_t v) {
+  const int iv = (int)v;
+  if constexpr (M == 1) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+  } else if constexpr (M == 2) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  } else if constexpr (M == 4) {
+    const int lo = __builtin_amdgcn_mov_dpp(iv, 0x12C, 0xF, 0xF, false);  // lane i+4
+    const int hi = __builtin_amdgcn_mov_dpp(iv, 0x124, 0xF, 0xF, false);  // lane i-4
+    return (uint32_t)((threadIdx.x & 4) ? hi : lo);
+  } else if constexpr (M == 8) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp(iv, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if constexpr (M == 16) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle(iv, 0x401F);  // xor 16 within 32 lanes
+  } else {
+    return (uint32_t)__shfl_xor(iv, 32, kWave);
   }
 }
 
-// All threads of the workgroup call this with identical arguments.
-// out_sel (LDS, k entries) receives the kept blocks, ascending, -1 padded.
-__device__ void block_topk(const float* __restrict__ scores, int own, int k, int* out_sel,
-                           TopkShared& sh) {
+// One compare-exchange stage of a bitonic sort: lanes pair with lane ^ J;
+// blocks of K lanes alternate direction so that the full sort (K = 64) is
+// descending from lane 0.
+template <int K, int J>
+__device__ __forceinline__ void bitonic_stage(uint32_t& hi, uint32_t& lo) {
+  const uint32_t oh = xor_exchange<J>(hi), ol = xor_exchange<J>(lo);
+  const int lane = threadIdx.x & (kWave - 1);
+  const bool take_max = ((lane & J) == 0) == ((lane & K) == 0);
+  const bool other_bigger = oh > hi || (oh == hi && ol > lo);
+  if (take_max == other_bigger) {
+    hi = oh;
+    lo = ol;
+  }
+}
+template <int K>
+__device__ __forceinline__ void bitonic_merge(uint32_t& hi, uint32_t& lo) {
+  if constexpr (K >= 64) bitonic_stage<K, 32>(hi, lo);
+  if constexpr (K >= 32) bitonic_stage<K, 16>(hi, lo);
+  if constexpr (K >= 16) bitonic_stage<K, 8>(hi, lo);
+  if constexpr (K >= 8) bitonic_stage<K, 4>(hi, lo);
+  if constexpr (K >= 4) bitonic_stage<K, 2>(hi, lo);
+  bitonic_stage<K, 1>(hi, lo);
+}
+// Sort the 64 lane values (hi, lo) of a wave descending: lane 0 largest.
+__device__ __forceinline__ void wave_sort_desc(uint32_t& hi, uint32_t& lo) {
+  bitonic_merge<2>(hi, lo);
+  bitonic_merge<4>(hi, lo);
+  bitonic_merge<8>(hi, lo);
+  bitonic_merge<16>(hi, lo);
+  bitonic_merge<32>(hi, lo);
+  bitonic_merge<64>(hi, lo);
+}
+
+// Wave inclusive prefix sum.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Fast path; returns false (leaving out_sel untouched) when more than 64
+// keys reach the bound.  Requires 1 <= keep < own and keep <= 16.
+template <int MAXV>
+__device__ __forceinline__ bool topk_fast(const RegKeys<MAXV>& src, int own, int keep, int k,
+                                          int* out_sel, TopkShared& sh) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  // thread max (tree)
+  uint32_t mx[MAXV];
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) mx[j] = src.key[j];
+#pragma unroll
+  for (int w = MAXV / 2; w >= 1; w /= 2)
+#pragma unroll
+    for (int j = 0; j < w; ++j) mx[j] = umax_(mx[j], mx[j + w]);
+  // each wave's best `keep` thread maxima, then the keep-th best of those:
+  // T, reached by `keep` distinct scores, bounds the keep-th best score
+  uint32_t a = mx[0], z = 0u;
+  wave_sort_desc(a, z);
+  if (lane < 16) sh.cand_k[wave * 16 + lane] = lane < keep ? a : 0u;
+  __syncthreads();
+  uint32_t b = sh.cand_k[lane];
+  z = 0u;
+  wave_sort_desc(b, z);
+  const uint32_t t = umax_((uint32_t)__builtin_amdgcn_readlane((int)b, keep - 1), 1u);
+  // count, scan and gather the keys >= t (key 0 marks empty slots)
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) cnt += src.key[j] >= t;
+  const int incl = wave_incl_scan(cnt);
+  if (lane == kWave - 1) sh.wave_cnt[wave] = incl;
+  __syncthreads();  // also: every wave has read the thread maxima above
+  int base = incl - cnt, total = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkThreads / kWave; ++w) {
+    const int c = sh.wave_cnt[w];
+    if (w < wave) base += c;
+    total += c;
+  }
+  if (total > kWave) return false;  // uniform
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) {
+    if (src.key[j] >= t) {
+      sh.cand_k[base] = src.key[j];
+      sh.cand_i[base] = j * kTopkThreads + tid;
+      ++base;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // (key desc, index asc): sort (key, ~index) descending; lanes < keep win
+    uint32_t hi = lane < total ? sh.cand_k[lane] : 0u;
+    uint32_t lo = lane < total ? ~(uint32_t)sh.cand_i[lane] : 0u;
+    wave_sort_desc(hi, lo);
+    // kept indices ascending: sort ~index descending
+    uint32_t asc = lane < keep ? lo : 0u, dummy = 0u;
+    wave_sort_desc(asc, dummy);
+    if (lane < keep) out_sel[lane] = (int)~asc;
+    if (lane == 0) out_sel[keep] = own;
+    for (int i = keep + 1 + lane; i < k; i += kWave) out_sel[i] = -1;
+  }
+  __syncthreads();
+  return true;
+}
+
+// Sort keep+1 kept blocks (chosen[0..found) and own) ascending into out_sel.
+__device__ __forceinline__ void topk_write_sorted(const TopkShared& sh, int found, int own, int k,
+                                                  int* out_sel) {
+  const int tid = threadIdx.x;
+  if (tid <= found) {
+    const int x = tid < found ? sh.chosen[tid] : own;
+    int rank = 0;
+    for (int j = 0; j <= found; ++j) rank += (j < found ? sh.chosen[j] : own) < x;
+    out_sel[rank] = x;
+  }
+  for (int i = found + 1 + tid; i < k; i += kTopkThreads) out_sel[i] = -1;
+  __syncthreads();
+}
+
+// All 256 threads call this with identical arguments; src holds scores of
+// blocks 0 .. own-1.  out_sel (LDS, k entries) receives the kept blocks.
+template <class Src>
+__device__ __forceinline__ void topk_select(const Src& src, int own, int k, int* out_sel,
+                                            TopkShared& sh) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int keep = min(k - 1, own);
   if (keep >= own) {  // every eligible block is kept
@@ -122,16 +363,18 @@ __device__ void block_topk(const float* __restrict__ scores, int own, int k, int
     return;
   }
   if (tid == 0) sh.n_chosen = 0;
-  float lo, hi;
-  topk_range(scores, own, -INFINITY, INFINITY, false, 0.0, 0.0, 0, sh, lo, hi);
+  uint32_t lo, hi;
+  topk_range(src, 0u, 0xFFFFFFFFu, 0, -1, sh, lo, hi);
   int need = keep;
-  // every refinement strictly shrinks the boundary bin, so a few rounds
-  // suffice; the cap only guards against non-finite scores
-  for (int round = 0; need > 0 && round < 64; ++round) {
-    if (!(lo < hi)) {
-      topk_lowest_equal(scores, own, hi, need, sh);
+  // each refinement shrinks hi - lo at least 2^7-fold: at most 5 rounds
+  for (int round = 0; need > 0 && round < 8; ++round) {
+    if (lo == hi) {
+      topk_lowest_equal(src, hi, need, sh);
       break;
     }
+    const uint32_t span = hi - lo;
+    const int bits = 32 - __builtin_clz(span);
+    const int shift = bits > 8 ? bits - 8 : 0;
     for (int i = tid; i < kTopkBins; i += kTopkThreads) sh.hist[i] = 0u;
     if (tid == 0) {
       sh.bstar = kTopkBins;
@@ -139,12 +382,9 @@ __device__ void block_topk(const float* __restrict__ scores, int own, int k, int
       sh.c_eq = 0;
     }
     __syncthreads();
-    const double dhi = (double)hi;
-    const double scale = (double)kTopkBins / (dhi - (double)lo);
-    for (int i = tid; i < own; i += kTopkThreads) {
-      const float v = scores[i];
-      if (v >= lo && v <= hi) atomicAdd(&sh.hist[topk_bin(v, dhi, scale)], 1u);
-    }
+    src.each([&](int, uint32_t key) {
+      if (key >= lo && key <= hi) atomicAdd(&sh.hist[(hi - key) >> shift], 1u);
+    });
     __syncthreads();
     if (wave == 0) {  // find the bin holding the need-th item
       constexpr int kPer = kTopkBins / kWave;
@@ -175,55 +415,68 @@ __device__ void block_topk(const float* __restrict__ scores, int own, int k, int
     }
     __syncthreads();
     const int bstar = sh.bstar, c_lt = sh.c_lt, c_eq = sh.c_eq;
-    if (bstar >= kTopkBins) break;  // fewer live scores than needed (non-finite input)
+    if (bstar >= kTopkBins) break;  // cannot happen for well-formed input
     const bool fits = c_eq <= kTopkCap;
-    for (int i = tid; i < own; i += kTopkThreads) {
-      const float v = scores[i];
-      if (!(v >= lo && v <= hi)) continue;
-      const int b = topk_bin(v, dhi, scale);
+    src.each([&](int i, uint32_t key) {
+      if (!(key >= lo && key <= hi)) return;
+      const int b = (int)((hi - key) >> shift);
       if (b < bstar) {
         push_chosen(sh, i);
       } else if (b == bstar && fits) {
         const int p = atomicAdd(&sh.n_cand, 1);
         if (p < kTopkCap) {
-          sh.cand_v[p] = v;
+          sh.cand_k[p] = key;
           sh.cand_i[p] = i;
         }
       }
-    }
+    });
     __syncthreads();
     need -= c_lt;
     if (fits) {
       if (tid < c_eq) {
-        const float v = sh.cand_v[tid];
+        const uint32_t key = sh.cand_k[tid];
         const int idx = sh.cand_i[tid];
         int rank = 0;
         for (int j = 0; j < c_eq; ++j) {
-          const float w = sh.cand_v[j];
-          rank += (w > v) || (w == v && sh.cand_i[j] < idx);
+          const uint32_t o = sh.cand_k[j];
+          rank += (o > key) || (o == key && sh.cand_i[j] < idx);
         }
         if (rank < need) push_chosen(sh, idx);
       }
       __syncthreads();
       break;
     }
-    float nlo, nhi;
-    topk_range(scores, own, lo, hi, true, dhi, scale, bstar, sh, nlo, nhi);
+    uint32_t nlo, nhi;
+    topk_range(src, lo, hi, shift, bstar, sh, nlo, nhi);
     lo = nlo;
     hi = nhi;
   }
   __syncthreads();
-  // sort the kept blocks (own included) ascending; with non-finite scores
-  // fewer than keep may have been found, the rest is filled with -1
-  const int found = min(sh.n_chosen, keep);
-  if (tid <= found) {
-    const int x = tid < found ? sh.chosen[tid] : own;
-    int rank = 0;
-    for (int j = 0; j <= found; ++j) rank += (j < found ? sh.chosen[j] : own) < x;
-    out_sel[rank] = x;
+  // with non-finite scores fewer than keep may have been found; -1 fills
+  topk_write_sorted(sh, min(sh.n_chosen, keep), own, k, out_sel);
+}
+
+// TopK of scores[0 .. own) held in global memory.
+__device__ __forceinline__ void block_topk(const float* __restrict__ scores, int own, int k,
+                                           int* out_sel, TopkShared& sh) {
+  const int keep = min(k - 1, own);
+  if (keep >= own || keep == 0) {
+    GlobalKeys src{scores, own};  // nothing to rank
+    topk_select(src, own, k, out_sel, sh);
+  } else if (own <= kTopkThreads * 32) {
+    RegKeys<32> src;
+    src.load(scores, own);
+    if (keep > 16 || !topk_fast(src, own, keep, k, out_sel, sh))
+      topk_select(src, own, k, out_sel, sh);
+  } else if (own <= kTopkThreads * 64) {
+    RegKeys<64> src;
+    src.load(scores, own);
+    if (keep > 16 || !topk_fast(src, own, keep, k, out_sel, sh))
+      topk_select(src, own, k, out_sel, sh);
+  } else {
+    GlobalKeys src{scores, own};
+    topk_select(src, own, k, out_sel, sh);
   }
-  for (int i = found + 1 + tid; i < k; i += kTopkThreads) out_sel[i] = -1;
-  __syncthreads();
 }
 
 }  // namespace msa

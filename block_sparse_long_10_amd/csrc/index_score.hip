@@ -27,13 +27,10 @@ template <int B, int NI, int MT>
 __global__ __launch_bounds__(256) void index_score_decode_kernel(
     const uint16_t* __restrict__ idx_k, const int32_t* __restrict__ block_table,
     int32_t max_blocks, const uint16_t* __restrict__ idx_q, const int32_t* __restrict__ seq_lens,
-    int32_t num_kv_heads, int32_t blocks_per_wave, float* __restrict__ pooled,
-    uint32_t* __restrict__ zero_counters) {
+    int32_t num_kv_heads, int32_t blocks_per_wave, float* __restrict__ pooled) {
   constexpr int NT = B / 16;  // 16-token MFMA tiles per block
   const int s = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  if (zero_counters != nullptr && blockIdx.x == 0 && tid < num_kv_heads)
-    zero_counters[s * num_kv_heads + tid] = 0u;
   const int own = (seq_lens[s] - 1) / B;
   const int b_begin = (blockIdx.x * (256 / kWave) + wave) * blocks_per_wave;
   const int b_end = min(b_begin + blocks_per_wave, own);
@@ -120,13 +117,12 @@ __global__ __launch_bounds__(256) void index_score_decode_kernel(
 template <int B, int NI>
 static hipError_t launch_decode_ni(int mt, dim3 grid, hipStream_t st, const uint16_t* idx_k,
                                    const int32_t* bt, int32_t mb, const uint16_t* idx_q,
-                                   const int32_t* sl, int32_t hkv, int32_t bpw, float* pooled,
-                                   uint32_t* zc) {
+                                   const int32_t* sl, int32_t hkv, int32_t bpw, float* pooled) {
   switch (mt) {
-    case 1: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 1>), grid, dim3(256), 0, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled, zc); break;
-    case 2: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 2>), grid, dim3(256), 0, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled, zc); break;
-    case 3: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 3>), grid, dim3(256), 0, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled, zc); break;
-    default: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 4>), grid, dim3(256), 0, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled, zc); break;
+    case 1: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 1>), grid, dim3(256), 0, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled); break;
+    case 2: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 2>), grid, dim3(256), 0, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled); break;
+    case 3: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 3>), grid, dim3(256), 0, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled); break;
+    default: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 4>), grid, dim3(256), 0, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled); break;
   }
   return hipGetLastError();
 }
@@ -134,20 +130,19 @@ static hipError_t launch_decode_ni(int mt, dim3 grid, hipStream_t st, const uint
 template <int B>
 static hipError_t launch_decode_b(int ni, int mt, dim3 grid, hipStream_t st, const uint16_t* idx_k,
                                   const int32_t* bt, int32_t mb, const uint16_t* idx_q,
-                                  const int32_t* sl, int32_t hkv, int32_t bpw, float* pooled,
-                                  uint32_t* zc) {
+                                  const int32_t* sl, int32_t hkv, int32_t bpw, float* pooled) {
   switch (ni) {
-    case 1: return launch_decode_ni<B, 1>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled, zc);
-    case 2: return launch_decode_ni<B, 2>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled, zc);
-    case 4: return launch_decode_ni<B, 4>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled, zc);
-    case 8: return launch_decode_ni<B, 8>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled, zc);
-    default: return launch_decode_ni<B, 16>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled, zc);
+    case 1: return launch_decode_ni<B, 1>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled);
+    case 2: return launch_decode_ni<B, 2>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled);
+    case 4: return launch_decode_ni<B, 4>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled);
+    case 8: return launch_decode_ni<B, 8>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled);
+    default: return launch_decode_ni<B, 16>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled);
   }
 }
 
 hipError_t launch_index_score_decode(const Dims& d, const Cache& c, const uint16_t* idx_q,
                                      const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
-                                     float* pooled, uint32_t* zero_counters, hipStream_t stream) {
+                                     float* pooled, hipStream_t stream) {
   const int B = d.block_size;
   const int max_own = (max_seq_len - 1) / B;
   const int bpw = 2;
@@ -157,11 +152,9 @@ hipError_t launch_index_score_decode(const Dims& d, const Cache& c, const uint16
   dim3 grid(gx, batch);
   if (B == 64)
     return launch_decode_b<64>(d.num_idx_heads, mt, grid, stream, c.idx_k, c.block_table,
-                               c.max_blocks, idx_q, seq_lens, d.num_kv_heads, bpw, pooled,
-                               zero_counters);
+                               c.max_blocks, idx_q, seq_lens, d.num_kv_heads, bpw, pooled);
   return launch_decode_b<128>(d.num_idx_heads, mt, grid, stream, c.idx_k, c.block_table,
-                              c.max_blocks, idx_q, seq_lens, d.num_kv_heads, bpw, pooled,
-                              zero_counters);
+                              c.max_blocks, idx_q, seq_lens, d.num_kv_heads, bpw, pooled);
 }
 
 // --------------------------------------------------------------- prefill
