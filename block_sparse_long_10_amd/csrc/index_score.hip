@@ -3,13 +3,12 @@
 // "MiniMax wird dünn", section 1, Schritt 1.
 //
 // Decode (msa_index_score_decode): one pass over every cached index key of
-// every sequence.  The keys are streamed from HBM exactly once with 16-byte
-// loads straight into MFMA operand registers; all Hkv*n_i index-query rows of a
-// sequence (32 at 8 groups x 4 heads) are the M side of a
-// v_mfma_f32_16x16x32_bf16 so the 64-term dots run on the matrix cores and the
-// kernel stays bound by HBM.  Each wave owns a run of blocks, double-buffers
-// one block (B tokens x 128 B) in registers, and folds the 16x16 score tiles
-// into per-row running maxima; a DPP row reduction then gives the block max.
+// every sequence.  The keys are streamed from HBM exactly once, one KV block
+// per single-wave workgroup, through LDS (see the kernel); all Hkv*n_i
+// index-query rows of a sequence (32 at 8 groups x 4 heads) are the M side of
+// a v_mfma_f32_16x16x32_bf16 so the 64-term dots run on the matrix cores and
+// the kernel stays bound by HBM.  The 16x16 score tiles fold into per-row
+// running maxima; a DPP row reduction then gives the block max.
 //
 // Prefill (msa_index_score_prefill): per (tile, group) the tile's queries x
 // index heads (up to 512 rows) are held in registers as the A side of
@@ -23,22 +22,36 @@
 namespace msa {
 
 // ---------------------------------------------------------------- decode
+// One wave per workgroup and one block per wave.  The block's index keys
+// (B tokens x 128 bytes) are streamed with 1 KB wave-contiguous direct-to-LDS
+// loads (global_load_lds_dwordx4, non-temporal): lane l of load i fills LDS
+// bytes i*1024 + 16*l, i.e. token 8i + l/8 and chunk slot l%8, and reads the
+// source chunk (l%8) ^ (l/8), so the LDS image is XOR-swizzled and the MFMA
+// operand reads (16 tokens x one chunk per instruction) hit distinct banks.
+// Small single-wave workgroups let ten blocks per CU be in flight.
 template <int B, int NI, int MT>
-__global__ __launch_bounds__(256) void index_score_decode_kernel(
+__global__ __launch_bounds__(64) void index_score_decode_kernel(
     const uint16_t* __restrict__ idx_k, const int32_t* __restrict__ block_table,
     int32_t max_blocks, const uint16_t* __restrict__ idx_q, const int32_t* __restrict__ seq_lens,
-    int32_t num_kv_heads, int32_t blocks_per_wave, float* __restrict__ pooled) {
-  constexpr int NT = B / 16;  // 16-token MFMA tiles per block
-  const int s = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    int32_t num_kv_heads, float* __restrict__ pooled) {
+  constexpr int BYTES = B * 128;     // one block of index keys
+  constexpr int NLD = BYTES / 1024;  // 1 KB wave loads per block
+  constexpr int NT = B / 16;         // 16-token MFMA tiles per block
+  __shared__ __attribute__((aligned(16))) uint8_t stage[BYTES];
+  const int s = blockIdx.y, b = blockIdx.x;
+  const int lane = threadIdx.x;
   const int own = (seq_lens[s] - 1) / B;
-  const int b_begin = (blockIdx.x * (256 / kWave) + wave) * blocks_per_wave;
-  const int b_end = min(b_begin + blocks_per_wave, own);
-  if (b_begin >= b_end) return;
+  if (b >= own) return;
+  const uint8_t* page =
+      reinterpret_cast<const uint8_t*>(idx_k) + (size_t)block_table[(size_t)s * max_blocks + b] * BYTES;
+  const int src_off = (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) << 4);
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) load_lds16_stream(page + i * 1024 + src_off, &stage[i * 1024]);
 
+  // A operand: index-query rows (row = group*NI + head); K split: dims
+  // ks*32 + 8*q4 .. +7, the same for the keys below.
   const int R = num_kv_heads * NI;
   const int r16 = lane & 15, q4 = lane >> 4;
-  // A operand: index-query rows (row = group*NI + head), two 32-wide K steps.
   bf16x8 a[MT][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -47,67 +60,55 @@ __global__ __launch_bounds__(256) void index_score_decode_kernel(
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) a[mt][ks] = row < R ? load_bf16x8(p + ks * 32) : zero_bf16x8();
   }
-  const int32_t* bt = block_table + (size_t)s * max_blocks;
-  float* out = pooled + (size_t)s * num_kv_heads * max_blocks;
+  wait_vmem();  // the LDS image and the queries are in place (one wave: no barrier)
 
-  // B operand: token nt*16 + r16 of the block, same K split as A.
-  bf16x8 kb[NT][2];
-  auto load_block = [&](int b) {
-    const uint16_t* base = idx_k + (size_t)bt[b] * (B * 64) + r16 * 64 + q4 * 8;
+  f32x4 rmax[MT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      kb[nt][0] = load_bf16x8(base + nt * 16 * 64);
-      kb[nt][1] = load_bf16x8(base + nt * 16 * 64 + 32);
+  for (int mt = 0; mt < MT; ++mt) rmax[mt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int t = nt * 16 + r16;  // B operand: token t
+    bf16x8 kb[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c = ks * 4 + q4;
+      kb[ks] = __builtin_bit_cast(bf16x8,
+                                  *reinterpret_cast<const u32x4*>(&stage[t * 128 + ((c ^ (t & 7)) << 4)]));
     }
-  };
-  load_block(b_begin);
-  for (int b = b_begin; b < b_end; ++b) {
-    bf16x8 cur[NT][2];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      cur[nt][0] = kb[nt][0];
-      cur[nt][1] = kb[nt][1];
-    }
-    if (b + 1 < b_end) load_block(b + 1);
-    f32x4 rmax[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) rmax[mt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma16(a[mt][0], cur[nt][0], acc);
-        acc = mfma16(a[mt][1], cur[nt][1], acc);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) rmax[mt][j] = fmaxf(rmax[mt][j], acc[j]);
-      }
-    }
-    // lane holds rows mt*16 + 4*q4 + j; reduce over the 16 token lanes, then
-    // over the rows of each group.
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int row0 = mt * 16 + q4 * 4;
-      if constexpr (NI >= 4) {
-        float v = row16_max(max4(rmax[mt]));
-        if constexpr (NI >= 8) v = fmaxf(v, xor_lane(v, 16));
-        if constexpr (NI >= 16) v = fmaxf(v, xor_lane(v, 32));
-        const int g = row0 / NI;
-        if (r16 == 0 && (row0 % NI) == 0 && g < num_kv_heads) out[(size_t)g * max_blocks + b] = v;
-      } else {
-        float v[4];
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma16(a[mt][0], kb[0], acc);
+      acc = mfma16(a[mt][1], kb[1], acc);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = row16_max(rmax[mt][j]);
-        if (r16 == 0) {
-          if constexpr (NI == 2) {
-            const int g = row0 / 2;
-            if (g < num_kv_heads) out[(size_t)g * max_blocks + b] = fmaxf(v[0], v[1]);
-            if (g + 1 < num_kv_heads) out[(size_t)(g + 1) * max_blocks + b] = fmaxf(v[2], v[3]);
-          } else {
+      for (int j = 0; j < 4; ++j) rmax[mt][j] = fmaxf(rmax[mt][j], acc[j]);
+    }
+  }
+  // lane holds rows mt*16 + 4*q4 + j; reduce over the 16 token lanes, then
+  // over the rows of each group.
+  float* out = pooled + (size_t)s * num_kv_heads * max_blocks;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (row0 + j < num_kv_heads) out[(size_t)(row0 + j) * max_blocks + b] = v[j];
-          }
+  for (int mt = 0; mt < MT; ++mt) {
+    const int row0 = mt * 16 + q4 * 4;
+    if constexpr (NI >= 4) {
+      float v = row16_max(max4(rmax[mt]));
+      if constexpr (NI >= 8) v = fmaxf(v, xor_lane(v, 16));
+      if constexpr (NI >= 16) v = fmaxf(v, xor_lane(v, 32));
+      const int g = row0 / NI;
+      if (r16 == 0 && (row0 % NI) == 0 && g < num_kv_heads) out[(size_t)g * max_blocks + b] = v;
+    } else {
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = row16_max(rmax[mt][j]);
+      if (r16 == 0) {
+        if constexpr (NI == 2) {
+          const int g = row0 / 2;
+          if (g < num_kv_heads) out[(size_t)g * max_blocks + b] = fmaxf(v[0], v[1]);
+          if (g + 1 < num_kv_heads) out[(size_t)(g + 1) * max_blocks + b] = fmaxf(v[2], v[3]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (row0 + j < num_kv_heads) out[(size_t)(row0 + j) * max_blocks + b] = v[j];
         }
       }
     }
@@ -117,12 +118,12 @@ __global__ __launch_bounds__(256) void index_score_decode_kernel(
 template <int B, int NI>
 static hipError_t launch_decode_ni(int mt, dim3 grid, hipStream_t st, const uint16_t* idx_k,
                                    const int32_t* bt, int32_t mb, const uint16_t* idx_q,
-                                   const int32_t* sl, int32_t hkv, int32_t bpw, float* pooled) {
+                                   const int32_t* sl, int32_t hkv, float* pooled) {
   switch (mt) {
-    case 1: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 1>), grid, dim3(256), 0, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled); break;
-    case 2: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 2>), grid, dim3(256), 0, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled); break;
-    case 3: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 3>), grid, dim3(256), 0, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled); break;
-    default: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 4>), grid, dim3(256), 0, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled); break;
+    case 1: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 1>), grid, dim3(64), 0, st, idx_k, bt, mb, idx_q, sl, hkv, pooled); break;
+    case 2: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 2>), grid, dim3(64), 0, st, idx_k, bt, mb, idx_q, sl, hkv, pooled); break;
+    case 3: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 3>), grid, dim3(64), 0, st, idx_k, bt, mb, idx_q, sl, hkv, pooled); break;
+    default: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 4>), grid, dim3(64), 0, st, idx_k, bt, mb, idx_q, sl, hkv, pooled); break;
   }
   return hipGetLastError();
 }
@@ -130,13 +131,13 @@ static hipError_t launch_decode_ni(int mt, dim3 grid, hipStream_t st, const uint
 template <int B>
 static hipError_t launch_decode_b(int ni, int mt, dim3 grid, hipStream_t st, const uint16_t* idx_k,
                                   const int32_t* bt, int32_t mb, const uint16_t* idx_q,
-                                  const int32_t* sl, int32_t hkv, int32_t bpw, float* pooled) {
+                                  const int32_t* sl, int32_t hkv, float* pooled) {
   switch (ni) {
-    case 1: return launch_decode_ni<B, 1>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled);
-    case 2: return launch_decode_ni<B, 2>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled);
-    case 4: return launch_decode_ni<B, 4>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled);
-    case 8: return launch_decode_ni<B, 8>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled);
-    default: return launch_decode_ni<B, 16>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, bpw, pooled);
+    case 1: return launch_decode_ni<B, 1>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled);
+    case 2: return launch_decode_ni<B, 2>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled);
+    case 4: return launch_decode_ni<B, 4>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled);
+    case 8: return launch_decode_ni<B, 8>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled);
+    default: return launch_decode_ni<B, 16>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled);
   }
 }
 
@@ -145,16 +146,14 @@ hipError_t launch_index_score_decode(const Dims& d, const Cache& c, const uint16
                                      float* pooled, hipStream_t stream) {
   const int B = d.block_size;
   const int max_own = (max_seq_len - 1) / B;
-  const int bpw = 2;
-  const int per_wg = bpw * (256 / kWave);
-  const int gx = max_own > 0 ? (max_own + per_wg - 1) / per_wg : 1;
+  const int gx = max_own > 0 ? max_own : 1;
   const int mt = (d.num_kv_heads * d.num_idx_heads + 15) / 16;
   dim3 grid(gx, batch);
   if (B == 64)
     return launch_decode_b<64>(d.num_idx_heads, mt, grid, stream, c.idx_k, c.block_table,
-                               c.max_blocks, idx_q, seq_lens, d.num_kv_heads, bpw, pooled);
+                               c.max_blocks, idx_q, seq_lens, d.num_kv_heads, pooled);
   return launch_decode_b<128>(d.num_idx_heads, mt, grid, stream, c.idx_k, c.block_table,
-                              c.max_blocks, idx_q, seq_lens, d.num_kv_heads, bpw, pooled);
+                              c.max_blocks, idx_q, seq_lens, d.num_kv_heads, pooled);
 }
 
 // --------------------------------------------------------------- prefill

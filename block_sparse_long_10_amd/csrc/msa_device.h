@@ -29,6 +29,22 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
+// Streaming 16-byte load: the data is read once, keep it out of the caches.
+__device__ __forceinline__ bf16x8 load_bf16x8_stream(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
+// Direct global -> LDS copy of 16 bytes per lane (gfx950
+// global_load_lds_dwordx4): lane l's bytes land at lds_base + 16*l; the LDS
+// base must be the same for the whole wave.  Non-temporal (streamed once).
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* global_ptr_t;
+constexpr int kCachePolicyNT = 2;
+__device__ __forceinline__ void load_lds16_stream(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)lds_base, 16, 0, kCachePolicyNT);
+}
+// Wait for every outstanding vector-memory operation of this wave.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
+
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
   return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 }
