@@ -33,13 +33,14 @@ template <int B, int NI, int MT>
 __global__ __launch_bounds__(64) void index_score_decode_kernel(
     const uint16_t* __restrict__ idx_k, const int32_t* __restrict__ block_table,
     int32_t max_blocks, const uint16_t* __restrict__ idx_q, const int32_t* __restrict__ seq_lens,
-    int32_t num_kv_heads, float* __restrict__ pooled) {
+    int32_t num_kv_heads, float* __restrict__ pooled, uint32_t* __restrict__ counters) {
   constexpr int BYTES = B * 128;     // one block of index keys
   constexpr int NLD = BYTES / 1024;  // 1 KB wave loads per block
   constexpr int NT = B / 16;         // 16-token MFMA tiles per block
   __shared__ __attribute__((aligned(16))) uint8_t stage[BYTES];
   const int s = blockIdx.y, b = blockIdx.x;
   const int lane = threadIdx.x;
+  if (counters != nullptr && b == 0 && lane < num_kv_heads) counters[s * num_kv_heads + lane] = 0u;
   const int own = (seq_lens[s] - 1) / B;
   if (b >= own) return;
   const uint8_t* page =
@@ -118,12 +119,13 @@ __global__ __launch_bounds__(64) void index_score_decode_kernel(
 template <int B, int NI>
 static hipError_t launch_decode_ni(int mt, dim3 grid, hipStream_t st, const uint16_t* idx_k,
                                    const int32_t* bt, int32_t mb, const uint16_t* idx_q,
-                                   const int32_t* sl, int32_t hkv, float* pooled) {
+                                   const int32_t* sl, int32_t hkv, float* pooled,
+                                   uint32_t* ctr) {
   switch (mt) {
-    case 1: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 1>), grid, dim3(64), 0, st, idx_k, bt, mb, idx_q, sl, hkv, pooled); break;
-    case 2: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 2>), grid, dim3(64), 0, st, idx_k, bt, mb, idx_q, sl, hkv, pooled); break;
-    case 3: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 3>), grid, dim3(64), 0, st, idx_k, bt, mb, idx_q, sl, hkv, pooled); break;
-    default: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 4>), grid, dim3(64), 0, st, idx_k, bt, mb, idx_q, sl, hkv, pooled); break;
+    case 1: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 1>), grid, dim3(64), 0, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr); break;
+    case 2: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 2>), grid, dim3(64), 0, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr); break;
+    case 3: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 3>), grid, dim3(64), 0, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr); break;
+    default: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 4>), grid, dim3(64), 0, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr); break;
   }
   return hipGetLastError();
 }
@@ -131,19 +133,20 @@ static hipError_t launch_decode_ni(int mt, dim3 grid, hipStream_t st, const uint
 template <int B>
 static hipError_t launch_decode_b(int ni, int mt, dim3 grid, hipStream_t st, const uint16_t* idx_k,
                                   const int32_t* bt, int32_t mb, const uint16_t* idx_q,
-                                  const int32_t* sl, int32_t hkv, float* pooled) {
+                                  const int32_t* sl, int32_t hkv, float* pooled,
+                                  uint32_t* ctr) {
   switch (ni) {
-    case 1: return launch_decode_ni<B, 1>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled);
-    case 2: return launch_decode_ni<B, 2>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled);
-    case 4: return launch_decode_ni<B, 4>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled);
-    case 8: return launch_decode_ni<B, 8>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled);
-    default: return launch_decode_ni<B, 16>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled);
+    case 1: return launch_decode_ni<B, 1>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr);
+    case 2: return launch_decode_ni<B, 2>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr);
+    case 4: return launch_decode_ni<B, 4>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr);
+    case 8: return launch_decode_ni<B, 8>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr);
+    default: return launch_decode_ni<B, 16>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr);
   }
 }
 
 hipError_t launch_index_score_decode(const Dims& d, const Cache& c, const uint16_t* idx_q,
                                      const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
-                                     float* pooled, hipStream_t stream) {
+                                     float* pooled, uint32_t* counters, hipStream_t stream) {
   const int B = d.block_size;
   const int max_own = (max_seq_len - 1) / B;
   const int gx = max_own > 0 ? max_own : 1;
@@ -151,9 +154,9 @@ hipError_t launch_index_score_decode(const Dims& d, const Cache& c, const uint16
   dim3 grid(gx, batch);
   if (B == 64)
     return launch_decode_b<64>(d.num_idx_heads, mt, grid, stream, c.idx_k, c.block_table,
-                               c.max_blocks, idx_q, seq_lens, d.num_kv_heads, pooled);
+                               c.max_blocks, idx_q, seq_lens, d.num_kv_heads, pooled, counters);
   return launch_decode_b<128>(d.num_idx_heads, mt, grid, stream, c.idx_k, c.block_table,
-                              c.max_blocks, idx_q, seq_lens, d.num_kv_heads, pooled);
+                              c.max_blocks, idx_q, seq_lens, d.num_kv_heads, pooled, counters);
 }
 
 // --------------------------------------------------------------- prefill

@@ -76,7 +76,7 @@ msa_status hip_status(hipError_t e, const char* what) {
 
 // decode workspace layout
 struct DecodeWs {
-  size_t pooled, part_o, part_ml, sel, total;
+  size_t pooled, part_o, part_ml, counters, sel, total;
 };
 DecodeWs decode_layout(const msa_params* p, int32_t batch, int32_t max_blocks) {
   const size_t G = (size_t)(p->num_q_heads / p->num_kv_heads);
@@ -88,7 +88,9 @@ DecodeWs decode_layout(const msa_params* p, int32_t batch, int32_t max_blocks) {
   w.part_o = off;
   off += align_up(sg * p->top_k * G * p->head_dim * sizeof(float));
   w.part_ml = off;
-  off += align_up(sg * p->top_k * G * 2 * sizeof(float));
+  off += align_up(sg * p->top_k * G * 4 * sizeof(float));
+  w.counters = off;
+  off += align_up(sg * sizeof(uint32_t));
   w.sel = off;
   off += align_up(sg * p->top_k * sizeof(int32_t));
   w.total = off;
@@ -151,7 +153,7 @@ msa_status msa_index_score_decode(const msa_params* params, const msa_paged_kv* 
     return fail(MSA_ERR_INVALID_ARGUMENT, "max_seq_len must be in [1, max_blocks_per_seq*block_size]");
   return hip_status(msa::launch_index_score_decode(dims_of(params), cache_of(kv),
                                                    static_cast<const uint16_t*>(idx_q), seq_lens,
-                                                   batch, max_seq_len, pooled,
+                                                   batch, max_seq_len, pooled, nullptr,
                                                    static_cast<hipStream_t>(stream)),
                     "index score launch");
 }
@@ -174,17 +176,18 @@ msa_status msa_decode(const msa_params* params, const msa_paged_kv* kv, const vo
     return fail(MSA_ERR_WORKSPACE, "workspace missing or smaller than msa_decode_workspace_bytes()");
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   float* pooled = reinterpret_cast<float*>(ws + w.pooled);
+  uint32_t* counters = reinterpret_cast<uint32_t*>(ws + w.counters);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const msa::Dims d = dims_of(params);
   const msa::Cache c = cache_of(kv);
   st = hip_status(msa::launch_index_score_decode(d, c, static_cast<const uint16_t*>(idx_q),
-                                                 seq_lens, batch, max_seq_len, pooled, s),
+                                                 seq_lens, batch, max_seq_len, pooled, counters, s),
                   "index score launch");
   if (st != MSA_OK) return st;
   return hip_status(
       msa::launch_decode_attn(d, c, static_cast<const uint16_t*>(q), seq_lens, batch, pooled,
                               reinterpret_cast<float*>(ws + w.part_o),
-                              reinterpret_cast<float*>(ws + w.part_ml),
+                              reinterpret_cast<float*>(ws + w.part_ml), counters,
                               sel != nullptr ? sel : reinterpret_cast<int32_t*>(ws + w.sel), out, s),
       "sparse attention launch");
 }

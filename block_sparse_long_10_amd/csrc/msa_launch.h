@@ -21,17 +21,18 @@ struct Cache {
   int32_t num_pages, max_blocks;
 };
 
-// Step 1, decode: pooled[s][g][b] for b < own(s).
+// Step 1, decode: pooled[s][g][b] for b < own(s).  When counters is not
+// null, counters [batch][Hkv] are cleared for the attention launch.
 hipError_t launch_index_score_decode(const Dims& d, const Cache& c, const uint16_t* idx_q,
                                      const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
-                                     float* pooled, hipStream_t stream);
+                                     float* pooled, uint32_t* counters, hipStream_t stream);
 
 // TopK, Step 2 over the kept blocks (one partial per block) and the merge of
-// the partials, decode: three launches.
+// the partials, decode.  counters must be zero on entry.
 hipError_t launch_decode_attn(const Dims& d, const Cache& c, const uint16_t* q,
                               const int32_t* seq_lens, int32_t batch, const float* pooled,
-                              float* part_o, float* part_ml, int32_t* sel, float* out,
-                              hipStream_t stream);
+                              float* part_o, float* part_ml, uint32_t* counters, int32_t* sel,
+                              float* out, hipStream_t stream);
 
 // Step 1, prefill: pooled[t][g][b] for b < prior_len/B + t.
 hipError_t launch_index_score_prefill(const Dims& d, const Cache& c, const uint16_t* idx_q,
