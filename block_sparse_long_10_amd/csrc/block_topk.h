@@ -8,13 +8,13 @@
 // registers when own <= 256*MAXV (all loads issued at once; empty slots hold
 // key 0, below every finite score), otherwise re-read from global memory.
 //
-// Fast path (registers, k' = k-1 <= 16): each thread takes the max of its
-// keys; wave-wide DPP bitonic sorts give T, the k'-th largest of the 256
-// thread maxima, which k' distinct scores reach, so it bounds the k'-th best
-// score from below; the few keys >= T are gathered to LDS (prefix-sum
-// offsets) and one more bitonic sort on (key, ~index) picks the winners, a
-// last one orders them by block index.  If more than 64 keys reach T (heavy
-// ties), the general path below runs instead:
+// Fast path (registers): each thread takes the max of its keys; an LDS
+// histogram of the 256 thread maxima gives T, the lowest key of the bin that
+// completes k' = k-1 maxima; those k' distinct scores reach T, so it bounds
+// the k'-th best score from below.  The few keys >= T are gathered to LDS
+// (DPP prefix-sum offsets), ranked by counting against each other, and the
+// winners are put in block order by a wave-wide DPP bitonic sort.  If more
+// than 64 keys reach T (heavy ties), the general path below runs instead:
 //   1. key range [lo, hi] (DPP/shuffle wave reductions + LDS);
 //   2. LDS histogram of bin = (hi - key) >> shift, at most 256 bins; the bin
 //      is monotone in the key, so every item of a lower bin outranks every
@@ -228,57 +228,53 @@ __device__ __forceinline__ uint32_t xor_exchange(uint32_t v) {
   }
 }
 
-// One compare-exchange stage of a bitonic sort: lanes pair with lane ^ J;
-// blocks of K lanes alternate direction so that the full sort (K = 64) is
-// descending from lane 0.
+// One compare-exchange stage of a bitonic sort of one 32-bit value per lane:
+// lanes pair with lane ^ J; blocks of K lanes alternate direction so that the
+// full sort (K = 64) is descending from lane 0.
 template <int K, int J>
-__device__ __forceinline__ void bitonic_stage(uint32_t& hi, uint32_t& lo) {
-  const uint32_t oh = xor_exchange<J>(hi), ol = xor_exchange<J>(lo);
+__device__ __forceinline__ void bitonic_stage(uint32_t& v) {
+  const uint32_t o = xor_exchange<J>(v);
   const int lane = threadIdx.x & (kWave - 1);
   const bool take_max = ((lane & J) == 0) == ((lane & K) == 0);
-  const bool other_bigger = oh > hi || (oh == hi && ol > lo);
-  if (take_max == other_bigger) {
-    hi = oh;
-    lo = ol;
-  }
+  v = take_max ? umax_(v, o) : umin_(v, o);
 }
 template <int K>
-__device__ __forceinline__ void bitonic_merge(uint32_t& hi, uint32_t& lo) {
-  if constexpr (K >= 64) bitonic_stage<K, 32>(hi, lo);
-  if constexpr (K >= 32) bitonic_stage<K, 16>(hi, lo);
-  if constexpr (K >= 16) bitonic_stage<K, 8>(hi, lo);
-  if constexpr (K >= 8) bitonic_stage<K, 4>(hi, lo);
-  if constexpr (K >= 4) bitonic_stage<K, 2>(hi, lo);
-  bitonic_stage<K, 1>(hi, lo);
+__device__ __forceinline__ void bitonic_merge(uint32_t& v) {
+  if constexpr (K >= 64) bitonic_stage<K, 32>(v);
+  if constexpr (K >= 32) bitonic_stage<K, 16>(v);
+  if constexpr (K >= 16) bitonic_stage<K, 8>(v);
+  if constexpr (K >= 8) bitonic_stage<K, 4>(v);
+  if constexpr (K >= 4) bitonic_stage<K, 2>(v);
+  bitonic_stage<K, 1>(v);
 }
-// Sort the 64 lane values (hi, lo) of a wave descending: lane 0 largest.
-__device__ __forceinline__ void wave_sort_desc(uint32_t& hi, uint32_t& lo) {
-  bitonic_merge<2>(hi, lo);
-  bitonic_merge<4>(hi, lo);
-  bitonic_merge<8>(hi, lo);
-  bitonic_merge<16>(hi, lo);
-  bitonic_merge<32>(hi, lo);
-  bitonic_merge<64>(hi, lo);
+// Sort the 64 lane values of a wave descending: lane 0 largest.
+__device__ __forceinline__ void wave_sort_desc(uint32_t& v) {
+  bitonic_merge<2>(v);
+  bitonic_merge<4>(v);
+  bitonic_merge<8>(v);
+  bitonic_merge<16>(v);
+  bitonic_merge<32>(v);
+  bitonic_merge<64>(v);
 }
 
-// Wave inclusive prefix sum.
+// Wave inclusive prefix sum with DPP: row shifts, then row broadcasts.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return v;
 }
 
 // Fast path; returns false (leaving out_sel untouched) when more than 64
-// keys reach the bound.  Requires 1 <= keep < own and keep <= 16.
+// keys reach the bound.  Requires 1 <= keep < own.
 template <int MAXV>
 __device__ __forceinline__ bool topk_fast(const RegKeys<MAXV>& src, int own, int keep, int k,
                                           int* out_sel, TopkShared& sh) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  // thread max (tree)
+  // thread max (tree) and the range of the 256 thread maxima
   uint32_t mx[MAXV];
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) mx[j] = src.key[j];
@@ -286,23 +282,57 @@ __device__ __forceinline__ bool topk_fast(const RegKeys<MAXV>& src, int own, int
   for (int w = MAXV / 2; w >= 1; w /= 2)
 #pragma unroll
     for (int j = 0; j < w; ++j) mx[j] = umax_(mx[j], mx[j + w]);
-  // each wave's best `keep` thread maxima, then the keep-th best of those:
-  // T, reached by `keep` distinct scores, bounds the keep-th best score
-  uint32_t a = mx[0], z = 0u;
-  wave_sort_desc(a, z);
-  if (lane < 16) sh.cand_k[wave * 16 + lane] = lane < keep ? a : 0u;
+  const uint32_t m = mx[0];
+  const uint32_t wmax = wave_umax(m), wmin = wave_umin(m);
+  if (lane == 0) {
+    sh.red_a[wave] = wmax;
+    sh.red_b[wave] = wmin;
+  }
+  for (int i = tid; i < kTopkBins; i += kTopkThreads) sh.hist[i] = 0u;
+  if (tid < kWave) {  // empty candidate slots rank below every real key
+    sh.cand_k[tid] = 0u;
+    sh.cand_i[tid] = 0x7FFFFFFF;
+  }
   __syncthreads();
-  uint32_t b = sh.cand_k[lane];
-  z = 0u;
-  wave_sort_desc(b, z);
-  const uint32_t t = umax_((uint32_t)__builtin_amdgcn_readlane((int)b, keep - 1), 1u);
-  // count, scan and gather the keys >= t (key 0 marks empty slots)
+  uint32_t hi = sh.red_a[0], lo = sh.red_b[0];
+#pragma unroll
+  for (int w = 1; w < kTopkThreads / kWave; ++w) {
+    hi = umax_(hi, sh.red_a[w]);
+    lo = umin_(lo, sh.red_b[w]);
+  }
+  // histogram of the thread maxima, bin = (hi - m) >> shift (at most 256
+  // bins, monotone): T = lowest key of the bin that completes `keep` maxima;
+  // those `keep` distinct scores reach T, so T bounds the keep-th best score.
+  const uint32_t span = hi - lo;
+  const int bits = span == 0u ? 0 : 32 - __builtin_clz(span);
+  const int shift = bits > 8 ? bits - 8 : 0;
+  atomicAdd(&sh.hist[(hi - m) >> shift], 1u);
+  __syncthreads();
+  if (wave == 0) {
+    constexpr int kPer = kTopkBins / kWave;
+    unsigned h[kPer], local = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      h[j] = sh.hist[lane * kPer + j];
+      local += h[j];
+    }
+    unsigned prev = (unsigned)wave_incl_scan((int)local) - local;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (prev < (unsigned)keep && prev + h[j] >= (unsigned)keep) sh.bstar = lane * kPer + j;
+      prev += h[j];
+    }
+  }
+  __syncthreads();
+  const uint32_t edge = ((uint32_t)(sh.bstar + 1) << shift) - 1u;  // hi - key <= edge
+  const uint32_t t = umax_(hi - umin_(edge, hi - 1u), 1u);        // key 0 marks empty slots
+  // count, scan and gather the keys >= t
   int cnt = 0;
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) cnt += src.key[j] >= t;
   const int incl = wave_incl_scan(cnt);
   if (lane == kWave - 1) sh.wave_cnt[wave] = incl;
-  __syncthreads();  // also: every wave has read the thread maxima above
+  __syncthreads();
   int base = incl - cnt, total = 0;
 #pragma unroll
   for (int w = 0; w < kTopkThreads / kWave; ++w) {
@@ -321,14 +351,21 @@ __device__ __forceinline__ bool topk_fast(const RegKeys<MAXV>& src, int own, int
   }
   __syncthreads();
   if (wave == 0) {
-    // (key desc, index asc): sort (key, ~index) descending; lanes < keep win
-    uint32_t hi = lane < total ? sh.cand_k[lane] : 0u;
-    uint32_t lo = lane < total ? ~(uint32_t)sh.cand_i[lane] : 0u;
-    wave_sort_desc(hi, lo);
-    // kept indices ascending: sort ~index descending
-    uint32_t asc = lane < keep ? lo : 0u, dummy = 0u;
-    wave_sort_desc(asc, dummy);
-    if (lane < keep) out_sel[lane] = (int)~asc;
+    // rank of candidate `lane` by (key desc, index asc), counted against all
+    // 64 slots (empty ones rank last)
+    const uint32_t key = sh.cand_k[lane];
+    const int idx = sh.cand_i[lane];
+    int rank = 0;
+#pragma unroll
+    for (int j = 0; j < kWave; ++j) {
+      const uint32_t kj = sh.cand_k[j];
+      const int ij = sh.cand_i[j];
+      rank += (kj > key) || (kj == key && ij < idx);
+    }
+    // kept indices ascending: sort ~index descending (others sort last)
+    uint32_t v = lane < total && rank < keep ? ~(uint32_t)idx : 0u;
+    wave_sort_desc(v);
+    if (lane < keep) out_sel[lane] = (int)~v;
     if (lane == 0) out_sel[keep] = own;
     for (int i = keep + 1 + lane; i < k; i += kWave) out_sel[i] = -1;
   }
@@ -466,13 +503,11 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ scores, int
   } else if (own <= kTopkThreads * 32) {
     RegKeys<32> src;
     src.load(scores, own);
-    if (keep > 16 || !topk_fast(src, own, keep, k, out_sel, sh))
-      topk_select(src, own, k, out_sel, sh);
+    if (!topk_fast(src, own, keep, k, out_sel, sh)) topk_select(src, own, k, out_sel, sh);
   } else if (own <= kTopkThreads * 64) {
     RegKeys<64> src;
     src.load(scores, own);
-    if (keep > 16 || !topk_fast(src, own, keep, k, out_sel, sh))
-      topk_select(src, own, k, out_sel, sh);
+    if (!topk_fast(src, own, keep, k, out_sel, sh)) topk_select(src, own, k, out_sel, sh);
   } else {
     GlobalKeys src{scores, own};
     topk_select(src, own, k, out_sel, sh);

@@ -231,32 +231,32 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
     for (int k0 = 0; k0 < top_k; k0 += kChunk) {
       float m[kChunk], l[kChunk];
       f32x4 o[kChunk];
+      // no branches around the loads (a join would wait for them): slots
+      // past top_k read beyond the buffer range, which returns zeros, and
+      // are masked afterwards
 #pragma unroll
       for (int k = 0; k < kChunk; ++k) {
-        m[k] = -INFINITY;
-        if (k0 + k < top_k) {
-          const f32x4 v = load_shared4(rml, ((k0 + k) * group + h) * 16);
-          m[k] = v[0];
-          l[k] = v[1];
-          o[k] = load_shared4(ro, (((k0 + k) * group + h) * 128 + 4 * d4) * 4);
-        }
+        const f32x4 v = load_shared4(rml, ((k0 + k) * group + h) * 16);
+        o[k] = load_shared4(ro, (((k0 + k) * group + h) * 128 + 4 * d4) * 4);
+        m[k] = k0 + k < top_k ? v[0] : -INFINITY;
+        l[k] = v[1];
       }
+      // branch-free fold (selects, not products: an empty slot's partial
+      // output is stale memory)
       float Mc = M;
 #pragma unroll
       for (int k = 0; k < kChunk; ++k) Mc = fmaxf(Mc, m[k]);
-      if (Mc == -INFINITY) continue;  // only empty slots so far
       const float r = M == -INFINITY ? 0.f : exp2f(M - Mc);
       den *= r;
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[j] *= r;
 #pragma unroll
       for (int k = 0; k < kChunk; ++k) {
-        if (m[k] != -INFINITY) {  // empty slots hold no partial
-          const float e = exp2f(m[k] - Mc);
-          den += e * l[k];
+        const bool live = m[k] != -INFINITY;
+        const float e = exp2f(live ? m[k] - Mc : -INFINITY);
+        den = live ? den + e * l[k] : den;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[j] += e * o[k][j];
-        }
+        for (int j = 0; j < 4; ++j) acc[j] = live ? acc[j] + e * o[k][j] : acc[j];
       }
       M = Mc;
     }
