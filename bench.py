@@ -237,6 +237,89 @@ def cpu_baseline(case, budget_s):
                       % (len(times), DECODE_WORKLOAD)}
 
 
+COPY_PROBE_BYTES = 128 << 20
+
+
+def traffic_probe(args, torch, msa, mi, gu):
+    """Launches for the FETCH_SIZE / WRITE_SIZE counter runs: a plain device
+    copy of COPY_PROBE_BYTES (reads and writes that many bytes), then the
+    decode index kernel on rotated buffer sets of decode_b1_L1M."""
+    src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    base = mi.make_workload(DECODE_WORKLOAD, "cuda")
+    sets = [base] + [clone_decode_case(base) for _ in range(args.rotate - 1)]
+    sh = base.shape
+    p = gu.params_of(sh)
+    kvs = [gu.kv_of(c) for c in sets]
+    pooled = torch.empty(base.batch, sh.num_kv_heads, base.cache.max_blocks, device="cuda")
+    for i in range(8):
+        c = sets[i % len(sets)]
+        msa.msa_index_score_decode(p, kvs[i % len(sets)], c.idx_q, c.seq_lens, base.batch,
+                                   max(base.lengths), pooled)
+    torch.cuda.synchronize()
+    log("[bench] traffic probe done; kernel source hash %s" % kernel_source_hash())
+
+
+def summarize_kernel_trace(stats_csv, out_txt, command):
+    """Write a short text summary of a rocprofv3 --kernel-trace --stats run."""
+    import csv
+    rows = [r for r in csv.DictReader(open(stats_csv))]
+    lines = ["rocprofv3 kernel statistics (MSA kernels)", "", "command:", "  " + command, "",
+             "%-62s %6s %12s %12s %12s" % ("kernel", "calls", "avg us", "min us", "max us")]
+    for r in rows:
+        if "msa::" not in r["Name"]:
+            continue
+        name = r["Name"].split("(")[0].replace("void ", "")
+        lines.append("%-62s %6s %12.3f %12.3f %12.3f" % (
+            name[:62], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3))
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_traffic(fetch_csv, write_csv, out_json, command):
+    """HBM bytes per launch of the decode index kernel from FETCH_SIZE and
+    WRITE_SIZE runs of --traffic-probe, each scaled by what the counter reads
+    for the probe's plain copy of COPY_PROBE_BYTES."""
+    import csv
+    kib = COPY_PROBE_BYTES / 1024.0
+
+    def load(path, counter):
+        copy_vals, kern_vals = [], []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if "copyBuffer" in r["Kernel_Name"]:
+                copy_vals.append(v)
+            elif "index_score_decode_kernel" in r["Kernel_Name"]:
+                kern_vals.append(v)
+        return copy_vals[0], sum(kern_vals) / len(kern_vals), len(kern_vals)
+
+    f_copy, f_kern, n = load(fetch_csv, "FETCH_SIZE")
+    w_copy, w_kern, _ = load(write_csv, "WRITE_SIZE")
+    f_scale, w_scale = kib / f_copy, kib / w_copy
+    fetch_b = f_kern * f_scale * 1024.0
+    write_b = w_kern * w_scale * 1024.0
+    out = {"kernel": "index_score_decode", "workload": DECODE_WORKLOAD,
+           "kernel_source_hash": kernel_source_hash(), "command": command,
+           "copy_probe_bytes": COPY_PROBE_BYTES,
+           "fetch_size_kib_copy": f_copy, "write_size_kib_copy": w_copy,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "fetch_size_kib_per_launch": f_kern, "write_size_kib_per_launch": w_kern,
+           "launches": n, "hbm_read_bytes_per_launch": round(fetch_b),
+           "hbm_write_bytes_per_launch": round(write_b),
+           "hbm_bytes_per_launch": round(fetch_b + write_b)}
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,7 +331,21 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
+    ap.add_argument("--summarize-kernel-trace", nargs=3, metavar=("STATS_CSV", "OUT_TXT", "CMD"),
+                    help="write the profiles/ summary of a rocprofv3 kernel-trace run")
+    ap.add_argument("--summarize-traffic", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON", "CMD"),
+                    help="write the profiles/ traffic summary of two counter runs")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="for rocprofv3 counter runs: one 128 MiB device copy (the "
+                         "calibration), then 8 decode index-kernel launches; no timing")
     args = ap.parse_args()
+    if args.summarize_kernel_trace:
+        summarize_kernel_trace(*args.summarize_kernel_trace)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -262,6 +359,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     msa.lib()
+    if args.traffic_probe:
+        traffic_probe(args, torch, msa, mi, gu)
+        return
 
     dec = run_decode_bench(args, torch, msa, mi, gu)
     pre = None if args.no_prefill else run_prefill_bench(args, torch, msa, mi, gu)
