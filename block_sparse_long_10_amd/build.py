@@ -19,6 +19,9 @@ def sources():
 def command(out: str):
     return ["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA results in ordinary VGPRs: the epilogues (max-pool, softmax)
+            # then read them without a v_accvgpr_read per value
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wall", "-Wno-unused-result",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC] + sources() + ["-o", out]
 

@@ -218,6 +218,9 @@ __global__ __launch_bounds__(256) void index_score_prefill_kernel(
 
   gload(b_lo);
   lstore(0);
+  // every load issued so far has landed: without this wait the in-loop waits
+  // for the query operands would also wait for the next block's prefetch
+  wait_vmem();
   __syncthreads();
   for (int b = b_lo; b < b_hi; ++b) {
     const int buf = (b - b_lo) & 1;
