@@ -42,6 +42,10 @@ constexpr int kCachePolicyNT = 2;
 __device__ __forceinline__ void load_lds16_stream(const void* src, void* lds_base) {
   __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)lds_base, 16, 0, kCachePolicyNT);
 }
+// The same with the default cache policy (data read again by other workgroups).
+__device__ __forceinline__ void load_lds16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)lds_base, 16, 0, 0);
+}
 // Wait for every outstanding vector-memory operation of this wave.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 

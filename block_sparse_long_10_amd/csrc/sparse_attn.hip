@@ -303,31 +303,100 @@ hipError_t launch_decode_attn(const Dims& d, const Cache& c, const uint16_t* q,
 }
 
 // --------------------------------------------------------------- prefill
+// One workgroup: 8 waves x 32 rows = 256 (query, head) rows of one (tile,
+// group).  Every kept block is staged whole (K token-major, V^T
+// dimension-major) in a two-slot LDS ring by direct global->LDS loads: block
+// j+1 streams in while block j is computed.  Workgroups are numbered so that
+// the row groups of one (tile, group) run at the same time on the same XCD and
+// share its L2 for the block data.
+constexpr int kPrefillWaves = 8;
+constexpr int kPrefillRows = kPrefillWaves * 32;
+constexpr float kRescaleSlack = 8.f;  // log2 units the running max may lag by
+
+// Chunk swizzle of a 256-byte key row: the 16 lanes that read one 16-byte
+// chunk column (keys kmap(0..15) of a 32-key sub-tile) hit 16 different
+// chunk positions.
+__device__ __forceinline__ int kswz(int key) {
+  return (key & 3) | ((key >> 1) & 4) | ((key & 4) << 1);
+}
+// Row m of a 32-key S^T tile holds key kmap(m): then value v of lane half h
+// is key 16*(v/8) + 8*h + v%8, i.e. each lane's 16 scores are two runs of 8
+// consecutive keys, exactly the P^T operand layout of the PV product.
+__device__ __forceinline__ int kmap(int m) {
+  return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
+}
+// A value and its counterpart 32 lanes away (the other half of the same row):
+// v_permlane32_swap exchanges the upper half of one register with the lower
+// half of another, so with both holding v the two results are v and its
+// counterpart, in some order.  (Written as asm: the builtin's two results are
+// merged into one when both inputs are the same value.)
+__device__ __forceinline__ void half_swap(float v, float& a, float& b) {
+  a = v;
+  b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float half_swap_max(float v) {
+  float a, b;
+  half_swap(v, a, b);
+  return __builtin_fmaxf(a, b);
+}
+__device__ __forceinline__ float half_swap_sum(float v) {
+  float a, b;
+  half_swap(v, a, b);
+  return a + b;
+}
+// bf16 pair from the upper halves of two floats (truncation).
+__device__ __forceinline__ uint32_t upper_pair(float a, float b) {
+  return (__builtin_bit_cast(uint32_t, b) & 0xFFFF0000u) | (__builtin_bit_cast(uint32_t, a) >> 16);
+}
+__device__ __forceinline__ float truncated_rest(float a) {
+  return a - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) & 0xFFFF0000u);
+}
+
 template <int B>
-__global__ __launch_bounds__(256) void prefill_attn_kernel(
+__global__ __launch_bounds__(512) void prefill_attn_kernel(
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ block_table, const uint16_t* __restrict__ q,
     const int32_t* __restrict__ sel, int32_t prior_len, int32_t chunk_len, int32_t num_kv_heads,
-    int32_t group, int32_t top_k, float scale_log2, float* __restrict__ out) {
-  constexpr int KROW = 256;            // bytes per key row (128 bf16)
-  constexpr int VROW = 2 * B;          // bytes per value^T row (B bf16)
-  constexpr int VCH = B / 8;           // 16-byte chunks per value^T row
-  constexpr int LOADS = B * 256 / (16 * 256);  // per thread, per K (and per V) block
-  __shared__ __attribute__((aligned(16))) uint8_t ks_[B * KROW];
-  __shared__ __attribute__((aligned(16))) uint8_t vs_[128 * VROW];
+    int32_t group, int32_t top_k, int32_t num_units, int32_t zr, float scale_log2,
+    float* __restrict__ out) {
+  constexpr int KBYTES = B * 256;          // K block: B rows of 256 bytes
+  constexpr int VROW = 2 * B;              // V^T row: B keys
+  constexpr int VCH = B / 8;               // 16-byte chunks per V^T row
+  constexpr int VBYTES = 128 * VROW;
+  constexpr int SLOT = KBYTES + VBYTES;
+  constexpr int KI = KBYTES / 1024 / kPrefillWaves;  // 1 KB wave loads per block, K
+  constexpr int VI = VBYTES / 1024 / kPrefillWaves;  // and V^T
+  constexpr int VRPI = 1024 / VROW;                  // V^T rows per wave load
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[2][SLOT];
+  __shared__ int32_t pages[64], blocks[64];
 
-  const int tile = blockIdx.x, g = blockIdx.y;
+  // workgroup -> (unit, row group); unit = tile * Hkv + g
+  const int wg = blockIdx.x;
+  const int unit = (wg / (8 * zr)) * 8 + (wg & 7);
+  const int z = (wg >> 3) % zr;
+  if (unit >= num_units) return;
+  const int tile = unit / num_kv_heads, g = unit % num_kv_heads;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int own = prior_len / B + tile;
   const int q0 = max(0, own * B - prior_len);
   const int q1 = min(chunk_len, (own + 1) * B - prior_len);
   const int nq = q1 - q0;
   const int nrows = nq * group;
-  const int row0 = blockIdx.z * 128;
+  const int row0 = z * kPrefillRows;
   if (row0 >= nrows) return;
   const int Hq = num_kv_heads * group;
 
-  // this lane's query row (N side): (query, head) = (q0 + r % nq, r / nq)
+  const int32_t* srow = sel + (size_t)unit * top_k;
+  int blk_t = -1;
+  if (tid < top_k) {
+    blk_t = srow[tid];
+    pages[tid] = blk_t >= 0 ? block_table[blk_t] : 0;
+    blocks[tid] = blk_t;
+  }
+  const int nsel = __syncthreads_count(tid < top_k && blk_t >= 0);
+
+  // this lane's row (N side of S^T): (query, head) = (q0 + r % nq, r / nq)
   const int half = lane >> 5;
   int r = row0 + wave * 32 + (lane & 31);
   const bool row_ok = r < nrows;
@@ -340,98 +409,125 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = load_bf16x8(qp + ks * 16);
   }
+  // the wave's query positions, for the causal diagonal block
+  const float pos_min = wave_min((float)pos), pos_max = wave_max((float)pos);
+
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(kc);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vc);
+  auto issue = [&](int j) {
+    const size_t ph = (size_t)pages[j] * num_kv_heads + g;
+    const uint8_t* kg = kbase + ph * KBYTES;
+    const uint8_t* vg = vbase + ph * VBYTES;
+    uint8_t* dst = ring[j & 1];
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int ins = wave * KI + i;
+      const int key = ins * 4 + (lane >> 4);
+      const int c = (lane & 15) ^ kswz(key);
+      load_lds16(kg + key * 256 + c * 16, dst + ins * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int ins = wave * VI + i;
+      const int dd = ins * VRPI + lane / VCH;
+      const int c = (lane % VCH) ^ (dd & (VCH - 1));
+      load_lds16(vg + dd * VROW + c * 16, dst + KBYTES + ins * 1024);
+    }
+  };
+
   f32x16 o[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) o[mt] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -1e30f, l_run = 0.f;  // m_run: row max in log2 units (lagging)
 
-  const int32_t* srow = sel + ((size_t)tile * num_kv_heads + g) * top_k;
-  for (int si = 0; si < top_k; ++si) {
-    const int blk = srow[si];
-    if (blk < 0) break;
-    const size_t page = (size_t)block_table[blk];
-    // stage K (token-major) and V^T (dimension-major) of this block
-    const uint8_t* kg = reinterpret_cast<const uint8_t*>(kc) + (page * num_kv_heads + g) * (size_t)(B * KROW);
-    const uint8_t* vg = reinterpret_cast<const uint8_t*>(vc) + (page * num_kv_heads + g) * (size_t)(128 * VROW);
+  if (nsel > 0) issue(0);
+  for (int j = 0; j < nsel; ++j) {
+    wait_vmem();
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int ch = i * 256 + tid;
-      const u32x4 kv = *reinterpret_cast<const u32x4*>(kg + (size_t)ch * 16);
-      const u32x4 vv = *reinterpret_cast<const u32x4*>(vg + (size_t)ch * 16);
-      const int kt = ch >> 4, kcn = ch & 15;
-      *reinterpret_cast<u32x4*>(&ks_[kt * KROW + ((kcn ^ (kt & 15)) << 4)]) = kv;
-      const int vd = ch / VCH, vcn = ch % VCH;
-      *reinterpret_cast<u32x4*>(&vs_[vd * VROW + ((vcn ^ (vd & (VCH - 1))) << 4)]) = vv;
-    }
-    __syncthreads();
-    const bool diag = blk == own;
-#pragma unroll 1
-    for (int kt = 0; kt < B / 32; ++kt) {
-      // S^T: A = K rows; M row m of the tile is key kmap(m) so that value v of
-      // lane half h is key 16*(v/8) + 8*h + v%8.
-      const int m = lane & 31;
-      const int key = kt * 32 + 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
-      f32x16 acc = {};
+    if (j + 1 < nsel) issue(j + 1);
+    const uint8_t* ks_ = ring[j & 1];
+    const uint8_t* vs_ = ks_ + KBYTES;
+    const bool diag = blocks[j] == own;
+    const int key0 = own * B;
+    const int m = lane & 31;
+    auto load_k = [&](int s, bf16x8* kf) {
+      const int key = s * 32 + kmap(m);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const int c = ks * 2 + half;
-        const bf16x8 kf = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(&ks_[key * KROW + ((c ^ (key & 15)) << 4)]));
-        acc = mfma32(kf, qf[ks], acc);
+        kf[ks] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(ks_ + key * 256 + ((c ^ kswz(key)) << 4)));
       }
-      float z[16];
-      float mloc = -INFINITY;
+    };
+    bf16x8 kf[2][8];
+    load_k(0, kf[0]);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int kk = kt * 32 + 16 * (v >> 3) + 8 * half + (v & 7);
-        const bool ok = !diag || (blk * B + kk) <= pos;
-        z[v] = ok ? acc[v] * scale_log2 : -INFINITY;
-        mloc = fmaxf(mloc, z[v]);
-      }
-      mloc = fmaxf(mloc, xor_lane(mloc, 32));
-      // control flow stays wave-uniform around the MFMAs: a row that sees no
-      // key yet keeps alpha = 1 and p = 0
-      const float m_new = fmaxf(m_run, mloc);
-      const float alpha =
-          m_new == -INFINITY ? 1.f : (m_run == -INFINITY ? 0.f : exp2f(m_run - m_new));
-      float p[16], psum = 0.f;
+    for (int s = 0; s < B / 32; ++s) {
+      if (diag && (float)(key0 + 32 * s) > pos_max) break;  // wave sees none of these keys
+      f32x16 acc = {};
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        p[v] = z[v] == -INFINITY ? 0.f : exp2f(z[v] - m_new);
-        psum += p[v];
-      }
-      psum += xor_lane(psum, 32);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
+      for (int ks = 0; ks < 8; ++ks) acc = mfma32(kf[s & 1][ks], qf[ks], acc);
+      if (s + 1 < B / 32) load_k(s + 1, kf[(s + 1) & 1]);
+      bf16x8 vf[2][4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[mt][v] *= alpha;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        uint32_t hi[8], lo[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) split_bf16(p[8 * s2 + j], hi[j], lo[j]);
-        const bf16x8 phi = __builtin_bit_cast(
-            bf16x8, u32x4{pack2(hi[0], hi[1]), pack2(hi[2], hi[3]), pack2(hi[4], hi[5]), pack2(hi[6], hi[7])});
-        const bf16x8 plo = __builtin_bit_cast(
-            bf16x8, u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(lo[4], lo[5]), pack2(lo[6], lo[7])});
-        const int vch = kt * 4 + 2 * s2 + half;  // chunk of keys kt*32 + 16*s2 + 8*half
+      for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          const int dd = mt * 32 + (lane & 31);
-          const bf16x8 vf = __builtin_bit_cast(
-              bf16x8,
-              *reinterpret_cast<const u32x4*>(&vs_[dd * VROW + ((vch ^ (dd & (VCH - 1))) << 4)]));
-          o[mt] = mfma32(vf, phi, o[mt]);
-          o[mt] = mfma32(vf, plo, o[mt]);
+          const int dd = mt * 32 + m;
+          const int vch = s * 4 + 2 * s2 + half;  // keys 32*s + 16*s2 + 8*half ...
+          vf[s2][mt] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(vs_ + dd * VROW + ((vch ^ (dd & (VCH - 1))) << 4)));
+        }
+      if (diag && (float)(key0 + 32 * s + 31) > pos_min) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int kk = 32 * s + 16 * (v >> 3) + 8 * half + (v & 7);
+          if (key0 + kk > pos) acc[v] = -INFINITY;
+        }
+      }
+      float mx = acc[0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mx = __builtin_fmaxf(mx, acc[v]);
+      mx = half_swap_max(mx) * scale_log2;
+      if (__ballot(mx > m_run + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[mt][v] *= alpha;
+        m_run = m_new;
+      }
+      float p[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        p[v] = __builtin_amdgcn_exp2f(fmaf(acc[v], scale_log2, -m_run));
+        l_run += p[v];
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        // P = hi + lo in bfloat16, hi the truncation of P: P - hi - lo < 2^-16 P
+        const float* pp = p + 8 * s2;
+        const bf16x8 phi = __builtin_bit_cast(
+            bf16x8, u32x4{upper_pair(pp[0], pp[1]), upper_pair(pp[2], pp[3]),
+                          upper_pair(pp[4], pp[5]), upper_pair(pp[6], pp[7])});
+        const bf16x8 plo = __builtin_bit_cast(
+            bf16x8, u32x4{upper_pair(truncated_rest(pp[0]), truncated_rest(pp[1])),
+                          upper_pair(truncated_rest(pp[2]), truncated_rest(pp[3])),
+                          upper_pair(truncated_rest(pp[4]), truncated_rest(pp[5])),
+                          upper_pair(truncated_rest(pp[6]), truncated_rest(pp[7]))});
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          o[mt] = mfma32(vf[s2][mt], phi, o[mt]);
+          o[mt] = mfma32(vf[s2][mt], plo, o[mt]);
         }
       }
     }
   }
+  const float l_row = half_swap_sum(l_run);
   if (!row_ok) return;
-  const float inv = 1.f / l_run;
+  const float inv = 1.f / l_row;
   float* op = out + ((size_t)qi * Hq + (size_t)g * group + hh) * 128;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -451,17 +547,18 @@ hipError_t launch_sparse_attn_prefill(const Dims& d, const Cache& c, const uint1
   const int G = d.num_q_heads / d.num_kv_heads;
   const int first = prior_len / B;
   const int num_tiles = (prior_len + chunk_len + B - 1) / B - first;
-  const int zr = (B * G + 127) / 128;
+  const int units = num_tiles * d.num_kv_heads;
+  const int zr = (B * G + kPrefillRows - 1) / kPrefillRows;
+  const int nwg = (units + 7) / 8 * 8 * zr;
   const float sl2 = d.softmax_scale * kLog2e;
-  dim3 grid(num_tiles, d.num_kv_heads, zr);
   if (B == 64)
-    hipLaunchKernelGGL(prefill_attn_kernel<64>, grid, dim3(256), 0, stream, c.k, c.v,
+    hipLaunchKernelGGL(prefill_attn_kernel<64>, dim3(nwg), dim3(512), 0, stream, c.k, c.v,
                        c.block_table, q, sel, prior_len, chunk_len, d.num_kv_heads, G, d.top_k,
-                       sl2, out);
+                       units, zr, sl2, out);
   else
-    hipLaunchKernelGGL(prefill_attn_kernel<128>, grid, dim3(256), 0, stream, c.k, c.v,
+    hipLaunchKernelGGL(prefill_attn_kernel<128>, dim3(nwg), dim3(512), 0, stream, c.k, c.v,
                        c.block_table, q, sel, prior_len, chunk_len, d.num_kv_heads, G, d.top_k,
-                       sl2, out);
+                       units, zr, sl2, out);
   return hipGetLastError();
 }
 
