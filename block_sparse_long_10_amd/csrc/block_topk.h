@@ -257,6 +257,37 @@ __device__ __forceinline__ void wave_sort_desc(uint32_t& v) {
   bitonic_merge<64>(v);
 }
 
+// The same for (key, index) pairs ordered by key descending, then index
+// ascending (the selection order).
+template <int K, int J>
+__device__ __forceinline__ void bitonic_stage2(uint32_t& key, uint32_t& idx) {
+  const uint32_t ok = xor_exchange<J>(key), oi = xor_exchange<J>(idx);
+  const int lane = threadIdx.x & (kWave - 1);
+  const bool take_max = ((lane & J) == 0) == ((lane & K) == 0);
+  const bool other_first = ok > key || (ok == key && oi < idx);
+  const bool take_other = take_max == other_first;
+  key = take_other ? ok : key;
+  idx = take_other ? oi : idx;
+}
+template <int K>
+__device__ __forceinline__ void bitonic_merge2(uint32_t& key, uint32_t& idx) {
+  if constexpr (K >= 64) bitonic_stage2<K, 32>(key, idx);
+  if constexpr (K >= 32) bitonic_stage2<K, 16>(key, idx);
+  if constexpr (K >= 16) bitonic_stage2<K, 8>(key, idx);
+  if constexpr (K >= 8) bitonic_stage2<K, 4>(key, idx);
+  if constexpr (K >= 4) bitonic_stage2<K, 2>(key, idx);
+  bitonic_stage2<K, 1>(key, idx);
+}
+// Sort 64 (key, index) pairs of a wave into selection order: lane 0 first.
+__device__ __forceinline__ void wave_sort_pairs(uint32_t& key, uint32_t& idx) {
+  bitonic_merge2<2>(key, idx);
+  bitonic_merge2<4>(key, idx);
+  bitonic_merge2<8>(key, idx);
+  bitonic_merge2<16>(key, idx);
+  bitonic_merge2<32>(key, idx);
+  bitonic_merge2<64>(key, idx);
+}
+
 // Wave inclusive prefix sum with DPP: row shifts, then row broadcasts.
 __device__ __forceinline__ int wave_incl_scan(int v) {
   v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
@@ -351,19 +382,11 @@ __device__ __forceinline__ bool topk_fast(const RegKeys<MAXV>& src, int own, int
   }
   __syncthreads();
   if (wave == 0) {
-    // rank of candidate `lane` by (key desc, index asc), counted against all
-    // 64 slots (empty ones rank last)
-    const uint32_t key = sh.cand_k[lane];
-    const int idx = sh.cand_i[lane];
-    int rank = 0;
-#pragma unroll
-    for (int j = 0; j < kWave; ++j) {
-      const uint32_t kj = sh.cand_k[j];
-      const int ij = sh.cand_i[j];
-      rank += (kj > key) || (kj == key && ij < idx);
-    }
-    // kept indices ascending: sort ~index descending (others sort last)
-    uint32_t v = lane < total && rank < keep ? ~(uint32_t)idx : 0u;
+    // the 64 slots in selection order (empty ones sort last), then the first
+    // `keep` indices ascending: sort ~index descending (others sort last)
+    uint32_t key = sh.cand_k[lane], idx = (uint32_t)sh.cand_i[lane];
+    wave_sort_pairs(key, idx);
+    uint32_t v = lane < keep ? ~idx : 0u;
     wave_sort_desc(v);
     if (lane < keep) out_sel[lane] = (int)~v;
     if (lane == 0) out_sel[keep] = own;
