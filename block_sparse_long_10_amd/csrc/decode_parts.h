@@ -1,0 +1,311 @@
+// Device building blocks of the MSA decode step (index kernel, then the TopK
+// + attention kernel):
+//   index_block_scores  - pooled index scores of one KV block, all groups
+//                         ("MiniMax wird dünn", section 1, Schritt 1)
+//   attend_block        - softmax attention of a group's heads over one kept
+//                         block, as a partial (max, sum, unnormalised output)
+//                         (section 1, Schritt 2)
+//   merge_partials      - log-sum-exp merge of a group's partials
+#pragma once
+
+#include "msa_device.h"
+
+namespace msa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Cross-workgroup hand-off without a cache write-back: every value another
+// workgroup reads is written with an agent-scope (sc1) store, which writes
+// through to the point where the caches of all XCDs are coherent, and read
+// with an agent-scope (sc1) load.  Buffer instructions carry the cache policy
+// and move 16 bytes per lane (the (max, sum) pair of a head is padded to 16
+// bytes; only the 16-byte buffer forms are used).
+constexpr int kCachePolicySC1 = 16;
+constexpr int kBufferDword3 = 0x00020000;  // raw 32-bit elements (gfx9 family)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kBufferDword3);
+}
+__device__ __forceinline__ void store_shared4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kCachePolicySC1);
+}
+__device__ __forceinline__ f32x4 load_shared4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCachePolicySC1));
+}
+
+// ------------------------------------------------------------ index scores
+// One wave scores KV block b of one sequence against all Hkv*NI index-query
+// rows of the sequence (row = group*NI + head; 32 rows at 8 groups x 4
+// heads; MT = ceil(rows / 16) MFMA tiles).  The block's index keys (B tokens
+// x 128 bytes) are streamed with 1 KB wave-contiguous direct-to-LDS loads
+// (global_load_lds_dwordx4, non-temporal): lane l of load i fills bytes
+// i*1024 + 16*l of `stage`, i.e. token 8i + l/8 and chunk slot l%8, and reads
+// the source chunk (l%8) ^ (l/8), so the LDS image is XOR-swizzled and the
+// MFMA operand reads (16 tokens x one chunk per instruction) hit distinct
+// banks.  The rows are the M side of v_mfma_f32_16x16x32_bf16; the 16x16
+// score tiles fold into per-row running maxima and a DPP row reduction gives
+// the block max of each group, which emit(g, value) receives (one lane per
+// group calls it).
+template <int B, int NI, int MT, class Emit>
+__device__ __forceinline__ void index_block_scores(const uint16_t* __restrict__ idx_k,
+                                                   int32_t page, const uint16_t* __restrict__ idx_q_s,
+                                                   int num_kv_heads, uint8_t* stage, Emit emit) {
+  constexpr int BYTES = B * 128;     // one block of index keys
+  constexpr int NLD = BYTES / 1024;  // 1 KB wave loads per block
+  constexpr int NT = B / 16;         // 16-token MFMA tiles per block
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(idx_k) + (size_t)page * BYTES;
+  const int src_off = (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) << 4);
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) load_lds16_stream(src + i * 1024 + src_off, stage + i * 1024);
+
+  // A operand: index-query rows; K split: dims ks*32 + 8*q4 .. +7, the same
+  // for the keys below.
+  const int R = num_kv_heads * NI;
+  const int r16 = lane & 15, q4 = lane >> 4;
+  // (no branches around the loads; padding rows read row R-1 and are zeroed)
+  bf16x8 a[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int row = mt * 16 + r16;
+    const uint16_t* p = idx_q_s + (size_t)min(row, R - 1) * 64 + q4 * 8;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) a[mt][ks] = load_bf16x8(p + ks * 32);
+  }
+  wait_vmem();  // the LDS image and the queries are in place (one wave: no barrier)
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) a[mt][ks] = mt * 16 + r16 < R ? a[mt][ks] : zero_bf16x8();
+
+  f32x4 rmax[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) rmax[mt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int t = nt * 16 + r16;  // B operand: token t
+    bf16x8 kb[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c = ks * 4 + q4;
+      kb[ks] = __builtin_bit_cast(bf16x8,
+                                  *reinterpret_cast<const u32x4*>(&stage[t * 128 + ((c ^ (t & 7)) << 4)]));
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma16(a[mt][0], kb[0], acc);
+      acc = mfma16(a[mt][1], kb[1], acc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rmax[mt][j] = fmaxf(rmax[mt][j], acc[j]);
+    }
+  }
+  // lane holds rows mt*16 + 4*q4 + j; reduce over the 16 token lanes, then
+  // over the rows of each group.
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int row0 = mt * 16 + q4 * 4;
+    if constexpr (NI >= 4) {
+      float v = row16_max(max4(rmax[mt]));
+      if constexpr (NI >= 8) v = fmaxf(v, xor_lane(v, 16));
+      if constexpr (NI >= 16) v = fmaxf(v, xor_lane(v, 32));
+      const int g = row0 / NI;
+      if (r16 == 0 && (row0 % NI) == 0 && g < num_kv_heads) emit(g, v);
+    } else {
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = row16_max(rmax[mt][j]);
+      if (r16 == 0) {
+        if constexpr (NI == 2) {
+          const int g = row0 / 2;
+          if (g < num_kv_heads) emit(g, fmaxf(v[0], v[1]));
+          if (g + 1 < num_kv_heads) emit(g + 1, fmaxf(v[2], v[3]));
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (row0 + j < num_kv_heads) emit(row0 + j, v[j]);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------- block attention
+// Per-wave partials combined in LDS.
+struct AttendShared {
+  float w_m[4][16], w_l[4][16];
+  float w_o[4][16][128 + 4];
+};
+
+// Attention of the G heads of group g of sequence s over kept block blk
+// (blk < 0: an empty slot) by a 256-thread workgroup: 4 waves x 32 tokens,
+// S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 (heads padded to
+// 16), the per-wave partials combined in LDS.  The result is stored as the
+// partial of `slot`: o at ro[(slot*G + h)*128 ..] and (max, sum) at
+// rml[(slot*G + h)*16] (16-byte records), both with agent-scope stores.
+// Probabilities enter the PV contraction as hi + lo bf16 parts
+// (P - hi - lo < 2^-16 P).
+template <int B>
+__device__ __forceinline__ void attend_block(const uint16_t* __restrict__ kc,
+                                             const uint16_t* __restrict__ vc, int32_t page,
+                                             int blk, int L, const uint16_t* __restrict__ q_sg,
+                                             int num_kv_heads, int g, int group, float scale_log2,
+                                             int slot, __amdgpu_buffer_rsrc_t ro,
+                                             __amdgpu_buffer_rsrc_t rml, AttendShared& sh) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  if (blk < 0) {
+    for (int h = tid; h < group; h += 256)
+      store_shared4(rml, (slot * group + h) * 16, f32x4{-INFINITY, 0.f, 0.f, 0.f});
+    return;
+  }
+  const int n_valid = min(B, L - blk * B);
+  const int t0 = wave * 32;
+  const int r16 = lane & 15, q4 = lane >> 4;
+  float m_w = -INFINITY, l_w = 0.f;
+  f32x4 o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (t0 < n_valid) {
+    // all loads first: Q^T (B operand, head r16), K rows (A operand), V^T (A operand)
+    // (no branches around the loads: a join would wait for them; padding
+    // heads read head group-1 and are zeroed afterwards)
+    bf16x8 qf[4], kf[2][4], vf[8];
+    const uint16_t* qp = q_sg + (size_t)min(r16, group - 1) * 128 + q4 * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = load_bf16x8(qp + ks * 32);
+    // S^T tiles: M row r of tile mt is token t0 + 8*(r>>2) + 4*mt + (r&3), so
+    // that lane (r16, q4) ends up with tokens t0 + 8*q4 + 0..7 of head r16.
+    const uint16_t* kp = kc + ((size_t)page * num_kv_heads + g) * (size_t)(B * 128);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int tok = t0 + 8 * (r16 >> 2) + 4 * mt + (r16 & 3);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kf[mt][ks] = load_bf16x8(kp + (size_t)tok * 128 + q4 * 8 + ks * 32);
+    }
+    const uint16_t* vp = vc + ((size_t)page * num_kv_heads + g) * (size_t)(128 * B) + t0 + 8 * q4;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) vf[mt] = load_bf16x8(vp + (size_t)(16 * mt + r16) * B);
+
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = r16 < group ? qf[ks] : zero_bf16x8();
+    float z[8];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = mfma16(kf[mt][ks], qf[ks], acc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tok = t0 + 8 * q4 + 4 * mt + j;
+        z[mt * 4 + j] = tok < n_valid ? acc[j] * scale_log2 : -INFINITY;
+      }
+    }
+    float mx = z[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
+    mx = fmaxf(mx, xor_lane(mx, 16));
+    mx = fmaxf(mx, xor_lane(mx, 32));
+    float p[8], sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = z[i] == -INFINITY ? 0.f : exp2f(z[i] - mx);
+      sum += p[i];
+    }
+    sum += xor_lane(sum, 16);
+    sum += xor_lane(sum, 32);
+    m_w = mx;
+    l_w = sum;
+    // P^T as the B operand (keys 8*q4 + j of head r16), hi + lo bf16 parts
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) split_bf16(p[i], hi[i], lo[i]);
+    const bf16x8 phi = __builtin_bit_cast(
+        bf16x8, u32x4{pack2(hi[0], hi[1]), pack2(hi[2], hi[3]), pack2(hi[4], hi[5]), pack2(hi[6], hi[7])});
+    const bf16x8 plo = __builtin_bit_cast(
+        bf16x8, u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(lo[4], lo[5]), pack2(lo[6], lo[7])});
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      o[mt] = mfma16(vf[mt], phi, o[mt]);
+      o[mt] = mfma16(vf[mt], plo, o[mt]);
+    }
+  }
+  // o[mt][j] = O^T[dim 16*mt + 4*q4 + j][head r16]
+  if (lane < 16) {
+    sh.w_m[wave][lane] = m_w;
+    sh.w_l[wave][lane] = l_w;
+  }
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sh.w_o[wave][r16][16 * mt + 4 * q4 + j] = o[mt][j];
+  __syncthreads();
+  // combine the waves: thread -> (head h, dims 4*d4 .. +3)
+  for (int idx = tid; idx < group * 32; idx += 256) {
+    const int h = idx >> 5, d4 = idx & 31;
+    float M = sh.w_m[0][h];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, sh.w_m[w][h]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (sh.w_m[w][h] == -INFINITY) continue;
+      const float e = exp2f(sh.w_m[w][h] - M);
+      l += e * sh.w_l[w][h];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += e * sh.w_o[w][h][4 * d4 + j];
+    }
+    store_shared4(ro, ((slot * group + h) * 128 + 4 * d4) * 4, acc);
+    if (d4 == 0) store_shared4(rml, (slot * group + h) * 16, f32x4{M, l, 0.f, 0.f});
+  }
+}
+
+// Log-sum-exp merge of the top_k partials of one (sequence, group) into
+// out_sg[h*128 ..] (256 threads): thread -> (head h, dims 4*d4 .. +3); the
+// partial loads of 16 slots are issued together and folded into a running
+// (max, sum, output).
+__device__ __forceinline__ void merge_partials(__amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rml,
+                                               int top_k, int group, float* __restrict__ out_sg) {
+  constexpr int kChunk = 16;
+  for (int idx = threadIdx.x; idx < group * 32; idx += 256) {
+    const int h = idx >> 5, d4 = idx & 31;
+    float M = -INFINITY, den = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < top_k; k0 += kChunk) {
+      float m[kChunk], l[kChunk];
+      f32x4 o[kChunk];
+      // no branches around the loads (a join would wait for them): slots
+      // past top_k read beyond the buffer range, which returns zeros, and
+      // are masked afterwards
+#pragma unroll
+      for (int k = 0; k < kChunk; ++k) {
+        const f32x4 v = load_shared4(rml, ((k0 + k) * group + h) * 16);
+        o[k] = load_shared4(ro, (((k0 + k) * group + h) * 128 + 4 * d4) * 4);
+        m[k] = k0 + k < top_k ? v[0] : -INFINITY;
+        l[k] = v[1];
+      }
+      // branch-free fold (selects, not products: an empty slot's partial
+      // output is stale memory)
+      float Mc = M;
+#pragma unroll
+      for (int k = 0; k < kChunk; ++k) Mc = fmaxf(Mc, m[k]);
+      const float r = M == -INFINITY ? 0.f : exp2f(M - Mc);
+      den *= r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] *= r;
+#pragma unroll
+      for (int k = 0; k < kChunk; ++k) {
+        const bool live = m[k] != -INFINITY;
+        const float e = exp2f(live ? m[k] - Mc : -INFINITY);
+        den = live ? den + e * l[k] : den;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = live ? acc[j] + e * o[k][j] : acc[j];
+      }
+      M = Mc;
+    }
+    const float inv = 1.f / den;
+    *reinterpret_cast<f32x4*>(out_sg + (size_t)h * 128 + 4 * d4) =
+        f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+  }
+}
+
+}  // namespace msa

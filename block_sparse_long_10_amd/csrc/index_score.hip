@@ -16,104 +16,30 @@
 // (XOR-swizzled 16-byte chunks, double-buffered) as the B side.  The 32x32
 // accumulators are folded with v_max into one running max per lane and
 // reduced across the workgroup once per block.
+#include "decode_parts.h"
 #include "msa_device.h"
 #include "msa_launch.h"
 
 namespace msa {
 
 // ---------------------------------------------------------------- decode
-// One wave per workgroup and one block per wave.  The block's index keys
-// (B tokens x 128 bytes) are streamed with 1 KB wave-contiguous direct-to-LDS
-// loads (global_load_lds_dwordx4, non-temporal): lane l of load i fills LDS
-// bytes i*1024 + 16*l, i.e. token 8i + l/8 and chunk slot l%8, and reads the
-// source chunk (l%8) ^ (l/8), so the LDS image is XOR-swizzled and the MFMA
-// operand reads (16 tokens x one chunk per instruction) hit distinct banks.
-// Small single-wave workgroups let ten blocks per CU be in flight.
+// One wave per workgroup and one block per wave (index_block_scores); small
+// single-wave workgroups let ten blocks per CU be in flight.
 template <int B, int NI, int MT>
 __global__ __launch_bounds__(64) void index_score_decode_kernel(
     const uint16_t* __restrict__ idx_k, const int32_t* __restrict__ block_table,
     int32_t max_blocks, const uint16_t* __restrict__ idx_q, const int32_t* __restrict__ seq_lens,
     int32_t num_kv_heads, float* __restrict__ pooled, uint32_t* __restrict__ counters) {
-  constexpr int BYTES = B * 128;     // one block of index keys
-  constexpr int NLD = BYTES / 1024;  // 1 KB wave loads per block
-  constexpr int NT = B / 16;         // 16-token MFMA tiles per block
-  __shared__ __attribute__((aligned(16))) uint8_t stage[BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[B * 128];
   const int s = blockIdx.y, b = blockIdx.x;
   const int lane = threadIdx.x;
   if (counters != nullptr && b == 0 && lane < num_kv_heads) counters[s * num_kv_heads + lane] = 0u;
   const int own = (seq_lens[s] - 1) / B;
   if (b >= own) return;
-  const uint8_t* page =
-      reinterpret_cast<const uint8_t*>(idx_k) + (size_t)block_table[(size_t)s * max_blocks + b] * BYTES;
-  const int src_off = (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) << 4);
-#pragma unroll
-  for (int i = 0; i < NLD; ++i) load_lds16_stream(page + i * 1024 + src_off, &stage[i * 1024]);
-
-  // A operand: index-query rows (row = group*NI + head); K split: dims
-  // ks*32 + 8*q4 .. +7, the same for the keys below.
-  const int R = num_kv_heads * NI;
-  const int r16 = lane & 15, q4 = lane >> 4;
-  bf16x8 a[MT][2];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int row = mt * 16 + r16;
-    const uint16_t* p = idx_q + ((size_t)s * R + row) * 64 + q4 * 8;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) a[mt][ks] = row < R ? load_bf16x8(p + ks * 32) : zero_bf16x8();
-  }
-  wait_vmem();  // the LDS image and the queries are in place (one wave: no barrier)
-
-  f32x4 rmax[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) rmax[mt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int t = nt * 16 + r16;  // B operand: token t
-    bf16x8 kb[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int c = ks * 4 + q4;
-      kb[ks] = __builtin_bit_cast(bf16x8,
-                                  *reinterpret_cast<const u32x4*>(&stage[t * 128 + ((c ^ (t & 7)) << 4)]));
-    }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma16(a[mt][0], kb[0], acc);
-      acc = mfma16(a[mt][1], kb[1], acc);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) rmax[mt][j] = fmaxf(rmax[mt][j], acc[j]);
-    }
-  }
-  // lane holds rows mt*16 + 4*q4 + j; reduce over the 16 token lanes, then
-  // over the rows of each group.
-  float* out = pooled + (size_t)s * num_kv_heads * max_blocks;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int row0 = mt * 16 + q4 * 4;
-    if constexpr (NI >= 4) {
-      float v = row16_max(max4(rmax[mt]));
-      if constexpr (NI >= 8) v = fmaxf(v, xor_lane(v, 16));
-      if constexpr (NI >= 16) v = fmaxf(v, xor_lane(v, 32));
-      const int g = row0 / NI;
-      if (r16 == 0 && (row0 % NI) == 0 && g < num_kv_heads) out[(size_t)g * max_blocks + b] = v;
-    } else {
-      float v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = row16_max(rmax[mt][j]);
-      if (r16 == 0) {
-        if constexpr (NI == 2) {
-          const int g = row0 / 2;
-          if (g < num_kv_heads) out[(size_t)g * max_blocks + b] = fmaxf(v[0], v[1]);
-          if (g + 1 < num_kv_heads) out[(size_t)(g + 1) * max_blocks + b] = fmaxf(v[2], v[3]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (row0 + j < num_kv_heads) out[(size_t)(row0 + j) * max_blocks + b] = v[j];
-        }
-      }
-    }
-  }
+  float* out = pooled + (size_t)s * num_kv_heads * max_blocks + b;
+  index_block_scores<B, NI, MT>(idx_k, block_table[(size_t)s * max_blocks + b],
+                                idx_q + (size_t)s * num_kv_heads * NI * 64, num_kv_heads, stage,
+                                [&](int g, float v) { out[(size_t)g * max_blocks] = v; });
 }
 
 template <int B, int NI>

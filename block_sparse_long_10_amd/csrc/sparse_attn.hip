@@ -24,12 +24,11 @@
 // consumed 32 keys at a time with v_mfma_f32_32x32x16_bf16 and an online
 // softmax; the causal mask applies inside the tile's diagonal block only.
 #include "block_topk.h"
+#include "decode_parts.h"
 #include "msa_device.h"
 #include "msa_launch.h"
 
 namespace msa {
-
-constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------- decode
 // TopK of every (sequence, group): one workgroup each (large batches).
@@ -44,27 +43,6 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(const float* __restric
   const size_t sg = (size_t)s * num_kv_heads + g;
   block_topk(pooled + sg * max_blocks, (seq_lens[s] - 1) / B, top_k, sel_s, sh);
   for (int i = threadIdx.x; i < top_k; i += 256) sel[sg * top_k + i] = sel_s[i];
-}
-
-// Cross-workgroup hand-off of the partials without a cache write-back: every
-// value another workgroup reads is written with an agent-scope (sc1) store,
-// which writes through to the point where the caches of all XCDs are
-// coherent; the writer waits until its stores have completed before it
-// increments the (sequence, group) counter with an agent-scope atomic, and
-// the last workgroup reads the partials with agent-scope (sc1) loads issued
-// after its increment returned.  Buffer instructions carry the cache policy
-// and move 16 bytes per lane (the (max, sum) pair of a head is padded to 16
-// bytes; only the 16-byte buffer forms are used).
-constexpr int kCachePolicySC1 = 16;
-constexpr int kBufferDword3 = 0x00020000;  // raw 32-bit elements (gfx9 family)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kBufferDword3);
-}
-__device__ __forceinline__ void store_shared4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kCachePolicySC1);
-}
-__device__ __forceinline__ f32x4 load_shared4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCachePolicySC1));
 }
 
 // Attention of the G heads of group g over one kept block (slot) of
@@ -83,16 +61,14 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
     uint32_t* __restrict__ counters, float* __restrict__ out) {
   __shared__ TopkShared tsh;
   __shared__ int sel_s[kMaxTopK];
-  __shared__ float w_m[4][16], w_l[4][16];
-  __shared__ float w_o[4][16][128 + 4];
+  __shared__ AttendShared ash;
   __shared__ int is_last;
 
   const int slot = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int tid = threadIdx.x;
   const int Hq = num_kv_heads * group;
   const int L = seq_lens[s];
   const size_t sg = (size_t)s * num_kv_heads + g;
-  const size_t pbase = sg * top_k + slot;
   int blk;
   if constexpr (FUSED_TOPK) {
     block_topk(pooled + sg * max_blocks, (L - 1) / B, top_k, sel_s, tsh);
@@ -100,118 +76,20 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
       for (int i = tid; i < top_k; i += 256) sel[sg * top_k + i] = sel_s[i];
     blk = sel_s[slot];
   } else {
-    blk = sel[pbase];
+    blk = sel[sg * top_k + slot];
   }
 
   // partials of (s, g): o [top_k][group][128] and (m, l, -, -) [top_k][group]
   const uint32_t o_bytes = (uint32_t)top_k * group * 128 * 4, ml_bytes = (uint32_t)top_k * group * 16;
   const __amdgpu_buffer_rsrc_t ro = buffer_of(part_o + sg * top_k * group * 128, o_bytes);
   const __amdgpu_buffer_rsrc_t rml = buffer_of(part_ml + sg * top_k * group * 4, ml_bytes);
-  if (blk < 0) {
-    for (int h = tid; h < group; h += 256)
-      store_shared4(rml, (slot * group + h) * 16, f32x4{-INFINITY, 0.f, 0.f, 0.f});
-  } else {
-    const int n_valid = min(B, L - blk * B);
-    const size_t page = (size_t)block_table[(size_t)s * max_blocks + blk];
-    const int t0 = wave * 32;
-    const int r16 = lane & 15, q4 = lane >> 4;
-    float m_w = -INFINITY, l_w = 0.f;
-    f32x4 o[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (t0 < n_valid) {
-      // all loads first: Q^T (B operand, head r16), K rows (A operand), V^T (A operand)
-      bf16x8 qf[4], kf[2][4], vf[8];
-      const uint16_t* qp = q + ((size_t)s * Hq + (size_t)g * group + r16) * 128 + q4 * 8;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qf[ks] = r16 < group ? load_bf16x8(qp + ks * 32) : zero_bf16x8();
-      // S^T tiles: M row r of tile mt is token t0 + 8*(r>>2) + 4*mt + (r&3), so
-      // that lane (r16, q4) ends up with tokens t0 + 8*q4 + 0..7 of head r16.
-      const uint16_t* kp = kc + (page * num_kv_heads + g) * (size_t)(B * 128);
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int tok = t0 + 8 * (r16 >> 2) + 4 * mt + (r16 & 3);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          kf[mt][ks] = load_bf16x8(kp + (size_t)tok * 128 + q4 * 8 + ks * 32);
-      }
-      const uint16_t* vp = vc + (page * num_kv_heads + g) * (size_t)(128 * B) + t0 + 8 * q4;
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) vf[mt] = load_bf16x8(vp + (size_t)(16 * mt + r16) * B);
+  const int32_t page = blk >= 0 ? block_table[(size_t)s * max_blocks + blk] : 0;
+  attend_block<B>(kc, vc, page, blk, L, q + ((size_t)s * Hq + (size_t)g * group) * 128,
+                  num_kv_heads, g, group, scale_log2, slot, ro, rml, ash);
 
-      float z[8];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mfma16(kf[mt][ks], qf[ks], acc);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int tok = t0 + 8 * q4 + 4 * mt + j;
-          z[mt * 4 + j] = tok < n_valid ? acc[j] * scale_log2 : -INFINITY;
-        }
-      }
-      float mx = z[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
-      mx = fmaxf(mx, xor_lane(mx, 16));
-      mx = fmaxf(mx, xor_lane(mx, 32));
-      float p[8], sum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = z[i] == -INFINITY ? 0.f : exp2f(z[i] - mx);
-        sum += p[i];
-      }
-      sum += xor_lane(sum, 16);
-      sum += xor_lane(sum, 32);
-      m_w = mx;
-      l_w = sum;
-      // P^T as the B operand (keys 8*q4 + j of head r16), hi + lo bf16 parts
-      uint32_t hi[8], lo[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) split_bf16(p[i], hi[i], lo[i]);
-      const bf16x8 phi = __builtin_bit_cast(
-          bf16x8, u32x4{pack2(hi[0], hi[1]), pack2(hi[2], hi[3]), pack2(hi[4], hi[5]), pack2(hi[6], hi[7])});
-      const bf16x8 plo = __builtin_bit_cast(
-          bf16x8, u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(lo[4], lo[5]), pack2(lo[6], lo[7])});
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        o[mt] = mfma16(vf[mt], phi, o[mt]);
-        o[mt] = mfma16(vf[mt], plo, o[mt]);
-      }
-    }
-    // o[mt][j] = O^T[dim 16*mt + 4*q4 + j][head r16]
-    if (lane < 16) {
-      w_m[wave][lane] = m_w;
-      w_l[wave][lane] = l_w;
-    }
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) w_o[wave][r16][16 * mt + 4 * q4 + j] = o[mt][j];
-    __syncthreads();
-    // combine the waves: thread -> (head h, dims 4*d4 .. +3)
-    for (int idx = tid; idx < group * 32; idx += 256) {
-      const int h = idx >> 5, d4 = idx & 31;
-      float M = w_m[0][h];
-#pragma unroll
-      for (int w = 1; w < 4; ++w) M = fmaxf(M, w_m[w][h]);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      float l = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        if (w_m[w][h] == -INFINITY) continue;
-        const float e = exp2f(w_m[w][h] - M);
-        l += e * w_l[w][h];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] += e * w_o[w][h][4 * d4 + j];
-      }
-      store_shared4(ro, ((slot * group + h) * 128 + 4 * d4) * 4, acc);
-      if (d4 == 0) store_shared4(rml, (slot * group + h) * 16, f32x4{M, l, 0.f, 0.f});
-    }
-  }
-
-  // hand-off: stores complete, then count this slot in
+  // hand-off: stores complete, then count this slot in; the last slot
+  // workgroup reads the partials with agent-scope loads issued after its
+  // increment returned
   wait_vmem();
   __syncthreads();
   if (tid == 0)
@@ -219,51 +97,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
                                      __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(top_k - 1);
   __syncthreads();
   if (!is_last) return;
-
-  // log-sum-exp merge of the top_k partials of (s, g): thread -> (head h,
-  // dims 4*d4 .. +3); the partial loads of 16 slots are issued together and
-  // folded into a running (max, sum, output).
-  constexpr int kChunk = 16;
-  for (int idx = tid; idx < group * 32; idx += 256) {
-    const int h = idx >> 5, d4 = idx & 31;
-    float M = -INFINITY, den = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < top_k; k0 += kChunk) {
-      float m[kChunk], l[kChunk];
-      f32x4 o[kChunk];
-      // no branches around the loads (a join would wait for them): slots
-      // past top_k read beyond the buffer range, which returns zeros, and
-      // are masked afterwards
-#pragma unroll
-      for (int k = 0; k < kChunk; ++k) {
-        const f32x4 v = load_shared4(rml, ((k0 + k) * group + h) * 16);
-        o[k] = load_shared4(ro, (((k0 + k) * group + h) * 128 + 4 * d4) * 4);
-        m[k] = k0 + k < top_k ? v[0] : -INFINITY;
-        l[k] = v[1];
-      }
-      // branch-free fold (selects, not products: an empty slot's partial
-      // output is stale memory)
-      float Mc = M;
-#pragma unroll
-      for (int k = 0; k < kChunk; ++k) Mc = fmaxf(Mc, m[k]);
-      const float r = M == -INFINITY ? 0.f : exp2f(M - Mc);
-      den *= r;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] *= r;
-#pragma unroll
-      for (int k = 0; k < kChunk; ++k) {
-        const bool live = m[k] != -INFINITY;
-        const float e = exp2f(live ? m[k] - Mc : -INFINITY);
-        den = live ? den + e * l[k] : den;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = live ? acc[j] + e * o[k][j] : acc[j];
-      }
-      M = Mc;
-    }
-    const float inv = 1.f / den;
-    *reinterpret_cast<f32x4*>(out + ((size_t)s * Hq + (size_t)g * group + h) * 128 + 4 * d4) =
-        f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-  }
+  merge_partials(ro, rml, top_k, group, out + ((size_t)s * Hq + (size_t)g * group) * 128);
 }
 
 // Slot workgroups beyond which TopK runs in its own launch instead of being
