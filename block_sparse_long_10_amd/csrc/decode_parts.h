@@ -22,8 +22,16 @@ constexpr float kLog2e = 1.4426950408889634f;
 // bytes; only the 16-byte buffer forms are used).
 constexpr int kCachePolicySC1 = 16;
 constexpr int kBufferDword3 = 0x00020000;  // raw 32-bit elements (gfx9 family)
+// (The base address and size are made wave-uniform so that the descriptor
+// lives in scalar registers: a descriptor in vector registers turns every
+// buffer access into a loop over lanes.)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kBufferDword3);
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* base = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           kBufferDword3);
 }
 __device__ __forceinline__ void store_shared4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kCachePolicySC1);

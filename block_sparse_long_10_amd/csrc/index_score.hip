@@ -88,18 +88,24 @@ hipError_t launch_index_score_decode(const Dims& d, const Cache& c, const uint16
 // --------------------------------------------------------------- prefill
 // Workgroup: 4 waves x 128 row slots (4 M tiles of 32) = 512 rows of one
 // (tile, group); rows are (query, index head) pairs, padding rows repeat row 0.
-// Keys: blocks [b_lo, b_hi) of the tile's eligible range, one block per step.
+// Keys: blocks [b_lo, b_hi) of the tile's eligible range, one block per step,
+// double-buffered in LDS.  Each wave streams a quarter of the next block with
+// 1 KB direct-to-LDS loads (lane l of a load fills token 8q + l/8, chunk slot
+// l%8 with source chunk (l%8) ^ (l/8): the XOR-swizzled image the MFMA B
+// operand reads without bank conflicts).  Per block, each wave folds its
+// 32x32 score tiles with v_max3 into one value per lane, reduces within DPP
+// rows, and one thread combines the 16 row maxima of the workgroup.
 template <int B>
 __global__ __launch_bounds__(256) void index_score_prefill_kernel(
     const uint16_t* __restrict__ idx_k, const int32_t* __restrict__ block_table,
     const uint16_t* __restrict__ idx_q, int32_t prior_len, int32_t chunk_len, int32_t num_kv_heads,
     int32_t num_idx_heads, int32_t max_blocks, int32_t blocks_per_split,
     float* __restrict__ pooled) {
-  constexpr int NT = B / 32;                 // 32-token N tiles per block
-  constexpr int BLOCK_BYTES = B * 128;       // B tokens x 64 bf16
-  constexpr int LOADS = BLOCK_BYTES / (16 * 256);  // 16-byte loads per thread per block
-  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][BLOCK_BYTES];
-  __shared__ float wmax[2][4];
+  constexpr int NT = B / 32;                       // 32-token N tiles per block
+  constexpr int BLOCK_BYTES = B * 128;             // B tokens x 64 bf16
+  constexpr int WLOADS = BLOCK_BYTES / 1024 / 4;   // 1 KB loads per wave per block
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][BLOCK_BYTES];
+  __shared__ float wmax[2][16];
 
   const int tile = blockIdx.x, g = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -126,63 +132,62 @@ __global__ __launch_bounds__(256) void index_score_prefill_kernel(
   }
 
   const int32_t* bt = block_table;  // one sequence
-  u32x4 pre[LOADS];
-  auto gload = [&](int b) {
+  const int src_off = (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) << 4);
+  auto issue = [&](int b, int buf) {
     const uint8_t* src = reinterpret_cast<const uint8_t*>(idx_k) + (size_t)bt[b] * BLOCK_BYTES;
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      pre[i] = *reinterpret_cast<const u32x4*>(src + (size_t)(i * 256 + tid) * 16);
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int chunk = i * 256 + tid;        // 16-byte chunk id within the block
-      const int t = chunk >> 3, c = chunk & 7;  // token, chunk within the 128-byte row
-      *reinterpret_cast<u32x4*>(&kbuf[buf][t * 128 + ((c ^ (t & 7)) << 4)]) = pre[i];
+    for (int i = 0; i < WLOADS; ++i) {
+      const int q = wave * WLOADS + i;
+      load_lds16(src + q * 1024 + src_off, &kbuf[buf][q * 1024]);
     }
   };
 
-  gload(b_lo);
-  lstore(0);
-  // every load issued so far has landed: without this wait the in-loop waits
-  // for the query operands would also wait for the next block's prefetch
+  issue(b_lo, 0);
   wait_vmem();
   __syncthreads();
   for (int b = b_lo; b < b_hi; ++b) {
     const int buf = (b - b_lo) & 1;
-    const bool more = b + 1 < b_hi;
-    if (more) gload(b + 1);
+    // buf ^ 1 was last read in the previous step, which ended with a barrier
+    if (b + 1 < b_hi) issue(b + 1, buf ^ 1);
     f32x16 run;
 #pragma unroll
     for (int v = 0; v < 16; ++v) run[v] = -INFINITY;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int t = nt * 32 + (lane & 31);
-      bf16x8 bf[4];
+    for (int np = 0; np < NT / 2; ++np) {
+      bf16x8 bf[2][4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int c = ks * 2 + half;
-        bf[ks] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(&kbuf[buf][t * 128 + ((c ^ (t & 7)) << 4)]));
+      for (int u = 0; u < 2; ++u) {
+        const int t = (2 * np + u) * 32 + (lane & 31);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int c = ks * 2 + half;
+          bf[u][ks] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(&kbuf[buf][t * 128 + ((c ^ (t & 7)) << 4)]));
+        }
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        f32x16 acc = {};
+        f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mfma32(a[mt][ks], bf[ks], acc);
+        for (int ks = 0; ks < 4; ++ks) {
+          acc0 = mfma32(a[mt][ks], bf[0][ks], acc0);
+          acc1 = mfma32(a[mt][ks], bf[1][ks], acc1);
+        }
 #pragma unroll
-        for (int v = 0; v < 16; ++v) run[v] = fmaxf(run[v], acc[v]);
+        for (int v = 0; v < 16; ++v) run[v] = fmaxf(fmaxf(run[v], acc0[v]), acc1[v]);
       }
     }
     float m = run[0];
 #pragma unroll
     for (int v = 1; v < 16; ++v) m = fmaxf(m, run[v]);
-    m = wave_max(m);
-    if (lane == 0) wmax[buf][wave] = m;
-    if (more) lstore(buf ^ 1);
+    m = row16_max(m);
+    if ((lane & 15) == 0) wmax[buf][wave * 4 + (lane >> 4)] = m;
+    wait_vmem();  // this wave's quarter of block b + 1 has landed
     __syncthreads();
     if (tid == 0) {
-      const float r = fmaxf(fmaxf(wmax[buf][0], wmax[buf][1]), fmaxf(wmax[buf][2], wmax[buf][3]));
+      float r = wmax[buf][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) r = fmaxf(r, wmax[buf][i]);
       pooled[((size_t)tile * num_kv_heads + g) * max_blocks + b] = r;
     }
   }
@@ -195,9 +200,9 @@ hipError_t launch_index_score_prefill(const Dims& d, const Cache& c, const uint1
   const int first = prior_len / B;
   const int num_tiles = (prior_len + chunk_len + B - 1) / B - first;
   const int max_own = first + num_tiles - 1;
-  // split the key range so that the grid holds several workgroups per CU
+  // split the key range so that the grid holds many workgroups per CU
   const int units = num_tiles * d.num_kv_heads;
-  int splits = (2048 + units - 1) / units;
+  int splits = (4096 + units - 1) / units;
   if (splits > max_own) splits = max_own > 0 ? max_own : 1;
   const int per = max_own > 0 ? (max_own + splits - 1) / splits : 1;
   dim3 grid(num_tiles, d.num_kv_heads, splits);
