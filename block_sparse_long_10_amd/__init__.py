@@ -20,6 +20,7 @@ __all__ = [
     "msa_decode_workspace_bytes", "msa_decode", "msa_index_score_decode",
     "msa_prefill_workspace_bytes", "msa_prefill_chunk", "msa_index_score_prefill",
     "msa_block_topk_prefill", "msa_sparse_attn_prefill", "msa_last_error", "msa_version",
+    "PagedKVMut", "make_kv_mut", "msa_cache_append", "msa_decode_append",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -49,6 +50,12 @@ class PagedKV(ctypes.Structure):
                 ("max_blocks_per_seq", ctypes.c_int32)]
 
 
+class PagedKVMut(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("idx_k", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("num_pages", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -65,6 +72,7 @@ def lib():
                               "python block_sparse_long_10_amd/build.py")
         L = ctypes.CDLL(_LIB_PATH)
         P, K = ctypes.POINTER(Params), ctypes.POINTER(PagedKV)
+        KM = ctypes.POINTER(PagedKVMut)
         vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         sigs = {
             "msa_decode_workspace_bytes": (sz, [P, i32, i32]),
@@ -75,6 +83,9 @@ def lib():
             "msa_index_score_prefill": (ctypes.c_int, [P, K, vp, i32, i32, vp, vp]),
             "msa_block_topk_prefill": (ctypes.c_int, [P, i32, i32, i32, vp, vp, vp]),
             "msa_sparse_attn_prefill": (ctypes.c_int, [P, K, vp, i32, i32, vp, vp, vp]),
+            "msa_cache_append": (ctypes.c_int, [P, KM, vp, vp, vp, vp, i32, i32, vp]),
+            "msa_decode_append": (ctypes.c_int, [P, KM, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp,
+                                                 vp, sz, vp]),
             "msa_last_error": (ctypes.c_char_p, []),
             "msa_version": (ctypes.c_char_p, []),
         }
@@ -134,6 +145,41 @@ def make_kv(k: torch.Tensor, v: torch.Tensor, idx_k: torch.Tensor,
                  int(k.shape[0]), int(block_table.shape[-1]))
     kv._keep = (k, v, idx_k, block_table)
     return kv
+
+
+def make_kv_mut(k: torch.Tensor, v: torch.Tensor, idx_k: torch.Tensor,
+                block_table: torch.Tensor) -> PagedKVMut:
+    """Writable paged cache descriptor (same layouts as make_kv), for the calls that append."""
+    kv = PagedKVMut(_dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
+                    _dev(idx_k, torch.bfloat16, "idx_k"),
+                    _dev(block_table, torch.int32, "block_table"),
+                    int(k.shape[0]), int(block_table.shape[-1]))
+    kv._keep = (k, v, idx_k, block_table)
+    return kv
+
+
+def msa_cache_append(params: Params, kv: PagedKVMut, k_new, v_new, idx_k_new, start_pos,
+                     batch: int, n_new: int, stream=None) -> None:
+    _check(lib().msa_cache_append(ctypes.byref(params), ctypes.byref(kv),
+                                  _dev(k_new, torch.bfloat16, "k_new"),
+                                  _dev(v_new, torch.bfloat16, "v_new"),
+                                  _dev(idx_k_new, torch.bfloat16, "idx_k_new"),
+                                  _dev(start_pos, torch.int32, "start_pos"), batch, n_new,
+                                  _stream(stream)))
+
+
+def msa_decode_append(params: Params, kv: PagedKVMut, k_new, v_new, idx_k_new, q, idx_q,
+                      seq_lens, batch: int, max_seq_len: int, out, sel=None, workspace=None,
+                      stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().msa_decode_append(ctypes.byref(params), ctypes.byref(kv),
+                                   _dev(k_new, torch.bfloat16, "k_new"),
+                                   _dev(v_new, torch.bfloat16, "v_new"),
+                                   _dev(idx_k_new, torch.bfloat16, "idx_k_new"),
+                                   _dev(q, torch.bfloat16, "q"), _dev(idx_q, torch.bfloat16, "idx_q"),
+                                   _dev(seq_lens, torch.int32, "seq_lens"), batch, max_seq_len,
+                                   _dev(out, torch.float32, "out"), _dev(sel, torch.int32, "sel"),
+                                   _dev(workspace, None, "workspace"), ws_bytes, _stream(stream)))
 
 
 def msa_decode_workspace_bytes(params: Params, batch: int, max_blocks_per_seq: int) -> int:

@@ -1,0 +1,85 @@
+// Cache append: the keys, values and index keys of new tokens are written
+// into their pages before the index branch scores them.  "MiniMax wird dünn",
+// section 1, Schritt 1 produces one index key per token (K_idx has a single
+// head) and section 2 keeps the real, uncompressed K/V; the page layout is
+// the one the other kernels read:
+//   k     [page][Hkv][B][D]   token-major
+//   v     [page][Hkv][D][B]   transposed within the page
+//   idx_k [page][B][d_i]
+//
+// One 256-thread workgroup per (sequence, touched block, group) writes the
+// new tokens that fall into one page: K rows and index-key rows are 16-byte
+// copies; V is staged token-major in LDS and written out along the page's
+// token axis, so consecutive lanes store consecutive tokens of one dimension.
+#include "msa_device.h"
+#include "msa_launch.h"
+
+namespace msa {
+
+constexpr int kVStride = 130;  // bf16 per LDS row (128 dims + 2: conflict-free column reads)
+
+template <int B>
+__global__ __launch_bounds__(256) void cache_append_kernel(
+    uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, uint16_t* __restrict__ ic,
+    const int32_t* __restrict__ block_table, int32_t max_blocks, int32_t num_kv_heads,
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const uint16_t* __restrict__ idx_new, const int32_t* __restrict__ start_pos, int32_t n_new) {
+  __shared__ uint32_t vt[B * kVStride / 2];
+  const int j = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int start = start_pos[s];
+  const int b = start / B + j;
+  const int t_lo = max(start, b * B), t_hi = min(start + n_new, (b + 1) * B);
+  if (t_lo >= t_hi) return;  // uniform
+  const int n = t_hi - t_lo, slot0 = t_lo - b * B, i0 = t_lo - start;
+  const size_t page = (size_t)block_table[(size_t)s * max_blocks + b];
+  const size_t tok0 = (size_t)s * n_new + i0;  // first new token of this workgroup
+
+  // K rows of group g: 16 chunks of 16 bytes per token
+  for (int x = tid; x < n * 16; x += 256) {
+    const int i = x >> 4, c = x & 15;
+    const u32x4 val =
+        *reinterpret_cast<const u32x4*>(k_new + ((tok0 + i) * num_kv_heads + g) * 128 + c * 8);
+    *reinterpret_cast<u32x4*>(kc + ((page * num_kv_heads + g) * B + slot0 + i) * 128 + c * 8) = val;
+  }
+  // index-key rows (one shared head): written once, by group 0
+  if (g == 0) {
+    for (int x = tid; x < n * 8; x += 256) {
+      const int i = x >> 3, c = x & 7;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(idx_new + (tok0 + i) * 64 + c * 8);
+      *reinterpret_cast<u32x4*>(ic + (page * B + slot0 + i) * 64 + c * 8) = val;
+    }
+  }
+  // V of group g: token-major rows into LDS, then dimension-major out
+  for (int x = tid; x < n * 64; x += 256) {
+    const int i = x >> 6, w = x & 63;  // dims 2w, 2w+1
+    vt[i * (kVStride / 2) + w] =
+        *reinterpret_cast<const uint32_t*>(v_new + ((tok0 + i) * num_kv_heads + g) * 128 + 2 * w);
+  }
+  __syncthreads();
+  const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(vt);
+  for (int x = tid; x < n * 128; x += 256) {
+    const int d = x / n, i = x - d * n;
+    vc[((page * num_kv_heads + g) * 128 + d) * B + slot0 + i] = vt16[i * kVStride + d];
+  }
+}
+
+hipError_t launch_cache_append(const Dims& d, const CacheW& c, const uint16_t* k_new,
+                               const uint16_t* v_new, const uint16_t* idx_new,
+                               const int32_t* start_pos, int32_t batch, int32_t n_new,
+                               hipStream_t stream) {
+  const int B = d.block_size;
+  // n_new tokens starting anywhere touch at most ceil(n_new/B) + 1 blocks
+  const dim3 grid((n_new + B - 1) / B + 1, d.num_kv_heads, batch);
+  if (B == 64)
+    hipLaunchKernelGGL(cache_append_kernel<64>, grid, dim3(256), 0, stream, c.k, c.v, c.idx_k,
+                       c.block_table, c.max_blocks, d.num_kv_heads, k_new, v_new, idx_new,
+                       start_pos, n_new);
+  else
+    hipLaunchKernelGGL(cache_append_kernel<128>, grid, dim3(256), 0, stream, c.k, c.v, c.idx_k,
+                       c.block_table, c.max_blocks, d.num_kv_heads, k_new, v_new, idx_new,
+                       start_pos, n_new);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -58,6 +58,26 @@ msa_status check_kv(const msa_paged_kv* kv) {
   return MSA_OK;
 }
 
+msa_status check_kv_mut(const msa_paged_kv_mut* kv) {
+  if (kv == nullptr) return fail(MSA_ERR_INVALID_ARGUMENT, "kv is NULL");
+  if (kv->k == nullptr || kv->v == nullptr || kv->idx_k == nullptr || kv->block_table == nullptr)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "kv cache pointer is NULL");
+  if (kv->num_pages < 1 || kv->max_blocks_per_seq < 1)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "num_pages and max_blocks_per_seq must be >= 1");
+  return MSA_OK;
+}
+
+msa::CacheW cache_w_of(const msa_paged_kv_mut* kv) {
+  return msa::CacheW{static_cast<uint16_t*>(kv->k), static_cast<uint16_t*>(kv->v),
+                     static_cast<uint16_t*>(kv->idx_k), kv->block_table, kv->num_pages,
+                     kv->max_blocks_per_seq};
+}
+
+msa_paged_kv read_view(const msa_paged_kv_mut* kv) {
+  return msa_paged_kv{kv->k, kv->v, kv->idx_k, kv->block_table, kv->num_pages,
+                      kv->max_blocks_per_seq};
+}
+
 msa::Dims dims_of(const msa_params* p) {
   return msa::Dims{p->num_q_heads, p->num_kv_heads, p->head_dim, p->num_idx_heads,
                    p->idx_dim,     p->block_size,   p->top_k,    p->softmax_scale};
@@ -158,10 +178,62 @@ msa_status msa_index_score_decode(const msa_params* params, const msa_paged_kv* 
                     "index score launch");
 }
 
+msa_status msa_cache_append(const msa_params* params, const msa_paged_kv_mut* kv,
+                            const void* k_new, const void* v_new, const void* idx_k_new,
+                            const int32_t* start_pos, int32_t batch, int32_t n_new, void* stream) {
+  msa_status st = check_params(params);
+  if (st != MSA_OK) return st;
+  if ((st = check_kv_mut(kv)) != MSA_OK) return st;
+  if (k_new == nullptr || v_new == nullptr || idx_k_new == nullptr || start_pos == nullptr)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "k_new, v_new, idx_k_new and start_pos must not be NULL");
+  if (batch < 1 || n_new < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "batch and n_new must be >= 1");
+  if (batch > 65535) return fail(MSA_ERR_UNSUPPORTED, "batch must be <= 65535");
+  if ((int64_t)n_new > (int64_t)kv->max_blocks_per_seq * params->block_size)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "n_new exceeds max_blocks_per_seq * block_size");
+  return hip_status(msa::launch_cache_append(dims_of(params), cache_w_of(kv),
+                                             static_cast<const uint16_t*>(k_new),
+                                             static_cast<const uint16_t*>(v_new),
+                                             static_cast<const uint16_t*>(idx_k_new), start_pos,
+                                             batch, n_new, static_cast<hipStream_t>(stream)),
+                    "cache append launch");
+}
+
+static msa_status decode_impl(const msa_params* params, const msa_paged_kv* kv, const void* q,
+                              const void* idx_q, const int32_t* seq_lens, int32_t batch,
+                              int32_t max_seq_len, float* out, int32_t* sel, void* workspace,
+                              size_t workspace_bytes, void* stream,
+                              const msa::DecodeAppend* append);
+
 msa_status msa_decode(const msa_params* params, const msa_paged_kv* kv, const void* q,
                       const void* idx_q, const int32_t* seq_lens, int32_t batch,
                       int32_t max_seq_len, float* out, int32_t* sel, void* workspace,
                       size_t workspace_bytes, void* stream) {
+  return decode_impl(params, kv, q, idx_q, seq_lens, batch, max_seq_len, out, sel, workspace,
+                     workspace_bytes, stream, nullptr);
+}
+
+msa_status msa_decode_append(const msa_params* params, const msa_paged_kv_mut* kv,
+                             const void* k_new, const void* v_new, const void* idx_k_new,
+                             const void* q, const void* idx_q, const int32_t* seq_lens,
+                             int32_t batch, int32_t max_seq_len, float* out, int32_t* sel,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  msa_status st = check_kv_mut(kv);
+  if (st != MSA_OK) return st;
+  if (k_new == nullptr || v_new == nullptr || idx_k_new == nullptr)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "k_new, v_new and idx_k_new must not be NULL");
+  const msa_paged_kv view = read_view(kv);
+  const msa::DecodeAppend ap{cache_w_of(kv), static_cast<const uint16_t*>(k_new),
+                             static_cast<const uint16_t*>(v_new),
+                             static_cast<const uint16_t*>(idx_k_new)};
+  return decode_impl(params, &view, q, idx_q, seq_lens, batch, max_seq_len, out, sel, workspace,
+                     workspace_bytes, stream, &ap);
+}
+
+static msa_status decode_impl(const msa_params* params, const msa_paged_kv* kv, const void* q,
+                              const void* idx_q, const int32_t* seq_lens, int32_t batch,
+                              int32_t max_seq_len, float* out, int32_t* sel, void* workspace,
+                              size_t workspace_bytes, void* stream,
+                              const msa::DecodeAppend* append) {
   msa_status st = check_params(params);
   if (st != MSA_OK) return st;
   if ((st = check_kv(kv)) != MSA_OK) return st;
@@ -181,7 +253,8 @@ msa_status msa_decode(const msa_params* params, const msa_paged_kv* kv, const vo
   const msa::Dims d = dims_of(params);
   const msa::Cache c = cache_of(kv);
   st = hip_status(msa::launch_index_score_decode(d, c, static_cast<const uint16_t*>(idx_q),
-                                                 seq_lens, batch, max_seq_len, pooled, counters, s),
+                                                 seq_lens, batch, max_seq_len, pooled, counters, s,
+                                                 append),
                   "index score launch");
   if (st != MSA_OK) return st;
   return hip_status(

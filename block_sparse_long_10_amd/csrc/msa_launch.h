@@ -21,11 +21,40 @@ struct Cache {
   int32_t num_pages, max_blocks;
 };
 
+// Writable view of the same cache (cache append).
+struct CacheW {
+  uint16_t* k;
+  uint16_t* v;
+  uint16_t* idx_k;
+  const int32_t* block_table;
+  int32_t num_pages, max_blocks;
+};
+
+// The current token of each sequence (position seq_lens[s]-1) written into
+// its page: k_new, v_new [batch][Hkv][D], idx_new [batch][d_i].
+struct DecodeAppend {
+  CacheW cache;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const uint16_t* idx_new;
+};
+
 // Step 1, decode: pooled[s][g][b] for b < own(s).  When counters is not
-// null, counters [batch][Hkv] are cleared for the attention launch.
+// null, counters [batch][Hkv] are cleared for the attention launch.  When
+// append is not null, the launch also writes each sequence's current token
+// into its own block (which the index branch never reads).
 hipError_t launch_index_score_decode(const Dims& d, const Cache& c, const uint16_t* idx_q,
                                      const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
-                                     float* pooled, uint32_t* counters, hipStream_t stream);
+                                     float* pooled, uint32_t* counters, hipStream_t stream,
+                                     const DecodeAppend* append = nullptr);
+
+// Cache append: n_new tokens per sequence at positions start_pos[s] ..
+// start_pos[s]+n_new-1; k_new, v_new [batch][n_new][Hkv][D],
+// idx_new [batch][n_new][d_i].
+hipError_t launch_cache_append(const Dims& d, const CacheW& c, const uint16_t* k_new,
+                               const uint16_t* v_new, const uint16_t* idx_new,
+                               const int32_t* start_pos, int32_t batch, int32_t n_new,
+                               hipStream_t stream);
 
 // TopK, Step 2 over the kept blocks (one partial per block) and the merge of
 // the partials, decode.  counters must be zero on entry.

@@ -46,7 +46,8 @@
  *   block_table int32 [batch][max_blocks_per_seq]: logical block b of
  *          sequence s lives in page block_table[s*max_blocks_per_seq + b]
  * The caller has already written the current token's (decode) or the
- * chunk's (prefill) keys, values and index keys into the cache.
+ * chunk's (prefill) keys, values and index keys into the cache, for example
+ * with msa_cache_append (msa_decode_append does it in the same pass).
  */
 #ifndef MSA_H_
 #define MSA_H_
@@ -86,6 +87,38 @@ typedef struct {
   int32_t max_blocks_per_seq;
 } msa_paged_kv;
 
+/* The same cache, writable: used by the calls that append tokens.  Layouts
+ * and meaning as in msa_paged_kv. */
+typedef struct {
+  void *k;                    /* bf16 [num_pages][Hkv][B][D]  */
+  void *v;                    /* bf16 [num_pages][Hkv][D][B]  */
+  void *idx_k;                /* bf16 [num_pages][B][d_i]     */
+  const int32_t *block_table; /* int32 [batch][max_blocks_per_seq] */
+  int32_t num_pages;
+  int32_t max_blocks_per_seq;
+} msa_paged_kv_mut;
+
+/* ------------------------------------------------------------ cache append
+ * The step before the index branch: the keys, values and index keys of new
+ * tokens are written into their pages ("MiniMax wird dünn", section 1,
+ * Schritt 1: one index key per token, a single shared index-key head;
+ * section 2: the real, uncompressed K/V stay in the cache).
+ * Sequence s receives n_new >= 1 consecutive tokens at positions
+ * start_pos[s] .. start_pos[s]+n_new-1 (token t goes to page
+ * block_table[s][t/B], slot t%B; the V slot is column t%B of the page's
+ * transposed [D][B] rows).
+ *   k_new     bf16 [batch][n_new][Hkv][D]
+ *   v_new     bf16 [batch][n_new][Hkv][D]   (token-major; transposed here)
+ *   idx_k_new bf16 [batch][n_new][d_i]
+ *   start_pos int32 [batch]  (device)
+ * Only the slots of the new tokens are written.  Pages written for one
+ * sequence must not be shared with another sequence in the same call.
+ * Positions beyond max_blocks_per_seq*B are a device-side data error. */
+msa_status msa_cache_append(const msa_params *params, const msa_paged_kv_mut *kv,
+                            const void *k_new, const void *v_new,
+                            const void *idx_k_new, const int32_t *start_pos,
+                            int32_t batch, int32_t n_new, void *stream);
+
 /* ------------------------------------------------------------------ decode
  * One decode step for a batch of sequences (Step 1 + TopK + Step 2).
  * Sequence s holds seq_lens[s] >= 1 tokens, the last being the current one;
@@ -109,6 +142,22 @@ msa_status msa_decode(const msa_params *params, const msa_paged_kv *kv,
                       int32_t batch, int32_t max_seq_len, float *out,
                       int32_t *sel, void *workspace, size_t workspace_bytes,
                       void *stream);
+
+/* msa_decode with the current token's append fused in: the launch that
+ * scores the index keys also writes each sequence's current token (position
+ * seq_lens[s]-1) into its own block, which that launch never reads, before
+ * the sparse branch reads it.  Same arguments and results as msa_decode on
+ * a cache that already holds the token, plus
+ *   k_new, v_new  bf16 [batch][Hkv][D]   (the current token's key and value)
+ *   idx_k_new     bf16 [batch][d_i]      (its index key)
+ * The cache's slots of the current tokens are written. */
+msa_status msa_decode_append(const msa_params *params, const msa_paged_kv_mut *kv,
+                             const void *k_new, const void *v_new,
+                             const void *idx_k_new, const void *q,
+                             const void *idx_q, const int32_t *seq_lens,
+                             int32_t batch, int32_t max_seq_len, float *out,
+                             int32_t *sel, void *workspace,
+                             size_t workspace_bytes, void *stream);
 
 /* Step 1 of decode alone (index scores + block max pool):
  *   pooled f32 [batch][Hkv][max_blocks_per_seq]; entries b < c are written,

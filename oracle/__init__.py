@@ -73,9 +73,10 @@ def lib():
         L.msa_oracle_attend_prefill.argtypes = [P, C, vp, i32, i32, vp, i32, vp, vp]
         L.msa_oracle_select.argtypes = [vp, i32, i32, vp]
         L.msa_oracle_block_scores.argtypes = [P, C, i32, vp, i32, i32, i32, vp, i32, vp]
+        L.msa_oracle_append.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, i32]
         for f in ("msa_oracle_decode", "msa_oracle_attend_decode", "msa_oracle_prefill",
                   "msa_oracle_attend_prefill", "msa_oracle_select", "msa_oracle_max_threads",
-                  "msa_oracle_block_scores"):
+                  "msa_oracle_block_scores", "msa_oracle_append"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -254,3 +255,29 @@ def block_scores(case, group: int, blocks: Sequence[int], seq: int = 0, tile: Op
     if rc != 0:
         raise ValueError("oracle block_scores rejected its arguments")
     return out
+
+
+def cache_append(shape, k: np.ndarray, v: np.ndarray, idx_k: np.ndarray, block_table,
+                 k_new, v_new, idx_new, start_pos) -> None:
+    """Oracle cache append, in place on host arrays of bfloat16 bits (int16).
+
+    k [P][Hkv][B][D], v [P][Hkv][D][B], idx_k [P][B][d_i]; k_new, v_new
+    [batch][n_new][Hkv][D] and idx_new [batch][n_new][d_i] (tensors or
+    arrays); start_pos [batch]: position of each sequence's first new token.
+    """
+    params = _Params(shape.num_q_heads, shape.num_kv_heads, shape.head_dim, shape.num_idx_heads,
+                     shape.idx_dim, shape.block_size, shape.top_k, shape.softmax_scale)
+    for a in (k, v, idx_k):
+        assert a.dtype == np.int16 and a.flags["C_CONTIGUOUS"]
+    bt = _host_i32(block_table)
+    kn = k_new if isinstance(k_new, np.ndarray) else _host_u16(k_new)
+    vn = v_new if isinstance(v_new, np.ndarray) else _host_u16(v_new)
+    xn = idx_new if isinstance(idx_new, np.ndarray) else _host_u16(idx_new)
+    kn, vn, xn = (np.ascontiguousarray(a) for a in (kn, vn, xn))
+    st = _host_i32(start_pos)
+    batch, n_new = int(kn.shape[0]), int(kn.shape[1])
+    rc = lib().msa_oracle_append(ctypes.byref(params), _ptr(k), _ptr(v), _ptr(idx_k), _ptr(bt),
+                                 int(bt.shape[-1]), _ptr(kn), _ptr(vn), _ptr(xn), _ptr(st),
+                                 batch, n_new)
+    if rc != 0:
+        raise ValueError("oracle append rejected its arguments")

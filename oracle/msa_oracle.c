@@ -410,3 +410,37 @@ int msa_oracle_block_scores(const oracle_params *p, const oracle_cache *c, int32
     out[i] = block_score(p, c, seq, idx_q, q0, q1, g, blocks[i]);
   return 0;
 }
+
+/*
+ * Cache append: the step before Step 1.  Every token brings its key and value
+ * per KV head and its one index key (the index-key side has a single head,
+ * section 1 "Schritt 1"; the real K/V are kept, section 2).  Token i of
+ * sequence s sits at position t = start[s] + i and is stored in page
+ * block_table[s][t / B], slot t % B, in the layouts above:
+ *   k_new, v_new [batch][n_new][Hkv][D], idx_new [batch][n_new][d_i].
+ * The cache arrays are written in place; nothing else changes.
+ */
+int msa_oracle_append(const oracle_params *p, uint16_t *k, uint16_t *v, uint16_t *idx_k,
+                      const int32_t *block_table, int32_t max_blocks, const uint16_t *k_new,
+                      const uint16_t *v_new, const uint16_t *idx_new, const int32_t *start,
+                      int32_t batch, int32_t n_new) {
+  const int32_t B = p->block_size, D = p->head_dim, H = p->num_kv_heads, di = p->idx_dim;
+  if (batch < 1 || n_new < 1 || B < 1) return -1;
+  for (int32_t s = 0; s < batch; ++s) {
+    for (int32_t i = 0; i < n_new; ++i) {
+      const int64_t t = (int64_t)start[s] + i;
+      if (t < 0 || t >= (int64_t)max_blocks * B) return -1;
+      const int64_t pg = block_table[(int64_t)s * max_blocks + t / B];
+      const int64_t slot = t % B;
+      const int64_t src = (int64_t)s * n_new + i;
+      for (int32_t g = 0; g < H; ++g) {
+        for (int32_t d = 0; d < D; ++d) {
+          k[((pg * H + g) * B + slot) * D + d] = k_new[(src * H + g) * D + d];
+          v[((pg * H + g) * D + d) * B + slot] = v_new[(src * H + g) * D + d];
+        }
+      }
+      for (int32_t d = 0; d < di; ++d) idx_k[(pg * B + slot) * di + d] = idx_new[src * di + d];
+    }
+  }
+  return 0;
+}

@@ -7,13 +7,17 @@ import subprocess
 import numpy as np
 import pytest
 
+import torch
+
 import oracle
-from msa_inputs import make_decode_case, make_prefill_case
+from msa_inputs import Shape, build_paged_cache, make_decode_case, make_prefill_case
+from tests.append_util import holed_copy, new_token_batch
 from tests import bruteforce
 from tests.test_oracle_pins import TINY, TINY1, _by_sort
 from tests.test_oracle_pins import test_handworked_golden as _golden
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "msa_oracle.c")
+APPEND_SHAPE = Shape(num_q_heads=4, num_kv_heads=2, num_idx_heads=2, block_size=64, top_k=4)
 
 # (name, text in msa_oracle.c, replacement, replace every occurrence)
 MUTANTS = [
@@ -37,6 +41,13 @@ MUTANTS = [
     ("softmax not normalised", "out[d] = acc / den;", "out[d] = acc;", False),
     ("index key dims swapped with query", "dot += qry[row * di + d] * key[r * di + d];",
      "dot += qry[row * di + d] * key[d * B + r];", False),
+    ("append writes V untransposed", "v[((pg * H + g) * D + d) * B + slot] = v_new",
+     "v[((pg * H + g) * B + slot) * D + d] = v_new", False),
+    ("append slot off by one", "const int64_t slot = t % B;", "const int64_t slot = (t + 1) % B;",
+     False),
+    ("append ignores the block table",
+     "const int64_t pg = block_table[(int64_t)s * max_blocks + t / B];",
+     "const int64_t pg = t / B;", False),
 ]
 
 
@@ -67,9 +78,24 @@ def _pins_pass() -> bool:
             sc = rng.integers(-3, 4, size=max(own, 1)).astype(np.float64)
             assert oracle.select(sc[:own], own, k).tolist() == _by_sort(sc, own, k)
         _golden()
+        _append_pin()
     except AssertionError:
         return False
     return True
+
+
+def _append_pin():
+    """Append into punched-out slots must restore the generated cache."""
+    shape = APPEND_SHAPE
+    lengths = [300, 200]
+    full = build_paged_cache(shape, lengths, seed=17, shuffle_pages=True, poison_frac=0.1)
+    starts = [L - 70 - 9 for L in lengths]
+    kn, vn, xn = new_token_batch(full, shape, starts, 70)
+    hole = holed_copy(full, shape, starts, 70)
+    arrays = [np.ascontiguousarray(t.view(torch.int16).numpy()) for t in (hole.k, hole.v, hole.idx_k)]
+    oracle.cache_append(shape, *arrays, full.block_table, kn, vn, xn, starts)
+    for a, t in zip(arrays, (full.k, full.v, full.idx_k)):
+        np.testing.assert_array_equal(a, t.view(torch.int16).numpy())
 
 
 def test_unmutated_copy_passes(tmp_path):
