@@ -144,10 +144,22 @@ def run_decode_bench(args, torch, msa, mi, gu):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n  # ms
 
+    # decode with the current token's append fused in: each set's own current
+    # token is written into its slot again at every step
+    kvm = [msa.make_kv_mut(c.cache.k, c.cache.v, c.cache.idx_k, c.cache.block_table) for c in sets]
+    cur = [current_token_rows(torch, c) for c in sets]
+
+    def append_step(i):
+        c, (kn, vn, xn) = sets[i % len(sets)], cur[i % len(sets)]
+        msa.msa_decode_append(p, kvm[i % len(sets)], kn, vn, xn, c.q, c.idx_q, c.seq_lens, batch,
+                              maxL, out, sel, ws)
+
     log("[bench] decode: %d warmup + %d timed steps" % (args.warmup, args.steps))
     ms_step = timed(step, args.steps, args.warmup)
     log("[bench] decode index kernel alone")
     ms_index = timed(index_only, args.steps, args.warmup)
+    log("[bench] decode with the fused append")
+    ms_append_step = timed(append_step, args.steps, args.warmup)
     idx_bytes, kv_bytes, small = decode_algorithmic_bytes(base)
     own = (maxL - 1) // sh.block_size
     index_bytes = idx_bytes + base.idx_q.numel() * 2 + base.cache.block_table.numel() * 4 \
@@ -156,7 +168,87 @@ def run_decode_bench(args, torch, msa, mi, gu):
     return {
         "ms_step": ms_step, "ms_index": ms_index, "index_bytes": index_bytes,
         "step_bytes": step_bytes, "case": base, "sets": sets, "p": p, "kvs": kvs,
+        "ms_append_step": ms_append_step,
     }
+
+
+def current_token_rows(torch, case):
+    """k, v [batch][Hkv][D] and idx_k [batch][d_i] of each sequence's current
+    token, read out of its page (the rows a decode-with-append call writes)."""
+    sh, c = case.shape, case.cache
+    B = sh.block_size
+    pos = torch.tensor([L - 1 for L in case.lengths], dtype=torch.long, device=c.k.device)
+    rows = torch.arange(case.batch, device=c.k.device)
+    pages = c.block_table.long()[rows, pos // B]
+    slots = pos % B
+    return (c.k[pages, :, slots, :].contiguous(), c.v[pages, :, :, slots].contiguous(),
+            c.idx_k[pages, slots, :].contiguous())
+
+
+def run_layers_bench(args, torch, msa, mi, dec):
+    """Decode of one token through args.layers MSA layers at the 1M context:
+    every layer has its own index keys (so no layer's 128 MiB of index keys is
+    served from the Infinity Cache), queries and index queries; the K/V pages
+    are shared (each layer reads only its kept blocks, 8 MiB).  The layers run
+    eagerly (one msa_decode per layer, back to back) and as one captured HIP
+    graph replayed per token; both are reported per layer and per token."""
+    base = dec["case"]
+    sh = base.shape
+    p = dec["p"]
+    n = args.layers
+    log("[bench] %d-layer decode: generating per-layer index keys" % n)
+    c = base.cache
+    layers = []
+    for l in range(n):
+        seed = 1000 + l
+        ik = mi.normal_bf16(tuple(c.idx_k.shape), seed, mi.TENSOR_IDS["idx_k"], "cuda")
+        q = mi.normal_bf16(tuple(base.q.shape), seed, mi.TENSOR_IDS["q"], "cuda")
+        iq = mi.normal_bf16(tuple(base.idx_q.shape), seed, mi.TENSOR_IDS["idx_q"], "cuda")
+        layers.append((msa.make_kv(c.k, c.v, ik, c.block_table), q, iq))
+    batch, maxL, mb = base.batch, max(base.lengths), c.max_blocks
+    outs = torch.empty(n, batch, sh.num_q_heads, sh.head_dim, device="cuda")
+    ws = torch.empty(msa.msa_decode_workspace_bytes(p, batch, mb), dtype=torch.uint8,
+                     device="cuda")
+
+    def token():
+        for l, (kv, q, iq) in enumerate(layers):
+            msa.msa_decode(p, kv, q, iq, base.seq_lens, batch, maxL, outs[l], None, ws)
+
+    def timed(fn, reps, warm):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    reps = max(1, args.layer_tokens)
+    ms_eager = timed(token, reps, 2)
+    eager_out = outs.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        token()  # warm the stream before capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            token()
+    torch.cuda.current_stream().wait_stream(s)
+    outs.zero_()
+    ms_graph = timed(g.replay, reps, 2)
+    same = bool(torch.equal(outs, eager_out))
+    log("[bench] %d layers: eager %.1f us/layer, graph %.1f us/layer, replay == eager: %s"
+        % (n, ms_eager * 1e3 / n, ms_graph * 1e3 / n, same))
+    return {"layers": n, "tokens_timed": reps, "eager_us_per_token": round(ms_eager * 1e3, 2),
+            "graph_us_per_token": round(ms_graph * 1e3, 2),
+            "eager_us_per_layer": round(ms_eager * 1e3 / n, 3),
+            "graph_us_per_layer": round(ms_graph * 1e3 / n, 3),
+            "graph_replay_equals_eager": same,
+            "note": "per-layer index keys, queries and index queries; K/V pages shared"}
 
 
 def run_prefill_bench(args, torch, msa, mi, gu):
@@ -190,6 +282,18 @@ def run_prefill_bench(args, torch, msa, mi, gu):
     ms_index = timed(lambda: msa.msa_index_score_prefill(p, kv, case.idx_q, P, C, pooled), n, w)
     ms_topk = timed(lambda: msa.msa_block_topk_prefill(p, P, C, mb, pooled, sel), n, w)
     ms_attn = timed(lambda: msa.msa_sparse_attn_prefill(p, kv, case.q, P, C, sel, out), n, w)
+    # cache append of the chunk (its tokens are rewritten into their own slots)
+    B = sh.block_size
+    pos = torch.arange(P, P + C, device="cuda")
+    pages = case.cache.block_table[0].long()[pos // B]
+    slots = pos % B
+    k_new = case.cache.k[pages, :, slots, :].contiguous().unsqueeze(0)
+    v_new = case.cache.v[pages, :, :, slots].contiguous().unsqueeze(0)
+    x_new = case.cache.idx_k[pages, slots, :].contiguous().unsqueeze(0)
+    start = torch.tensor([P], dtype=torch.int32, device="cuda")
+    kvm = msa.make_kv_mut(case.cache.k, case.cache.v, case.cache.idx_k, case.cache.block_table)
+    ms_append = timed(lambda: msa.msa_cache_append(p, kvm, k_new, v_new, x_new, start, 1, C), n, w)
+    append_bytes = 2 * C * (2 * sh.num_kv_heads * sh.head_dim * 2 + sh.idx_dim * 2)
     # algorithmic flops: every (query, eligible key) pair x all index rows x d_i
     # multiply-adds; attention over the kept tokens visible to each query
     B, rows = sh.block_size, sh.num_kv_heads * sh.num_idx_heads
@@ -205,7 +309,8 @@ def run_prefill_bench(args, torch, msa, mi, gu):
     index_flops = pairs * rows * sh.idx_dim * 2
     attn_flops = attn_pairs * sh.num_q_heads * sh.head_dim * 4
     return {"case": case, "ms_chunk": ms_chunk, "ms_index": ms_index, "ms_topk": ms_topk,
-            "ms_attn": ms_attn, "index_flops": index_flops, "attn_flops": attn_flops}
+            "ms_attn": ms_attn, "index_flops": index_flops, "attn_flops": attn_flops,
+            "ms_append": ms_append, "append_bytes": append_bytes}
 
 
 def cpu_baseline(case, budget_s):
@@ -329,6 +434,10 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--prefill-warmup", type=int, default=2)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--layers", type=int, default=60,
+                    help="layers of the multi-layer decode leg (0 = skip)")
+    ap.add_argument("--layer-tokens", type=int, default=20,
+                    help="tokens timed in the multi-layer decode leg")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
     ap.add_argument("--summarize-kernel-trace", nargs=3, metavar=("STATS_CSV", "OUT_TXT", "CMD"),
@@ -364,6 +473,7 @@ def main():
         return
 
     dec = run_decode_bench(args, torch, msa, mi, gu)
+    lay = run_layers_bench(args, torch, msa, mi, dec) if args.layers > 0 else None
     pre = None if args.no_prefill else run_prefill_bench(args, torch, msa, mi, gu)
 
     case = dec["case"]
@@ -392,6 +502,7 @@ def main():
                    "rotated_buffer_sets": args.rotate},
         "decode_step_gbps": round(step_gbps, 1),
         "decode_step_bytes": dec["step_bytes"],
+        "decode_append_us_per_step": round(dec["ms_append_step"] * 1e3, 3),
         "roofline": {
             "kernel": "index_score_decode",
             "bound": "hbm",
@@ -422,7 +533,11 @@ def main():
                                     / BF16_PEAK_TFLOPS, 4),
             "index_flops": pre["index_flops"], "attn_flops": pre["attn_flops"],
             "peak_tflops": BF16_PEAK_TFLOPS,
+            "chunk_append_us": round(pre["ms_append"] * 1e3, 2),
+            "chunk_append_gbps": round(pre["append_bytes"] / (pre["ms_append"] * 1e-3) / 1e9, 1),
         }
+    if lay is not None:
+        result["multi_layer_decode"] = lay
     if args.cpu_budget > 0:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     else:

@@ -25,8 +25,9 @@ namespace msa {
 // ---------------------------------------------------------------- decode
 // One wave per workgroup and one block per wave (index_block_scores); small
 // single-wave workgroups let ten blocks per CU be in flight.  With an append
-// (ap.k_new != nullptr) the workgroup of each sequence's own block instead
-// writes the current token's key, value and index key into that page.
+// (ap.k_new != nullptr) one extra workgroup per sequence writes the current
+// token's key, value and index key into its own block's page, which the
+// index branch never reads.
 template <int B>
 __device__ __forceinline__ void append_current_token(const DecodeAppend& ap, int s, int L,
                                                      int num_kv_heads) {
@@ -55,15 +56,24 @@ __global__ __launch_bounds__(64) void index_score_decode_kernel(
     int32_t num_kv_heads, float* __restrict__ pooled, uint32_t* __restrict__ counters,
     DecodeAppend ap) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[B * 128];
-  const int s = blockIdx.y, b = blockIdx.x;
+  const int s = blockIdx.y;
   const int lane = threadIdx.x;
-  if (counters != nullptr && b == 0 && lane < num_kv_heads) counters[s * num_kv_heads + lane] = 0u;
+  if (counters != nullptr && blockIdx.x == 0 && lane < num_kv_heads)
+    counters[s * num_kv_heads + lane] = 0u;
   const int L = seq_lens[s];
-  const int own = (L - 1) / B;
-  if (b >= own) {
-    if (b == own && ap.k_new != nullptr) append_current_token<B>(ap, s, L, num_kv_heads);
-    return;
+  // with an append, workgroup 0 (dispatched first, so its latency hides
+  // behind the scoring) writes the current token and block b is scored by
+  // workgroup b + 1
+  int b = blockIdx.x;
+  if (ap.k_new != nullptr) {
+    if (b == 0) {
+      append_current_token<B>(ap, s, L, num_kv_heads);
+      return;
+    }
+    --b;
   }
+  const int own = (L - 1) / B;
+  if (b >= own) return;
   float* out = pooled + (size_t)s * num_kv_heads * max_blocks + b;
   index_block_scores<B, NI, MT>(idx_k, block_table[(size_t)s * max_blocks + b],
                                 idx_q + (size_t)s * num_kv_heads * NI * 64, num_kv_heads, stage,
@@ -104,8 +114,8 @@ hipError_t launch_index_score_decode(const Dims& d, const Cache& c, const uint16
                                      const DecodeAppend* append) {
   const int B = d.block_size;
   const int max_own = (max_seq_len - 1) / B;
-  // blocks 0 .. max_own-1 are scored; with an append, block max_own too
-  // (the own block of the longest sequence) gets a workgroup
+  // blocks 0 .. max_own-1 are scored; with an append, one more workgroup
+  // per sequence writes the current token
   const int gx = append != nullptr ? max_own + 1 : (max_own > 0 ? max_own : 1);
   DecodeAppend ap{};
   if (append != nullptr) ap = *append;
