@@ -59,6 +59,8 @@ class Shape:
     block_size: int = 128
     top_k: int = 16
     scale: Optional[float] = None  # softmax scale; None means 1/sqrt(head_dim)
+    sink_blocks: int = 0           # blocks always kept from the start of the sequence
+    local_blocks: int = 0          # blocks always kept just before the own block
 
     @property
     def group_size(self) -> int:

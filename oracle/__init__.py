@@ -36,7 +36,8 @@ class _Params(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("num_idx_heads", ctypes.c_int32),
                 ("idx_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
-                ("top_k", ctypes.c_int32), ("softmax_scale", ctypes.c_double)]
+                ("top_k", ctypes.c_int32), ("softmax_scale", ctypes.c_double),
+                ("sink_blocks", ctypes.c_int32), ("local_blocks", ctypes.c_int32)]
 
 
 class _Cache(ctypes.Structure):
@@ -72,11 +73,12 @@ def lib():
         L.msa_oracle_prefill.argtypes = [P, C, vp, vp, i32, i32, vp, i32, vp, vp, vp]
         L.msa_oracle_attend_prefill.argtypes = [P, C, vp, i32, i32, vp, i32, vp, vp]
         L.msa_oracle_select.argtypes = [vp, i32, i32, vp]
+        L.msa_oracle_select_forced.argtypes = [vp, i32, i32, i32, i32, vp]
         L.msa_oracle_block_scores.argtypes = [P, C, i32, vp, i32, i32, i32, vp, i32, vp]
         L.msa_oracle_append.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, i32]
         for f in ("msa_oracle_decode", "msa_oracle_attend_decode", "msa_oracle_prefill",
                   "msa_oracle_attend_prefill", "msa_oracle_select", "msa_oracle_max_threads",
-                  "msa_oracle_block_scores", "msa_oracle_append"):
+                  "msa_oracle_block_scores", "msa_oracle_append", "msa_oracle_select_forced"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -111,7 +113,8 @@ class _Prepared:
     def __init__(self, case, kv_pages=None):
         sh, cache = case.shape, case.cache
         self.params = _Params(sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.num_idx_heads,
-                              sh.idx_dim, sh.block_size, sh.top_k, sh.softmax_scale)
+                              sh.idx_dim, sh.block_size, sh.top_k, sh.softmax_scale,
+                              sh.sink_blocks, sh.local_blocks)
         if kv_pages is None:
             self.k = _host_u16(cache.k)
             self.v = _host_u16(cache.v)
@@ -223,11 +226,17 @@ def attend_prefill(case, sel, tiles: Optional[Sequence[int]] = None,
     return out
 
 
-def select(scores: np.ndarray, own: int, k: int) -> np.ndarray:
-    """The TopK rule alone: scores of blocks 0..own-1 -> sorted selection."""
+def select(scores: np.ndarray, own: int, k: int, sink_blocks: int = 0,
+           local_blocks: int = 0) -> np.ndarray:
+    """The TopK rule alone: scores of blocks 0..own-1 -> sorted selection
+    (with forced sink / local blocks when given)."""
     sc = np.ascontiguousarray(np.asarray(scores, dtype=np.float64))
     sel = np.zeros(k, dtype=np.int32)
-    rc = lib().msa_oracle_select(_ptr(sc) if own > 0 else None, own, k, _ptr(sel))
+    if sink_blocks == 0 and local_blocks == 0:
+        rc = lib().msa_oracle_select(_ptr(sc) if own > 0 else None, own, k, _ptr(sel))
+    else:
+        rc = lib().msa_oracle_select_forced(_ptr(sc) if own > 0 else None, own, k, sink_blocks,
+                                            local_blocks, _ptr(sel))
     if rc != 0:
         raise ValueError("oracle select rejected its arguments")
     return sel

@@ -27,7 +27,12 @@
  *     scored; only blocks strictly before it are eligible (causal limit);
  *   - blocks are ranked by (score descending, block index ascending);
  *   - query head j belongs to group j / (Hq / Hkv);
- *   - the index lists are returned sorted ascending, padded with -1.
+ *   - the index lists are returned sorted ascending, padded with -1;
+ *   - optional forced blocks (section 2: the dropped sliding-window branch is
+ *     probably replaced by an attention sink or local attention): the first
+ *     sink_blocks blocks and the local_blocks blocks just before the own
+ *     block are always kept and not ranked; they count toward k, so TopK
+ *     chooses k-1-(number forced) of the remaining eligible blocks.
  *
  * Arithmetic: every bfloat16 input is widened exactly to double; products,
  * sums, exp and the softmax are double.  OpenMP runs independent units
@@ -51,6 +56,7 @@ typedef struct {
   int32_t num_idx_heads, idx_dim;
   int32_t block_size, top_k;
   double softmax_scale;
+  int32_t sink_blocks, local_blocks;  /* forced blocks (0, 0: none) */
 } oracle_params;
 
 typedef struct {
@@ -125,16 +131,28 @@ static double block_score(const oracle_params *p, const oracle_cache *c,
 }
 
 /*
- * TopK: keep k' = min(k-1, own) of the eligible blocks 0..own-1, ranked by
- * (score descending, index ascending), plus the own block; sorted ascending,
+ * TopK: the forced blocks among 0..own-1 (the first n_sink and the last
+ * n_local before the own block) are kept unranked; of the other blocks before
+ * the own block, keep k' = min(k-1-forced, how many there are), ranked by
+ * (score descending, index ascending); plus the own block; sorted ascending,
  * padded with -1 up to k entries.  Chosen by repeated arg-max, the plainest
- * statement of "keep the k highest-scored".
+ * statement of "keep the k highest-scored".  Without forced blocks
+ * k' = min(k-1, own).
  */
-static void select_blocks(const double *score, int32_t own, int32_t k,
-                          int32_t *sel) {
-  int32_t kk = (k - 1 < own) ? k - 1 : own;
+static void select_blocks(const double *score, int32_t own, int32_t k, int32_t n_sink,
+                          int32_t n_local, int32_t *sel) {
   char *taken = (char *)calloc((size_t)(own > 0 ? own : 1), 1);
-  int32_t n = 0;
+  int32_t n = 0, eligible = 0;
+  for (int32_t b = 0; b < own; b++) {
+    if (b < n_sink || b >= own - n_local) {
+      taken[b] = 1;  /* forced: kept, never ranked */
+      sel[n++] = b;
+    } else {
+      eligible++;
+    }
+  }
+  int32_t kk = k - 1 - n;
+  if (kk > eligible) kk = eligible;
   for (int32_t r = 0; r < kk; r++) {
     int32_t best = -1;
     for (int32_t b = 0; b < own; b++) {
@@ -203,6 +221,8 @@ static int check(const oracle_params *p, const oracle_cache *c) {
   if (p->block_size < 1 || p->top_k < 1 || p->head_dim < 1 || p->idx_dim < 1 ||
       p->num_idx_heads < 1)
     return -1;
+  if (p->sink_blocks < 0 || p->local_blocks < 0 || p->sink_blocks + p->local_blocks > p->top_k - 1)
+    return -1;
   return 0;
 }
 
@@ -211,7 +231,16 @@ int msa_oracle_max_threads(void) { return omp_get_max_threads(); }
 /* Exported for the tests: the TopK rule on a given score vector. */
 int msa_oracle_select(const double *score, int32_t own, int32_t k, int32_t *sel) {
   if (!sel || k < 1 || own < 0 || (own > 0 && !score)) return -1;
-  select_blocks(score, own, k, sel);
+  select_blocks(score, own, k, 0, 0, sel);
+  return 0;
+}
+
+/* The same with forced sink and local blocks. */
+int msa_oracle_select_forced(const double *score, int32_t own, int32_t k, int32_t n_sink,
+                             int32_t n_local, int32_t *sel) {
+  if (!sel || k < 1 || own < 0 || (own > 0 && !score)) return -1;
+  if (n_sink < 0 || n_local < 0 || n_sink + n_local > k - 1) return -1;
+  select_blocks(score, own, k, n_sink, n_local, sel);
   return 0;
 }
 
@@ -252,7 +281,7 @@ int msa_oracle_decode(const oracle_params *p, const oracle_cache *c,
   for (int32_t s = 0; s < batch; s++)
     for (int32_t g = 0; g < H; g++)
       select_blocks(score + ((int64_t)s * H + g) * MB, (seq_lens[s] - 1) / B, k,
-                    sel + ((int64_t)s * H + g) * k);
+                    p->sink_blocks, p->local_blocks, sel + ((int64_t)s * H + g) * k);
 
   /* Step 2 per query head. */
 #pragma omp parallel for collapse(2) schedule(dynamic, 1)
@@ -333,8 +362,8 @@ static int prefill_impl(const oracle_params *p, const oracle_cache *c,
         }
     for (int32_t u = 0; u < nt; u++)
       for (int32_t g = 0; g < H; g++) {
-        select_blocks(score + ((int64_t)u * H + g) * MB, first + list[u], k,
-                      sel + ((int64_t)list[u] * H + g) * k);
+        select_blocks(score + ((int64_t)u * H + g) * MB, first + list[u], k, p->sink_blocks,
+                      p->local_blocks, sel + ((int64_t)list[u] * H + g) * k);
         if (pooled)
           memcpy(pooled + ((int64_t)list[u] * H + g) * MB, score + ((int64_t)u * H + g) * MB,
                  sizeof(double) * (size_t)MB);

@@ -31,9 +31,14 @@ def logical(case, s: int, length: int):
     return K, V, IK
 
 
-def topk_sorted(scores: np.ndarray, own: int, k: int) -> np.ndarray:
-    order = sorted(range(own), key=lambda b: (-scores[b], b))
-    keep = sorted(order[:min(k - 1, own)] + [own])
+def topk_sorted(scores: np.ndarray, own: int, k: int, sink: int = 0, local: int = 0) -> np.ndarray:
+    """Forced blocks (the first `sink`, the last `local` before own) plus the best
+    of the rest by a full sort, plus own; the forced ones count toward k."""
+    forced = [b for b in range(own) if b < sink or b >= own - local]
+    rest = [b for b in range(own) if b not in forced]
+    order = sorted(rest, key=lambda b: (-scores[b], b))
+    n = max(0, min(k - 1 - len(forced), len(rest)))
+    keep = sorted(forced + order[:n] + [own])
     return np.array(keep + [-1] * (k - len(keep)), dtype=np.int32)
 
 
@@ -66,7 +71,8 @@ def decode(case):
         qi = f64(case.idx_q[s])                          # [Hkv][n_i][d_i]
         sc = qi @ IK.T                                   # [Hkv][n_i][L]
         pooled = [pool_blocks(sc[g], own, B) for g in range(H)]
-        sel = np.stack([topk_sorted(pooled[g], own, k) for g in range(H)])
+        sel = np.stack([topk_sorted(pooled[g], own, k, sh.sink_blocks, sh.local_blocks)
+                        for g in range(H)])
         q = f64(case.q[s])
         out = np.stack([softmax_attend(q[j], K[j // G][tokens_of(sel[j // G], B, L - 1)],
                                        V[j // G][tokens_of(sel[j // G], B, L - 1)],
@@ -95,7 +101,7 @@ def prefill(case):
         for g in range(H):
             rows = qi[q0:q1, g].reshape(-1, sh.idx_dim)  # tile queries x heads
             pooled = pool_blocks(rows @ IK.T, own, B)
-            sel_t.append(topk_sorted(pooled, own, k))
+            sel_t.append(topk_sorted(pooled, own, k, sh.sink_blocks, sh.local_blocks))
             pool_t.append(pooled)
         sel_t = np.stack(sel_t)
         for i in range(q0, q1):

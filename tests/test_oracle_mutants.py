@@ -12,6 +12,7 @@ import torch
 import oracle
 from msa_inputs import Shape, build_paged_cache, make_decode_case, make_prefill_case
 from tests.append_util import holed_copy, new_token_batch
+from tests.test_oracle_forced import FORCED
 from tests import bruteforce
 from tests.test_oracle_pins import TINY, TINY1, _by_sort
 from tests.test_oracle_pins import test_handworked_golden as _golden
@@ -29,8 +30,7 @@ MUTANTS = [
      "return bf(c->v[((pg * H + g) * B + t % B) * D + d]);", False),
     ("softmax scale dropped", "z[i] = p->softmax_scale * dot;", "z[i] = dot;", False),
     ("heads mapped to groups round-robin", "int32_t g = j / G;", "int32_t g = j % H;", True),
-    ("one block too few", "int32_t kk = (k - 1 < own) ? k - 1 : own;",
-     "int32_t kk = (k - 2 < own) ? k - 2 : own;", False),
+    ("one block too few", "int32_t kk = k - 1 - n;", "int32_t kk = k - 2 - n;", False),
     ("current token excluded", "if (hi > last_pos + 1) hi = last_pos + 1;",
      "if (hi > last_pos) hi = last_pos;", True),
     ("block table ignored for index keys",
@@ -45,6 +45,10 @@ MUTANTS = [
      "v[((pg * H + g) * B + slot) * D + d] = v_new", False),
     ("append slot off by one", "const int64_t slot = t % B;", "const int64_t slot = (t + 1) % B;",
      False),
+    ("local window one block short", "if (b < n_sink || b >= own - n_local) {",
+     "if (b < n_sink || b > own - n_local) {", False),
+    ("sink blocks ignored", "if (b < n_sink || b >= own - n_local) {",
+     "if (b < 0 || b >= own - n_local) {", False),
     ("append ignores the block table",
      "const int64_t pg = block_table[(int64_t)s * max_blocks + t / B];",
      "const int64_t pg = t / B;", False),
@@ -79,6 +83,8 @@ def _pins_pass() -> bool:
             assert oracle.select(sc[:own], own, k).tolist() == _by_sort(sc, own, k)
         _golden()
         _append_pin()
+        case = make_decode_case(FORCED, [37, 9, 1, 64], 81, shuffle_pages=True, poison_frac=0.2)
+        np.testing.assert_array_equal(oracle.decode(case)["sel"], bruteforce.decode(case)["sel"])
     except AssertionError:
         return False
     return True
