@@ -41,7 +41,8 @@ class Params(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("num_idx_heads", ctypes.c_int32),
                 ("idx_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
-                ("top_k", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+                ("top_k", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("sink_blocks", ctypes.c_int32), ("local_blocks", ctypes.c_int32)]
 
 
 class PagedKV(ctypes.Structure):
@@ -129,11 +130,12 @@ def _stream(stream) -> ctypes.c_void_p:
 
 def make_params(num_q_heads: int, num_kv_heads: int, head_dim: int = 128, num_idx_heads: int = 4,
                 idx_dim: int = 64, block_size: int = 128, top_k: int = 16,
-                softmax_scale: Optional[float] = None) -> Params:
+                softmax_scale: Optional[float] = None, sink_blocks: int = 0,
+                local_blocks: int = 0) -> Params:
     if softmax_scale is None:
         softmax_scale = head_dim ** -0.5
     return Params(num_q_heads, num_kv_heads, head_dim, num_idx_heads, idx_dim, block_size, top_k,
-                  float(softmax_scale))
+                  float(softmax_scale), sink_blocks, local_blocks)
 
 
 def make_kv(k: torch.Tensor, v: torch.Tensor, idx_k: torch.Tensor,

@@ -537,4 +537,34 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ scores, int
   }
 }
 
+// TopK with forced blocks: blocks [0, n_sink) and the n_local blocks just
+// before the own block are kept unranked and count toward k; the other
+// eligible blocks form the contiguous range [lo, hi), ranked by block_topk as
+// if hi were the own block with a budget of k - (number forced).  tmp is an
+// LDS array of kMaxTopK entries.  Result as block_topk's (ascending, own
+// block included, -1 padded).
+__device__ __forceinline__ void block_topk_forced(const float* __restrict__ scores, int own, int k,
+                                                  int n_sink, int n_local, int* out_sel,
+                                                  int* tmp, TopkShared& sh) {
+  if (n_sink == 0 && n_local == 0) {
+    block_topk(scores, own, k, out_sel, sh);
+    return;
+  }
+  const int lo = min(n_sink, own);
+  const int hi = max(own - n_local, lo);
+  const int forced = lo + (own - hi);
+  const int kr = k - forced;                 // >= 1: the host checks sink + local <= k - 1
+  block_topk(scores + lo, hi - lo, kr, tmp, sh);
+  const int chosen = min(kr - 1, hi - lo);  // tmp[0 .. chosen) are relative block ids
+  for (int i = threadIdx.x; i < k; i += kTopkThreads) {
+    int b;
+    if (i < lo) b = i;
+    else if (i < lo + chosen) b = lo + tmp[i - lo];
+    else if (i <= lo + chosen + (own - hi)) b = hi + (i - lo - chosen);
+    else b = -1;
+    out_sel[i] = b;
+  }
+  __syncthreads();
+}
+
 }  // namespace msa

@@ -35,6 +35,10 @@ msa_status check_params(const msa_params* p) {
     return fail(MSA_ERR_INVALID_ARGUMENT, "num_q_heads must be a multiple of num_kv_heads");
   if (!std::isfinite(p->softmax_scale))
     return fail(MSA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
+  if (p->sink_blocks < 0 || p->local_blocks < 0 ||
+      (int64_t)p->sink_blocks + p->local_blocks > (int64_t)p->top_k - 1)
+    return fail(MSA_ERR_INVALID_ARGUMENT,
+                "sink_blocks and local_blocks must be >= 0 with sink + local <= top_k - 1");
   if (p->head_dim != 128) return fail(MSA_ERR_UNSUPPORTED, "head_dim must be 128");
   if (p->idx_dim != 64) return fail(MSA_ERR_UNSUPPORTED, "idx_dim must be 64");
   if (p->block_size != 64 && p->block_size != 128)
@@ -79,8 +83,9 @@ msa_paged_kv read_view(const msa_paged_kv_mut* kv) {
 }
 
 msa::Dims dims_of(const msa_params* p) {
-  return msa::Dims{p->num_q_heads, p->num_kv_heads, p->head_dim, p->num_idx_heads,
-                   p->idx_dim,     p->block_size,   p->top_k,    p->softmax_scale};
+  return msa::Dims{p->num_q_heads, p->num_kv_heads, p->head_dim,   p->num_idx_heads,
+                   p->idx_dim,     p->block_size,   p->top_k,      p->softmax_scale,
+                   p->sink_blocks, p->local_blocks};
 }
 
 msa::Cache cache_of(const msa_paged_kv* kv) {

@@ -11,6 +11,7 @@ namespace msa {
 struct Dims {
   int32_t num_q_heads, num_kv_heads, head_dim, num_idx_heads, idx_dim, block_size, top_k;
   float softmax_scale;
+  int32_t sink_blocks, local_blocks;  // forced blocks of the selection
 };
 
 struct Cache {

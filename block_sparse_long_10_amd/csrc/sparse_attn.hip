@@ -36,12 +36,14 @@ template <int B>
 __global__ __launch_bounds__(256) void decode_topk_kernel(const float* __restrict__ pooled,
                                                           const int32_t* __restrict__ seq_lens,
                                                           int32_t num_kv_heads, int32_t max_blocks,
-                                                          int32_t top_k, int32_t* __restrict__ sel) {
+                                                          int32_t top_k, int32_t n_sink,
+                                                          int32_t n_local, int32_t* __restrict__ sel) {
   __shared__ TopkShared sh;
-  __shared__ int sel_s[kMaxTopK];
+  __shared__ int sel_s[kMaxTopK], tmp_s[kMaxTopK];
   const int g = blockIdx.x, s = blockIdx.y;
   const size_t sg = (size_t)s * num_kv_heads + g;
-  block_topk(pooled + sg * max_blocks, (seq_lens[s] - 1) / B, top_k, sel_s, sh);
+  block_topk_forced(pooled + sg * max_blocks, (seq_lens[s] - 1) / B, top_k, n_sink, n_local, sel_s,
+                    tmp_s, sh);
   for (int i = threadIdx.x; i < top_k; i += 256) sel[sg * top_k + i] = sel_s[i];
 }
 
@@ -57,10 +59,10 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
     const int32_t* __restrict__ block_table, int32_t max_blocks, const uint16_t* __restrict__ q,
     const int32_t* __restrict__ seq_lens, const float* __restrict__ pooled,
     int32_t* __restrict__ sel, int32_t num_kv_heads, int32_t group, int32_t top_k,
-    float scale_log2, float* __restrict__ part_o, float* __restrict__ part_ml,
-    uint32_t* __restrict__ counters, float* __restrict__ out) {
+    int32_t n_sink, int32_t n_local, float scale_log2, float* __restrict__ part_o,
+    float* __restrict__ part_ml, uint32_t* __restrict__ counters, float* __restrict__ out) {
   __shared__ TopkShared tsh;
-  __shared__ int sel_s[kMaxTopK];
+  __shared__ int sel_s[kMaxTopK], tmp_s[kMaxTopK];
   __shared__ AttendShared ash;
   __shared__ int is_last;
 
@@ -71,7 +73,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
   const size_t sg = (size_t)s * num_kv_heads + g;
   int blk;
   if constexpr (FUSED_TOPK) {
-    block_topk(pooled + sg * max_blocks, (L - 1) / B, top_k, sel_s, tsh);
+    block_topk_forced(pooled + sg * max_blocks, (L - 1) / B, top_k, n_sink, n_local, sel_s, tmp_s,
+                      tsh);
     if (slot == 0)
       for (int i = tid; i < top_k; i += 256) sel[sg * top_k + i] = sel_s[i];
     blk = sel_s[slot];
@@ -114,13 +117,13 @@ hipError_t launch_decode_attn(const Dims& d, const Cache& c, const uint16_t* q,
   const dim3 grid_attn(d.top_k, d.num_kv_heads, batch);
   const bool fused = (size_t)d.top_k * d.num_kv_heads * batch <= kFusedTopkMaxWorkgroups;
 #define MSA_ATTN_ARGS c.k, c.v, c.block_table, c.max_blocks, q, seq_lens, pooled, sel, \
-    d.num_kv_heads, G, d.top_k, sl2, part_o, part_ml, counters, out
+    d.num_kv_heads, G, d.top_k, d.sink_blocks, d.local_blocks, sl2, part_o, part_ml, counters, out
   if (d.block_size == 64) {
     if (fused) {
       hipLaunchKernelGGL((decode_attn_kernel<64, true>), grid_attn, dim3(256), 0, stream, MSA_ATTN_ARGS);
     } else {
       hipLaunchKernelGGL(decode_topk_kernel<64>, grid_sg, dim3(256), 0, stream, pooled, seq_lens,
-                         d.num_kv_heads, c.max_blocks, d.top_k, sel);
+                         d.num_kv_heads, c.max_blocks, d.top_k, d.sink_blocks, d.local_blocks, sel);
       hipLaunchKernelGGL((decode_attn_kernel<64, false>), grid_attn, dim3(256), 0, stream, MSA_ATTN_ARGS);
     }
   } else {
@@ -128,7 +131,7 @@ hipError_t launch_decode_attn(const Dims& d, const Cache& c, const uint16_t* q,
       hipLaunchKernelGGL((decode_attn_kernel<128, true>), grid_attn, dim3(256), 0, stream, MSA_ATTN_ARGS);
     } else {
       hipLaunchKernelGGL(decode_topk_kernel<128>, grid_sg, dim3(256), 0, stream, pooled, seq_lens,
-                         d.num_kv_heads, c.max_blocks, d.top_k, sel);
+                         d.num_kv_heads, c.max_blocks, d.top_k, d.sink_blocks, d.local_blocks, sel);
       hipLaunchKernelGGL((decode_attn_kernel<128, false>), grid_attn, dim3(256), 0, stream, MSA_ATTN_ARGS);
     }
   }

@@ -18,6 +18,12 @@
  * current block, which is always kept and never scored; only blocks before it
  * are eligible; ranking is by (score descending, block index ascending); query
  * head j belongs to group j / (num_q_heads / num_kv_heads).
+ * Forced blocks (section 2 of the same page: NSA's sliding-window branch is
+ * dropped, probably in favour of an attention sink or local attention): the
+ * first sink_blocks blocks and the local_blocks blocks just before the own
+ * block are always kept and never ranked; they count toward top_k, so TopK
+ * chooses top_k - 1 - (number forced) of the other blocks before the own one.
+ * sink_blocks = local_blocks = 0 is the plain method.
  *
  * Conventions for every entry point
  * ---------------------------------
@@ -36,7 +42,9 @@
  * - Supported set: head_dim 128, idx_dim 64, block_size 64 or 128,
  *   1 <= top_k <= 64, num_idx_heads in {1, 2, 4, 8, 16},
  *   num_kv_heads * num_idx_heads <= 64, group size num_q_heads/num_kv_heads
- *   in 1..16.  Other values return MSA_ERR_UNSUPPORTED.
+ *   in 1..16.  Other values return MSA_ERR_UNSUPPORTED.  sink_blocks and
+ *   local_blocks must be >= 0 with sink_blocks + local_blocks <= top_k - 1
+ *   (else MSA_ERR_INVALID_ARGUMENT).
  *
  * Paged KV cache (one page holds one KV block of block_size tokens)
  * -----------------------------------------------------------------
@@ -76,6 +84,9 @@ typedef struct {
   int32_t block_size;    /* B tokens per block (= page)                   */
   int32_t top_k;         /* k kept blocks per group, own block included   */
   float softmax_scale;   /* applied to attention scores only, e.g. 1/sqrt(D) */
+  int32_t sink_blocks;   /* blocks 0..sink_blocks-1 always kept (0: none)   */
+  int32_t local_blocks;  /* the local_blocks blocks just before the own block
+                            always kept (0: none)                          */
 } msa_params;
 
 typedef struct {

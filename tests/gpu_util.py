@@ -28,7 +28,7 @@ OUT_ROW_TOL = 2e-3
 def params_of(shape):
     return msa.make_params(shape.num_q_heads, shape.num_kv_heads, shape.head_dim,
                            shape.num_idx_heads, shape.idx_dim, shape.block_size, shape.top_k,
-                           shape.softmax_scale)
+                           shape.softmax_scale, shape.sink_blocks, shape.local_blocks)
 
 
 def kv_of(case):
@@ -87,21 +87,26 @@ def check_pooled(gpu, ref, what=""):
     return float(err.max()) if err.size else 0.0
 
 
-def check_selection(gpu_row, scores, own, k, exact_only=False):
+def check_selection(gpu_row, scores, own, k, exact_only=False, sink=0, local=0):
     """Validate one GPU selection row against the oracle scores of blocks
-    0..own-1.  Returns "exact" or "near-tie"; raises on a wrong selection."""
+    0..own-1 (with `sink` leading and `local` trailing blocks forced).
+    Returns "exact" or "near-tie"; raises on a wrong selection."""
     g = [int(b) for b in gpu_row]
-    keep = min(k - 1, own)
+    forced = [b for b in range(own) if b < sink or b >= own - local]
+    elig = [b for b in range(own) if not (b < sink or b >= own - local)]
+    keep = min(k - 1 - len(forced), len(elig))
     kept = [b for b in g if b >= 0]
     assert g[len(kept):] == [-1] * (k - len(kept)), "padding is not -1: %s" % g
     assert kept == sorted(kept) and len(set(kept)) == len(kept), "not ascending: %s" % g
-    assert len(kept) == keep + 1 and kept[-1] == own, "own block / count wrong: %s (own %d)" % (g, own)
-    chosen = kept[:-1]
-    if keep >= own:
-        assert chosen == list(range(own)), g
+    assert len(kept) == len(forced) + keep + 1 and kept[-1] == own, \
+        "own block / count wrong: %s (own %d)" % (g, own)
+    assert set(forced) <= set(kept), "forced blocks missing: %s" % g
+    chosen = sorted(set(kept[:-1]) - set(forced))
+    if keep >= len(elig):
+        assert chosen == elig, g
         return "exact"
     s = np.asarray(scores[:own], np.float64)
-    order = sorted(range(own), key=lambda b: (-s[b], b))
+    order = sorted(elig, key=lambda b: (-s[b], b))
     ref = sorted(order[:keep])
     if chosen == ref:
         return "exact"
@@ -113,8 +118,8 @@ def check_selection(gpu_row, scores, own, k, exact_only=False):
         return abs(x - s_star) <= GAP_REL * max(abs(x), abs(s_star))
 
     assert in_band(s_next), "selection %s != oracle %s and no near tie" % (chosen, ref)
-    above = {b for b in range(own) if s[b] > s_star and not in_band(s[b])}
-    band = {b for b in range(own) if in_band(s[b])}
+    above = {b for b in elig if s[b] > s_star and not in_band(s[b])}
+    band = {b for b in elig if in_band(s[b])}
     assert above <= set(chosen) <= above | band, "near-tie selection invalid: %s" % chosen
     return "near-tie"
 

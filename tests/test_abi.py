@@ -75,6 +75,8 @@ def decode_status(p, kv, batch=2, max_seq_len=1000, ws_bytes=None, **null):
     (dict(num_idx_heads=16), UNSUPPORTED, "num_kv_heads * num_idx_heads"),
     (dict(num_q_heads=256), UNSUPPORTED, "group size"),
     (dict(softmax_scale=float("inf")), INVALID, "finite"),
+    (dict(sink_blocks=-1), INVALID, "sink"),
+    (dict(sink_blocks=8, local_blocks=8), INVALID, "top_k - 1"),
 ])
 def test_decode_rejects_bad_params(change, status, msg):
     assert decode_status(good_params(**change), fake_kv()) == status
