@@ -21,6 +21,7 @@ __all__ = [
     "msa_prefill_workspace_bytes", "msa_prefill_chunk", "msa_index_score_prefill",
     "msa_block_topk_prefill", "msa_sparse_attn_prefill", "msa_last_error", "msa_version",
     "PagedKVMut", "make_kv_mut", "msa_cache_append", "msa_decode_append",
+    "msa_prefill_varlen_workspace_bytes", "msa_prefill_varlen",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -87,6 +88,9 @@ def lib():
             "msa_cache_append": (ctypes.c_int, [P, KM, vp, vp, vp, vp, i32, i32, vp]),
             "msa_decode_append": (ctypes.c_int, [P, KM, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp,
                                                  vp, sz, vp]),
+            "msa_prefill_varlen_workspace_bytes": (sz, [P, vp, vp, i32, i32]),
+            "msa_prefill_varlen": (ctypes.c_int, [P, K, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                                                  sz, vp]),
             "msa_last_error": (ctypes.c_char_p, []),
             "msa_version": (ctypes.c_char_p, []),
         }
@@ -243,3 +247,36 @@ def msa_sparse_attn_prefill(params: Params, kv: PagedKV, q, prior_len: int, chun
                                          _dev(q, torch.bfloat16, "q"), prior_len, chunk_len,
                                          _dev(sel, torch.int32, "sel"),
                                          _dev(out, torch.float32, "out"), _stream(stream)))
+
+
+def _host_i32(values):
+    arr = (ctypes.c_int32 * len(values))(*[int(x) for x in values])
+    return arr
+
+
+def msa_prefill_varlen_workspace_bytes(params: Params, prior_lens, chunk_lens,
+                                       max_blocks_per_seq: int) -> int:
+    """prior_lens, chunk_lens: host sequences of ints."""
+    n = len(prior_lens)
+    return int(lib().msa_prefill_varlen_workspace_bytes(
+        ctypes.byref(params), ctypes.cast(_host_i32(prior_lens), ctypes.c_void_p),
+        ctypes.cast(_host_i32(chunk_lens), ctypes.c_void_p), n, max_blocks_per_seq))
+
+
+def msa_prefill_varlen(params: Params, kv: PagedKV, q, idx_q, prior_lens, chunk_lens,
+                       prior_lens_host, chunk_lens_host, out, sel=None, workspace=None,
+                       stream=None) -> None:
+    """prior_lens, chunk_lens: int32 GPU tensors [batch]; the *_host arguments
+    are host sequences of the same values."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ph, ch = _host_i32(prior_lens_host), _host_i32(chunk_lens_host)
+    _check(lib().msa_prefill_varlen(ctypes.byref(params), ctypes.byref(kv),
+                                    _dev(q, torch.bfloat16, "q"),
+                                    _dev(idx_q, torch.bfloat16, "idx_q"),
+                                    _dev(prior_lens, torch.int32, "prior_lens"),
+                                    _dev(chunk_lens, torch.int32, "chunk_lens"),
+                                    ctypes.cast(ph, ctypes.c_void_p),
+                                    ctypes.cast(ch, ctypes.c_void_p), len(prior_lens_host),
+                                    _dev(out, torch.float32, "out"), _dev(sel, torch.int32, "sel"),
+                                    _dev(workspace, None, "workspace"), ws_bytes,
+                                    _stream(stream)))

@@ -16,6 +16,7 @@
 // (XOR-swizzled 16-byte chunks, double-buffered) as the B side.  The 32x32
 // accumulators are folded with v_max into one running max per lane and
 // reduced across the workgroup once per block.
+#include "chunk_map.h"
 #include "decode_parts.h"
 #include "msa_device.h"
 #include "msa_launch.h"
@@ -141,7 +142,7 @@ hipError_t launch_index_score_decode(const Dims& d, const Cache& c, const uint16
 template <int B>
 __global__ __launch_bounds__(256) void index_score_prefill_kernel(
     const uint16_t* __restrict__ idx_k, const int32_t* __restrict__ block_table,
-    const uint16_t* __restrict__ idx_q, int32_t prior_len, int32_t chunk_len, int32_t num_kv_heads,
+    const uint16_t* __restrict__ idx_q, ChunkMap map, int32_t num_kv_heads,
     int32_t num_idx_heads, int32_t max_blocks, int32_t blocks_per_split,
     float* __restrict__ pooled) {
   constexpr int NT = B / 32;                       // 32-token N tiles per block
@@ -152,12 +153,13 @@ __global__ __launch_bounds__(256) void index_score_prefill_kernel(
 
   const int tile = blockIdx.x, g = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int own = prior_len / B + tile;
+  const TileLoc loc = locate_tile(map, tile);
+  const int own = loc.prior / B + loc.tile;
   const int b_lo = split * blocks_per_split;
   const int b_hi = min(b_lo + blocks_per_split, own);
   if (b_lo >= b_hi) return;
-  const int q0 = max(0, own * B - prior_len);
-  const int q1 = min(chunk_len, (own + 1) * B - prior_len);
+  const int q0 = loc.q0 + max(0, own * B - loc.prior);  // rows of q / idx_q
+  const int q1 = loc.q0 + min(loc.chunk, (own + 1) * B - loc.prior);
   const int nrows = (q1 - q0) * num_idx_heads;
 
   // A operand: row slot = wave*128 + mt*32 + (lane & 31); K = 64 in 4 steps of 16.
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(256) void index_score_prefill_kernel(
     for (int ks = 0; ks < 4; ++ks) a[mt][ks] = load_bf16x8(p + ks * 16);
   }
 
-  const int32_t* bt = block_table;  // one sequence
+  const int32_t* bt = block_table + (size_t)loc.seq * map.max_blocks;
   const int src_off = (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) << 4);
   auto issue = [&](int b, int buf) {
     const uint8_t* src = reinterpret_cast<const uint8_t*>(idx_k) + (size_t)bt[b] * BLOCK_BYTES;
@@ -237,12 +239,9 @@ __global__ __launch_bounds__(256) void index_score_prefill_kernel(
 }
 
 hipError_t launch_index_score_prefill(const Dims& d, const Cache& c, const uint16_t* idx_q,
-                                      int32_t prior_len, int32_t chunk_len, float* pooled,
-                                      hipStream_t stream) {
+                                      const ChunkMap& map, int32_t num_tiles, int32_t max_own,
+                                      float* pooled, hipStream_t stream) {
   const int B = d.block_size;
-  const int first = prior_len / B;
-  const int num_tiles = (prior_len + chunk_len + B - 1) / B - first;
-  const int max_own = first + num_tiles - 1;
   // split the key range so that the grid holds many workgroups per CU
   const int units = num_tiles * d.num_kv_heads;
   int splits = (4096 + units - 1) / units;
@@ -251,11 +250,11 @@ hipError_t launch_index_score_prefill(const Dims& d, const Cache& c, const uint1
   dim3 grid(num_tiles, d.num_kv_heads, splits);
   if (B == 64)
     hipLaunchKernelGGL(index_score_prefill_kernel<64>, grid, dim3(256), 0, stream, c.idx_k,
-                       c.block_table, idx_q, prior_len, chunk_len, d.num_kv_heads,
+                       c.block_table, idx_q, map, d.num_kv_heads,
                        d.num_idx_heads, c.max_blocks, per, pooled);
   else
     hipLaunchKernelGGL(index_score_prefill_kernel<128>, grid, dim3(256), 0, stream, c.idx_k,
-                       c.block_table, idx_q, prior_len, chunk_len, d.num_kv_heads,
+                       c.block_table, idx_q, map, d.num_kv_heads,
                        d.num_idx_heads, c.max_blocks, per, pooled);
   return hipGetLastError();
 }

@@ -6,6 +6,7 @@
 // synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <string>
@@ -137,6 +138,69 @@ PrefillWs prefill_layout(const msa_params* p, int32_t prior_len, int32_t chunk_l
   w.sel = align_up(rows * (size_t)max_blocks * sizeof(float));
   w.total = w.sel + align_up(rows * p->top_k * sizeof(int32_t));
   return w;
+}
+
+// One sequence as a chunk map (no device tables).
+msa::ChunkMap single_map(int32_t prior_len, int32_t chunk_len, int32_t max_blocks) {
+  return msa::ChunkMap{nullptr, nullptr, nullptr, nullptr, nullptr, prior_len, chunk_len,
+                       max_blocks};
+}
+
+// Sizes of a batch of chunks, from the host copies of the lengths.
+struct VarlenSizes {
+  int64_t tiles, rows;
+  int32_t max_own;
+};
+VarlenSizes varlen_sizes(const int32_t* prior, const int32_t* chunk, int32_t batch, int32_t B) {
+  VarlenSizes v{0, 0, 0};
+  for (int32_t s = 0; s < batch; ++s) {
+    const int64_t p = prior[s], c = chunk[s];
+    v.tiles += (p + c + B - 1) / B - p / B;
+    v.rows += c;
+    v.max_own = std::max(v.max_own, (int32_t)((p + c - 1) / B));
+  }
+  return v;
+}
+
+struct VarlenWs {
+  size_t pooled, sel, tile_seq, tile_start, q_start, total;
+};
+VarlenWs varlen_layout(const msa_params* p, int64_t tiles, int32_t batch, int32_t max_blocks) {
+  const size_t rows = (size_t)tiles * p->num_kv_heads;
+  VarlenWs w{};
+  size_t off = 0;
+  w.pooled = off;
+  off += align_up(rows * (size_t)max_blocks * sizeof(float));
+  w.sel = off;
+  off += align_up(rows * p->top_k * sizeof(int32_t));
+  w.tile_seq = off;
+  off += align_up((size_t)tiles * sizeof(int32_t));
+  w.tile_start = off;
+  off += align_up(((size_t)batch + 1) * sizeof(int32_t));
+  w.q_start = off;
+  off += align_up(((size_t)batch + 1) * sizeof(int32_t));
+  w.total = off;
+  return w;
+}
+
+msa_status check_varlen(const msa_params* p, int32_t max_blocks, const int32_t* prior_host,
+                        const int32_t* chunk_host, int32_t batch) {
+  if (prior_host == nullptr || chunk_host == nullptr)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "host length arrays must not be NULL");
+  if (batch < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "batch must be >= 1");
+  for (int32_t s = 0; s < batch; ++s) {
+    if (prior_host[s] < 0 || chunk_host[s] < 1)
+      return fail(MSA_ERR_INVALID_ARGUMENT, "prior_lens must be >= 0 and chunk_lens >= 1");
+    if ((int64_t)prior_host[s] + chunk_host[s] > (int64_t)max_blocks * p->block_size)
+      return fail(MSA_ERR_INVALID_ARGUMENT,
+                  "prior_len + chunk_len exceeds max_blocks_per_seq * block_size");
+  }
+  const VarlenSizes v = varlen_sizes(prior_host, chunk_host, batch, p->block_size);
+  if (v.tiles > 0x7FFFFFFF || v.rows > 0x7FFFFFFF)
+    return fail(MSA_ERR_UNSUPPORTED, "total tiles and chunk rows must fit in int32");
+  if (p->block_size * p->num_idx_heads > 512)
+    return fail(MSA_ERR_UNSUPPORTED, "prefill needs block_size * num_idx_heads <= 512");
+  return MSA_OK;
 }
 
 msa_status check_prefill_sizes(const msa_params* p, const msa_paged_kv* kv, int32_t prior_len,
@@ -286,10 +350,12 @@ msa_status msa_index_score_prefill(const msa_params* params, const msa_paged_kv*
   if (idx_q == nullptr || pooled == nullptr)
     return fail(MSA_ERR_INVALID_ARGUMENT, "idx_q and pooled must not be NULL");
   if ((st = check_prefill_sizes(params, kv, prior_len, chunk_len)) != MSA_OK) return st;
-  return hip_status(msa::launch_index_score_prefill(dims_of(params), cache_of(kv),
-                                                    static_cast<const uint16_t*>(idx_q), prior_len,
-                                                    chunk_len, pooled,
-                                                    static_cast<hipStream_t>(stream)),
+  const int32_t B = params->block_size;
+  const int32_t tiles = num_tiles_of(prior_len, chunk_len, B);
+  return hip_status(msa::launch_index_score_prefill(
+                        dims_of(params), cache_of(kv), static_cast<const uint16_t*>(idx_q),
+                        single_map(prior_len, chunk_len, kv->max_blocks_per_seq), tiles,
+                        prior_len / B + tiles - 1, pooled, static_cast<hipStream_t>(stream)),
                     "prefill index score launch");
 }
 
@@ -303,9 +369,10 @@ msa_status msa_block_topk_prefill(const msa_params* params, int32_t prior_len, i
   if (prior_len < 0 || chunk_len < 1 || max_blocks_per_seq < 1 ||
       (int64_t)prior_len + chunk_len > (int64_t)max_blocks_per_seq * params->block_size)
     return fail(MSA_ERR_INVALID_ARGUMENT, "inconsistent prior_len, chunk_len, max_blocks_per_seq");
-  return hip_status(msa::launch_block_topk_prefill(dims_of(params), prior_len, chunk_len,
-                                                   max_blocks_per_seq, pooled, sel,
-                                                   static_cast<hipStream_t>(stream)),
+  return hip_status(msa::launch_block_topk_prefill(
+                        dims_of(params), single_map(prior_len, chunk_len, max_blocks_per_seq),
+                        num_tiles_of(prior_len, chunk_len, params->block_size),
+                        max_blocks_per_seq, pooled, sel, static_cast<hipStream_t>(stream)),
                     "prefill topk launch");
 }
 
@@ -318,10 +385,11 @@ msa_status msa_sparse_attn_prefill(const msa_params* params, const msa_paged_kv*
   if (q == nullptr || sel == nullptr || out == nullptr)
     return fail(MSA_ERR_INVALID_ARGUMENT, "q, sel and out must not be NULL");
   if ((st = check_prefill_sizes(params, kv, prior_len, chunk_len)) != MSA_OK) return st;
-  return hip_status(msa::launch_sparse_attn_prefill(dims_of(params), cache_of(kv),
-                                                    static_cast<const uint16_t*>(q), prior_len,
-                                                    chunk_len, sel, out,
-                                                    static_cast<hipStream_t>(stream)),
+  return hip_status(msa::launch_sparse_attn_prefill(
+                        dims_of(params), cache_of(kv), static_cast<const uint16_t*>(q),
+                        single_map(prior_len, chunk_len, kv->max_blocks_per_seq),
+                        num_tiles_of(prior_len, chunk_len, params->block_size), sel, out,
+                        static_cast<hipStream_t>(stream)),
                     "prefill sparse attention launch");
 }
 
@@ -343,16 +411,80 @@ msa_status msa_prefill_chunk(const msa_params* params, const msa_paged_kv* kv, c
   hipStream_t s = static_cast<hipStream_t>(stream);
   const msa::Dims d = dims_of(params);
   const msa::Cache c = cache_of(kv);
-  st = hip_status(msa::launch_index_score_prefill(d, c, static_cast<const uint16_t*>(idx_q),
-                                                  prior_len, chunk_len, pooled, s),
+  const msa::ChunkMap m = single_map(prior_len, chunk_len, kv->max_blocks_per_seq);
+  const int32_t tiles = num_tiles_of(prior_len, chunk_len, params->block_size);
+  const int32_t max_own = prior_len / params->block_size + tiles - 1;
+  st = hip_status(msa::launch_index_score_prefill(d, c, static_cast<const uint16_t*>(idx_q), m,
+                                                  tiles, max_own, pooled, s),
                   "prefill index score launch");
   if (st != MSA_OK) return st;
-  st = hip_status(msa::launch_block_topk_prefill(d, prior_len, chunk_len, kv->max_blocks_per_seq,
-                                                 pooled, sel_buf, s),
+  st = hip_status(msa::launch_block_topk_prefill(d, m, tiles, kv->max_blocks_per_seq, pooled,
+                                                 sel_buf, s),
                   "prefill topk launch");
   if (st != MSA_OK) return st;
-  return hip_status(msa::launch_sparse_attn_prefill(d, c, static_cast<const uint16_t*>(q),
-                                                    prior_len, chunk_len, sel_buf, out, s),
+  return hip_status(msa::launch_sparse_attn_prefill(d, c, static_cast<const uint16_t*>(q), m,
+                                                    tiles, sel_buf, out, s),
+                    "prefill sparse attention launch");
+}
+
+size_t msa_prefill_varlen_workspace_bytes(const msa_params* params, const int32_t* prior_lens_host,
+                                          const int32_t* chunk_lens_host, int32_t batch,
+                                          int32_t max_blocks_per_seq) {
+  if (check_params(params) != MSA_OK || max_blocks_per_seq < 1 ||
+      check_varlen(params, max_blocks_per_seq, prior_lens_host, chunk_lens_host, batch) != MSA_OK)
+    return 0;
+  const VarlenSizes v = varlen_sizes(prior_lens_host, chunk_lens_host, batch, params->block_size);
+  return varlen_layout(params, v.tiles, batch, max_blocks_per_seq).total;
+}
+
+msa_status msa_prefill_varlen(const msa_params* params, const msa_paged_kv* kv, const void* q,
+                              const void* idx_q, const int32_t* prior_lens,
+                              const int32_t* chunk_lens, const int32_t* prior_lens_host,
+                              const int32_t* chunk_lens_host, int32_t batch, float* out,
+                              int32_t* sel, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  msa_status st = check_params(params);
+  if (st != MSA_OK) return st;
+  if ((st = check_kv(kv)) != MSA_OK) return st;
+  if (q == nullptr || idx_q == nullptr || out == nullptr || prior_lens == nullptr ||
+      chunk_lens == nullptr)
+    return fail(MSA_ERR_INVALID_ARGUMENT,
+                "q, idx_q, out, prior_lens and chunk_lens must not be NULL");
+  if (batch > 65535) return fail(MSA_ERR_UNSUPPORTED, "batch must be <= 65535");
+  if ((st = check_varlen(params, kv->max_blocks_per_seq, prior_lens_host, chunk_lens_host,
+                         batch)) != MSA_OK)
+    return st;
+  const VarlenSizes v = varlen_sizes(prior_lens_host, chunk_lens_host, batch, params->block_size);
+  const VarlenWs w = varlen_layout(params, v.tiles, batch, kv->max_blocks_per_seq);
+  if (workspace == nullptr || workspace_bytes < w.total)
+    return fail(MSA_ERR_WORKSPACE,
+                "workspace missing or smaller than msa_prefill_varlen_workspace_bytes()");
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* pooled = reinterpret_cast<float*>(ws + w.pooled);
+  int32_t* sel_buf = sel != nullptr ? sel : reinterpret_cast<int32_t*>(ws + w.sel);
+  int32_t* tile_seq = reinterpret_cast<int32_t*>(ws + w.tile_seq);
+  int32_t* tile_start = reinterpret_cast<int32_t*>(ws + w.tile_start);
+  int32_t* q_start = reinterpret_cast<int32_t*>(ws + w.q_start);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const msa::Dims d = dims_of(params);
+  const msa::Cache c = cache_of(kv);
+  const int32_t tiles = (int32_t)v.tiles;
+  st = hip_status(msa::launch_chunk_map(prior_lens, chunk_lens, batch, params->block_size, tiles,
+                                        tile_seq, tile_start, q_start, s),
+                  "prefill chunk map launch");
+  if (st != MSA_OK) return st;
+  const msa::ChunkMap m{tile_seq, tile_start, q_start, prior_lens, chunk_lens, 0, 0,
+                        kv->max_blocks_per_seq};
+  st = hip_status(msa::launch_index_score_prefill(d, c, static_cast<const uint16_t*>(idx_q), m,
+                                                  tiles, v.max_own, pooled, s),
+                  "prefill index score launch");
+  if (st != MSA_OK) return st;
+  st = hip_status(msa::launch_block_topk_prefill(d, m, tiles, kv->max_blocks_per_seq, pooled,
+                                                 sel_buf, s),
+                  "prefill topk launch");
+  if (st != MSA_OK) return st;
+  return hip_status(msa::launch_sparse_attn_prefill(d, c, static_cast<const uint16_t*>(q), m,
+                                                    tiles, sel_buf, out, s),
                     "prefill sparse attention launch");
 }
 

@@ -64,19 +64,41 @@ hipError_t launch_decode_attn(const Dims& d, const Cache& c, const uint16_t* q,
                               float* part_o, float* part_ml, uint32_t* counters, int32_t* sel,
                               float* out, hipStream_t stream);
 
-// Step 1, prefill: pooled[t][g][b] for b < prior_len/B + t.
-hipError_t launch_index_score_prefill(const Dims& d, const Cache& c, const uint16_t* idx_q,
-                                      int32_t prior_len, int32_t chunk_len, float* pooled,
-                                      hipStream_t stream);
+// Prefill chunks of one or several sequences.  Tiles are numbered sequence
+// after sequence; tile u of the call is local tile t of sequence s, whose
+// chunk rows start at row q_start[s] of q / idx_q / out.  With
+// tile_seq == nullptr there is one sequence (s = 0, t = u, q rows from 0)
+// whose lengths are prior_len and chunk_len.
+struct ChunkMap {
+  const int32_t* tile_seq;    // [num_tiles] sequence of each tile (device)
+  const int32_t* tile_start;  // [batch + 1] first tile of each sequence
+  const int32_t* q_start;     // [batch + 1] first chunk row of each sequence
+  const int32_t* prior_lens;  // [batch]
+  const int32_t* chunk_lens;  // [batch]
+  int32_t prior_len, chunk_len;
+  int32_t max_blocks;         // block-table row stride
+};
 
-// TopK, prefill: sel[t][g][k].
-hipError_t launch_block_topk_prefill(const Dims& d, int32_t prior_len, int32_t chunk_len,
+// Builds tile_seq, tile_start and q_start of a batch of chunks (one
+// workgroup) from the device lengths.
+hipError_t launch_chunk_map(const int32_t* prior_lens, const int32_t* chunk_lens, int32_t batch,
+                            int32_t block_size, int32_t num_tiles, int32_t* tile_seq,
+                            int32_t* tile_start, int32_t* q_start, hipStream_t stream);
+
+// Step 1, prefill: pooled[u][g][b] for b < own(u) = prior/B + t; max_own is
+// the largest own block of the call.
+hipError_t launch_index_score_prefill(const Dims& d, const Cache& c, const uint16_t* idx_q,
+                                      const ChunkMap& m, int32_t num_tiles, int32_t max_own,
+                                      float* pooled, hipStream_t stream);
+
+// TopK, prefill: sel[u][g][k].
+hipError_t launch_block_topk_prefill(const Dims& d, const ChunkMap& m, int32_t num_tiles,
                                      int32_t max_blocks, const float* pooled, int32_t* sel,
                                      hipStream_t stream);
 
 // Step 2, prefill, for a given selection.
 hipError_t launch_sparse_attn_prefill(const Dims& d, const Cache& c, const uint16_t* q,
-                                      int32_t prior_len, int32_t chunk_len, const int32_t* sel,
+                                      const ChunkMap& m, int32_t num_tiles, const int32_t* sel,
                                       float* out, hipStream_t stream);
 
 }  // namespace msa

@@ -24,6 +24,7 @@
 // consumed 32 keys at a time with v_mfma_f32_32x32x16_bf16 and an online
 // softmax; the causal mask applies inside the tile's diagonal block only.
 #include "block_topk.h"
+#include "chunk_map.h"
 #include "decode_parts.h"
 #include "msa_device.h"
 #include "msa_launch.h"
@@ -194,9 +195,8 @@ template <int B>
 __global__ __launch_bounds__(512) void prefill_attn_kernel(
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ block_table, const uint16_t* __restrict__ q,
-    const int32_t* __restrict__ sel, int32_t prior_len, int32_t chunk_len, int32_t num_kv_heads,
-    int32_t group, int32_t top_k, int32_t num_units, int32_t zr, float scale_log2,
-    float* __restrict__ out) {
+    const int32_t* __restrict__ sel, ChunkMap map, int32_t num_kv_heads, int32_t group,
+    int32_t top_k, int32_t num_units, int32_t zr, float scale_log2, float* __restrict__ out) {
   constexpr int KBYTES = B * 256;          // K block: B rows of 256 bytes
   constexpr int VROW = 2 * B;              // V^T row: B keys
   constexpr int VCH = B / 8;               // 16-byte chunks per V^T row
@@ -215,9 +215,11 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   if (unit >= num_units) return;
   const int tile = unit / num_kv_heads, g = unit % num_kv_heads;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int own = prior_len / B + tile;
-  const int q0 = max(0, own * B - prior_len);
-  const int q1 = min(chunk_len, (own + 1) * B - prior_len);
+  const TileLoc loc = locate_tile(map, tile);
+  const int prior_len = loc.prior;
+  const int own = prior_len / B + loc.tile;
+  const int q0 = max(0, own * B - prior_len);  // chunk-local query range of the tile
+  const int q1 = min(loc.chunk, (own + 1) * B - prior_len);
   const int nq = q1 - q0;
   const int nrows = nq * group;
   const int row0 = z * kPrefillRows;
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   int blk_t = -1;
   if (tid < top_k) {
     blk_t = srow[tid];
-    pages[tid] = blk_t >= 0 ? block_table[blk_t] : 0;
+    pages[tid] = blk_t >= 0 ? block_table[(size_t)loc.seq * map.max_blocks + blk_t] : 0;
     blocks[tid] = blk_t;
   }
   const int nsel = __syncthreads_count(tid < top_k && blk_t >= 0);
@@ -242,7 +244,8 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   const int pos = prior_len + qi;
   bf16x8 qf[8];
   {
-    const uint16_t* qp = q + ((size_t)qi * Hq + (size_t)g * group + hh) * 128 + half * 8;
+    const uint16_t* qp =
+        q + ((size_t)(loc.q0 + qi) * Hq + (size_t)g * group + hh) * 128 + half * 8;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = load_bf16x8(qp + ks * 16);
   }
@@ -365,7 +368,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   const float l_row = half_swap_sum(l_run);
   if (!row_ok) return;
   const float inv = 1.f / l_row;
-  float* op = out + ((size_t)qi * Hq + (size_t)g * group + hh) * 128;
+  float* op = out + ((size_t)(loc.q0 + qi) * Hq + (size_t)g * group + hh) * 128;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -378,24 +381,22 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
 }
 
 hipError_t launch_sparse_attn_prefill(const Dims& d, const Cache& c, const uint16_t* q,
-                                      int32_t prior_len, int32_t chunk_len, const int32_t* sel,
+                                      const ChunkMap& map, int32_t num_tiles, const int32_t* sel,
                                       float* out, hipStream_t stream) {
   const int B = d.block_size;
   const int G = d.num_q_heads / d.num_kv_heads;
-  const int first = prior_len / B;
-  const int num_tiles = (prior_len + chunk_len + B - 1) / B - first;
   const int units = num_tiles * d.num_kv_heads;
   const int zr = (B * G + kPrefillRows - 1) / kPrefillRows;
   const int nwg = (units + 7) / 8 * 8 * zr;
   const float sl2 = d.softmax_scale * kLog2e;
   if (B == 64)
     hipLaunchKernelGGL(prefill_attn_kernel<64>, dim3(nwg), dim3(512), 0, stream, c.k, c.v,
-                       c.block_table, q, sel, prior_len, chunk_len, d.num_kv_heads, G, d.top_k,
-                       units, zr, sl2, out);
+                       c.block_table, q, sel, map, d.num_kv_heads, G, d.top_k, units, zr, sl2,
+                       out);
   else
     hipLaunchKernelGGL(prefill_attn_kernel<128>, dim3(nwg), dim3(512), 0, stream, c.k, c.v,
-                       c.block_table, q, sel, prior_len, chunk_len, d.num_kv_heads, G, d.top_k,
-                       units, zr, sl2, out);
+                       c.block_table, q, sel, map, d.num_kv_heads, G, d.top_k, units, zr, sl2,
+                       out);
   return hipGetLastError();
 }
 

@@ -202,6 +202,37 @@ msa_status msa_prefill_chunk(const msa_params *params, const msa_paged_kv *kv,
                              int32_t *sel, void *workspace,
                              size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------- batched prefill (varlen)
+ * Chunks of `batch` sequences in one call, each with its own context: the
+ * same computation as msa_prefill_chunk for every sequence s, with prior
+ * length prior_lens[s], chunk length chunk_lens[s] and block-table row s.
+ * The chunks' rows are packed sequence after sequence: sequence s owns rows
+ * q_start[s] .. q_start[s]+chunk_lens[s]-1 of q, idx_q and out, where
+ * q_start[s] = chunk_lens[0] + ... + chunk_lens[s-1].  Tiles are numbered the
+ * same way (those of sequence 0 first), giving the rows of sel.
+ *   q          bf16 [total_rows][Hq][D]
+ *   idx_q      bf16 [total_rows][Hkv][n_i][d_i]
+ *   prior_lens, chunk_lens       int32 [batch], device
+ *   prior_lens_host, chunk_lens_host  int32 [batch], host copies of the
+ *              same values (they size the launches; read during the call
+ *              only)
+ *   out        f32 [total_rows][Hq][D]
+ *   sel        int32 [total_tiles][Hkv][top_k] or NULL
+ * Each prior_lens[s] >= 0, chunk_lens[s] >= 1, and prior + chunk must fit
+ * in max_blocks_per_seq blocks; batch <= 65535. */
+size_t msa_prefill_varlen_workspace_bytes(const msa_params *params,
+                                          const int32_t *prior_lens_host,
+                                          const int32_t *chunk_lens_host,
+                                          int32_t batch, int32_t max_blocks_per_seq);
+
+msa_status msa_prefill_varlen(const msa_params *params, const msa_paged_kv *kv,
+                              const void *q, const void *idx_q,
+                              const int32_t *prior_lens, const int32_t *chunk_lens,
+                              const int32_t *prior_lens_host,
+                              const int32_t *chunk_lens_host, int32_t batch,
+                              float *out, int32_t *sel, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
 /* Step 1 of prefill alone: pooled f32 [num_tiles][Hkv][max_blocks_per_seq];
  * entries b < c_t are written, the others are left untouched. */
 msa_status msa_index_score_prefill(const msa_params *params,

@@ -304,6 +304,60 @@ def make_prefill_case(shape: Shape, prior_len: int, chunk_len: int, seed: int,
     return PrefillCase(shape, cache, q, idx_q, prior_len, chunk_len)
 
 
+@dataclasses.dataclass
+class VarlenPrefillCase:
+    """Chunks of several sequences for one batched prefill call: sequence s has
+    prior_lens[s] cached tokens before its chunk of chunk_lens[s] queries; the
+    chunks' rows of q / idx_q are packed sequence after sequence."""
+    shape: Shape
+    cache: PagedCache            # lengths[s] = prior_lens[s] + chunk_lens[s]
+    q: torch.Tensor              # bf16 [total_rows][Hq][D]
+    idx_q: torch.Tensor          # bf16 [total_rows][Hkv][n_i][d_i]
+    prior_lens: List[int]
+    chunk_lens: List[int]
+
+    @property
+    def batch(self) -> int:
+        return len(self.prior_lens)
+
+    @property
+    def q_start(self) -> List[int]:
+        out, acc = [], 0
+        for c in self.chunk_lens:
+            out.append(acc)
+            acc += c
+        return out
+
+    def num_tiles_of(self, s: int) -> int:
+        B = self.shape.block_size
+        P, C = self.prior_lens[s], self.chunk_lens[s]
+        return (P + C + B - 1) // B - P // B
+
+    def sequence(self, s: int) -> PrefillCase:
+        """Sequence s alone, as a one-sequence prefill case sharing the tensors."""
+        c = self.cache
+        one = PagedCache(k=c.k, v=c.v, idx_k=c.idx_k, block_table=c.block_table[s:s + 1],
+                         num_pages=c.num_pages, max_blocks=c.max_blocks,
+                         lengths=[c.lengths[s]])
+        r0, n = self.q_start[s], self.chunk_lens[s]
+        return PrefillCase(self.shape, one, self.q[r0:r0 + n], self.idx_q[r0:r0 + n],
+                           self.prior_lens[s], n)
+
+
+def make_varlen_prefill_case(shape: Shape, prior_lens: Sequence[int], chunk_lens: Sequence[int],
+                             seed: int, device="cpu", shuffle_pages=False,
+                             poison_frac=0.0) -> VarlenPrefillCase:
+    priors, chunks = [int(p) for p in prior_lens], [int(c) for c in chunk_lens]
+    assert len(priors) == len(chunks) and all(p >= 0 for p in priors) and all(c >= 1 for c in chunks)
+    cache = build_paged_cache(shape, [p + c for p, c in zip(priors, chunks)], seed, device,
+                              shuffle_pages, poison_frac)
+    rows = sum(chunks)
+    q = normal_bf16((rows, shape.num_q_heads, shape.head_dim), seed, TENSOR_IDS["q"], device)
+    idx_q = normal_bf16((rows, shape.num_kv_heads, shape.num_idx_heads, shape.idx_dim), seed,
+                        TENSOR_IDS["idx_q"], device)
+    return VarlenPrefillCase(shape, cache, q, idx_q, priors, chunks)
+
+
 def make_workload(name: str, device="cpu"):
     """Inputs of a named workload of ``WORKLOADS``."""
     w = WORKLOADS[name]

@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
     for n in ["msa_decode", "msa_prefill_chunk", "msa_decode_workspace_bytes",
               "msa_prefill_workspace_bytes", "msa_last_error", "msa_index_score_decode",
               "msa_index_score_prefill", "msa_block_topk_prefill", "msa_sparse_attn_prefill",
-              "msa_cache_append", "msa_decode_append"]:
+              "msa_cache_append", "msa_decode_append", "msa_prefill_varlen",
+              "msa_prefill_varlen_workspace_bytes"]:
         assert n in names
 
 
@@ -176,3 +177,31 @@ def test_append_entry_points_reject_bad_arguments():
     assert dec(q=None) == INVALID
     assert dec(kvv=PagedKVMut(FAKE, FAKE, None, FAKE, 100, 40)) == INVALID
     assert dec(wsb=ws - 1) == WORKSPACE
+
+
+def test_varlen_prefill_rejects_bad_arguments():
+    L = msa.lib()
+    p = good_params()
+    kv = fake_kv(num_pages=100, max_blocks=40)
+
+    def arr(v):
+        return ctypes.cast((ctypes.c_int32 * len(v))(*v), ctypes.c_void_p)
+
+    def st(prior, chunk, batch=None, wsb=None, host=True, q=FAKE):
+        batch = len(prior) if batch is None else batch
+        ph, ch = (arr(prior), arr(chunk)) if host else (None, None)
+        if wsb is None:
+            wsb = L.msa_prefill_varlen_workspace_bytes(ctypes.byref(p), ph, ch, batch, 40)
+        return L.msa_prefill_varlen(ctypes.byref(p), ctypes.byref(kv), q, FAKE, FAKE, FAKE, ph, ch,
+                                    batch, FAKE, None, FAKE, wsb, None)
+
+    assert st([0, 100], [10, 0]) == INVALID            # empty chunk
+    assert st([-1], [10]) == INVALID
+    assert st([5000], [200]) == INVALID               # beyond max_blocks * block_size
+    assert st([10], [10], batch=0) == INVALID
+    assert st([10], [10], host=False, wsb=1 << 20) == INVALID
+    assert st([10], [10], q=None) == INVALID
+    need = L.msa_prefill_varlen_workspace_bytes(ctypes.byref(p), arr([10, 300]), arr([5, 40]), 2, 40)
+    assert need > 0
+    assert st([10, 300], [5, 40], wsb=need - 1) == WORKSPACE
+    assert L.msa_prefill_varlen_workspace_bytes(ctypes.byref(p), arr([10]), arr([0]), 1, 40) == 0
