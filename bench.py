@@ -313,6 +313,57 @@ def run_prefill_bench(args, torch, msa, mi, gu):
             "ms_append": ms_append, "append_bytes": append_bytes}
 
 
+def run_varlen_bench(args, torch, msa, mi, gu):
+    """Batched prefill over the 32-sequence paged workload: every sequence
+    (log-uniform length in [4096, 524288], shuffled pages) prefills its last
+    args.varlen_chunk tokens in one msa_prefill_varlen call."""
+    w = mi.WORKLOADS["decode_paged_b32"]
+    lengths = mi.log_uniform_lengths(w.batch, *w.log_uniform, w.seed)
+    C = args.varlen_chunk
+    priors = [L - C for L in lengths]
+    log("[bench] generating batched prefill over decode_paged_b32 (chunk %d)" % C)
+    case = mi.make_varlen_prefill_case(w.shape, priors, [C] * w.batch, w.seed, "cuda",
+                                       shuffle_pages=True, poison_frac=w.poison_frac)
+    sh = case.shape
+    p = gu.params_of(sh)
+    c = case.cache
+    kv = msa.make_kv(c.k, c.v, c.idx_k, c.block_table)
+    rows = C * w.batch
+    out = torch.empty(rows, sh.num_q_heads, sh.head_dim, device="cuda")
+    ws = torch.empty(msa.msa_prefill_varlen_workspace_bytes(p, priors, [C] * w.batch,
+                                                            c.max_blocks),
+                     dtype=torch.uint8, device="cuda")
+    pd = torch.tensor(priors, dtype=torch.int32, device="cuda")
+    cd = torch.tensor([C] * w.batch, dtype=torch.int32, device="cuda")
+
+    def call():
+        msa.msa_prefill_varlen(p, kv, case.q, case.idx_q, pd, cd, priors, [C] * w.batch, out,
+                               None, ws)
+
+    for _ in range(args.prefill_warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.prefill_steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.prefill_steps
+    B = sh.block_size
+    pairs = 0
+    for P in priors:
+        for t in range((P + C + B - 1) // B - P // B):
+            own = P // B + t
+            q0, q1 = max(0, own * B - P), min(C, (own + 1) * B - P)
+            pairs += (q1 - q0) * own * B
+    index_flops = pairs * sh.num_kv_heads * sh.num_idx_heads * sh.idx_dim * 2
+    return {"workload": "prefill_paged_b32_c%d" % C, "sequences": w.batch, "chunk_len": C,
+            "context_tokens": sum(lengths), "ms_per_call": round(ms, 4),
+            "tokens_per_s": round(rows / (ms * 1e-3), 1),
+            "index_tflops_effective": round(index_flops / (ms * 1e-3) / 1e12, 1)}
+
+
 def cpu_baseline(case, budget_s):
     """The oracle on the host cores: whole decode steps of the same workload
     (index scores of every block, TopK, attention), repeated for about
@@ -438,6 +489,8 @@ def main():
                     help="layers of the multi-layer decode leg (0 = skip)")
     ap.add_argument("--layer-tokens", type=int, default=20,
                     help="tokens timed in the multi-layer decode leg")
+    ap.add_argument("--varlen-chunk", type=int, default=512,
+                    help="tokens per sequence of the batched prefill leg (0 = skip)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
     ap.add_argument("--summarize-kernel-trace", nargs=3, metavar=("STATS_CSV", "OUT_TXT", "CMD"),
@@ -475,6 +528,8 @@ def main():
     dec = run_decode_bench(args, torch, msa, mi, gu)
     lay = run_layers_bench(args, torch, msa, mi, dec) if args.layers > 0 else None
     pre = None if args.no_prefill else run_prefill_bench(args, torch, msa, mi, gu)
+    var = (run_varlen_bench(args, torch, msa, mi, gu)
+           if not args.no_prefill and args.varlen_chunk > 0 else None)
 
     case = dec["case"]
     sh = case.shape
@@ -538,6 +593,8 @@ def main():
         }
     if lay is not None:
         result["multi_layer_decode"] = lay
+    if var is not None:
+        result["batched_prefill"] = var
     if args.cpu_budget > 0:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     else:

@@ -238,6 +238,8 @@ __global__ __launch_bounds__(256) void index_score_prefill_kernel(
   }
 }
 
+constexpr int kPrefillMaxBlocksPerSplit = 256;
+
 hipError_t launch_index_score_prefill(const Dims& d, const Cache& c, const uint16_t* idx_q,
                                       const ChunkMap& map, int32_t num_tiles, int32_t max_own,
                                       float* pooled, hipStream_t stream) {
@@ -246,7 +248,14 @@ hipError_t launch_index_score_prefill(const Dims& d, const Cache& c, const uint1
   const int units = num_tiles * d.num_kv_heads;
   int splits = (4096 + units - 1) / units;
   if (splits > max_own) splits = max_own > 0 ? max_own : 1;
-  const int per = max_own > 0 ? (max_own + splits - 1) / splits : 1;
+  int per = max_own > 0 ? (max_own + splits - 1) / splits : 1;
+  // cap the key range of one workgroup: with tiles of very different context
+  // lengths (batched prefill) long ranges would leave a few workgroups
+  // running long after the rest
+  if (per > kPrefillMaxBlocksPerSplit) {
+    per = kPrefillMaxBlocksPerSplit;
+    splits = (max_own + per - 1) / per;
+  }
   dim3 grid(num_tiles, d.num_kv_heads, splits);
   if (B == 64)
     hipLaunchKernelGGL(index_score_prefill_kernel<64>, grid, dim3(256), 0, stream, c.idx_k,
