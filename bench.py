@@ -32,7 +32,10 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, datasheet
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, datasheet
 DECODE_WORKLOAD = "decode_b1_L1M"
 PREFILL_WORKLOAD = "prefill_P1M_C8k"
-KERNEL_SOURCES = ["block_sparse_long_10_amd/csrc/index_score.hip",
+# the sources the decode index kernel is compiled from (its counters are
+# reported only while these are unchanged)
+KERNEL_SOURCES = ["block_sparse_long_10_amd/csrc/index_decode.hip",
+                  "block_sparse_long_10_amd/csrc/index_block.h",
                   "block_sparse_long_10_amd/csrc/msa_device.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_index_score_decode_L1M.json")
 
@@ -420,19 +423,27 @@ def traffic_probe(args, torch, msa, mi, gu):
     log("[bench] traffic probe done; kernel source hash %s" % kernel_source_hash())
 
 
-def summarize_kernel_trace(stats_csv, out_txt, command):
-    """Write a short text summary of a rocprofv3 --kernel-trace --stats run."""
+def summarize_kernel_trace(trace_csv, out_txt, command):
+    """Write a short text summary of a rocprofv3 --kernel-trace run: per MSA
+    kernel and launch grid (workgroups x, y, z), the dispatch count and the
+    average / min / max duration."""
     import csv
-    rows = [r for r in csv.DictReader(open(stats_csv))]
-    lines = ["rocprofv3 kernel statistics (MSA kernels)", "", "command:", "  " + command, "",
-             "%-62s %6s %12s %12s %12s" % ("kernel", "calls", "avg us", "min us", "max us")]
-    for r in rows:
-        if "msa::" not in r["Name"]:
+    groups = {}
+    for r in csv.DictReader(open(trace_csv)):
+        if "msa::" not in r["Kernel_Name"]:
             continue
-        name = r["Name"].split("(")[0].replace("void ", "")
-        lines.append("%-62s %6s %12.3f %12.3f %12.3f" % (
-            name[:62], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
-            float(r["MaxNs"]) / 1e3))
+        name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+        wg = tuple(int(r["Grid_Size_" + a]) // max(1, int(r["Workgroup_Size_" + a]))
+                   for a in "XYZ")
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups.setdefault((name, wg), []).append(us)
+    lines = ["rocprofv3 kernel trace (MSA kernels), per kernel and launch grid", "",
+             "command:", "  " + command, "",
+             "%-44s %-18s %6s %12s %12s %12s" % ("kernel", "workgroups", "calls", "avg us",
+                                                  "min us", "max us")]
+    for (name, wg), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append("%-44s %-18s %6d %12.3f %12.3f %12.3f" % (
+            name[:44], "%dx%dx%d" % wg, len(v), sum(v) / len(v), min(v), max(v)))
     with open(out_txt, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -493,7 +504,7 @@ def main():
                     help="tokens per sequence of the batched prefill leg (0 = skip)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
-    ap.add_argument("--summarize-kernel-trace", nargs=3, metavar=("STATS_CSV", "OUT_TXT", "CMD"),
+    ap.add_argument("--summarize-kernel-trace", nargs=3, metavar=("TRACE_CSV", "OUT_TXT", "CMD"),
                     help="write the profiles/ summary of a rocprofv3 kernel-trace run")
     ap.add_argument("--summarize-traffic", nargs=4,
                     metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON", "CMD"),

@@ -1,0 +1,123 @@
+// Index branch of MSA, decode: token scores Q_idx . K_idx^T against the single
+// shared index-key head, max-pooled per KV block ("Block Max Pool"), following
+// "MiniMax wird dünn", section 1, Schritt 1.
+//
+// One pass over every cached index key of every sequence: the keys are
+// streamed from HBM exactly once, one KV block per single-wave workgroup,
+// through LDS (index_block_scores); all Hkv*n_i index-query rows of a
+// sequence (32 at 8 groups x 4 heads) are the M side of a
+// v_mfma_f32_16x16x32_bf16 so the 64-term dots run on the matrix cores and
+// the kernel stays bound by HBM.
+#include "index_block.h"
+#include "msa_device.h"
+#include "msa_launch.h"
+
+namespace msa {
+
+// ---------------------------------------------------------------- decode
+// One wave per workgroup and one block per wave (index_block_scores); small
+// single-wave workgroups let ten blocks per CU be in flight.  With an append
+// (ap.k_new != nullptr) one extra workgroup per sequence writes the current
+// token's key, value and index key into its own block's page, which the
+// index branch never reads.
+template <int B>
+__device__ __forceinline__ void append_current_token(const DecodeAppend& ap, int s, int L,
+                                                     int num_kv_heads) {
+  const int lane = threadIdx.x;
+  const int own = (L - 1) / B, slot = (L - 1) % B;
+  const size_t page = (size_t)ap.cache.block_table[(size_t)s * ap.cache.max_blocks + own];
+  const size_t kv0 = (size_t)s * num_kv_heads * 128;
+  for (int x = lane; x < num_kv_heads * 16; x += kWave) {  // K rows, 16-byte chunks
+    const int g = x >> 4, c = x & 15;
+    *reinterpret_cast<u32x4*>(ap.cache.k + ((page * num_kv_heads + g) * B + slot) * 128 + c * 8) =
+        *reinterpret_cast<const u32x4*>(ap.k_new + kv0 + g * 128 + c * 8);
+  }
+  for (int x = lane; x < num_kv_heads * 128; x += kWave) {  // V columns of the page
+    const int g = x >> 7, d = x & 127;
+    ap.cache.v[((page * num_kv_heads + g) * 128 + d) * B + slot] = ap.v_new[kv0 + x];
+  }
+  if (lane < 8)
+    *reinterpret_cast<u32x4*>(ap.cache.idx_k + (page * B + slot) * 64 + lane * 8) =
+        *reinterpret_cast<const u32x4*>(ap.idx_new + (size_t)s * 64 + lane * 8);
+}
+
+template <int B, int NI, int MT>
+__global__ __launch_bounds__(64) void index_score_decode_kernel(
+    const uint16_t* __restrict__ idx_k, const int32_t* __restrict__ block_table,
+    int32_t max_blocks, const uint16_t* __restrict__ idx_q, const int32_t* __restrict__ seq_lens,
+    int32_t num_kv_heads, float* __restrict__ pooled, uint32_t* __restrict__ counters,
+    DecodeAppend ap) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[B * 128];
+  const int s = blockIdx.y;
+  const int lane = threadIdx.x;
+  if (counters != nullptr && blockIdx.x == 0 && lane < num_kv_heads)
+    counters[s * num_kv_heads + lane] = 0u;
+  const int L = seq_lens[s];
+  // with an append, workgroup 0 (dispatched first, so its latency hides
+  // behind the scoring) writes the current token and block b is scored by
+  // workgroup b + 1
+  int b = blockIdx.x;
+  if (ap.k_new != nullptr) {
+    if (b == 0) {
+      append_current_token<B>(ap, s, L, num_kv_heads);
+      return;
+    }
+    --b;
+  }
+  const int own = (L - 1) / B;
+  if (b >= own) return;
+  float* out = pooled + (size_t)s * num_kv_heads * max_blocks + b;
+  index_block_scores<B, NI, MT>(idx_k, block_table[(size_t)s * max_blocks + b],
+                                idx_q + (size_t)s * num_kv_heads * NI * 64, num_kv_heads, stage,
+                                [&](int g, float v) { out[(size_t)g * max_blocks] = v; });
+}
+
+template <int B, int NI>
+static hipError_t launch_decode_ni(int mt, dim3 grid, hipStream_t st, const uint16_t* idx_k,
+                                   const int32_t* bt, int32_t mb, const uint16_t* idx_q,
+                                   const int32_t* sl, int32_t hkv, float* pooled,
+                                   uint32_t* ctr, const DecodeAppend& ap) {
+  switch (mt) {
+    case 1: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 1>), grid, dim3(64), 0, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr, ap); break;
+    case 2: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 2>), grid, dim3(64), 0, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr, ap); break;
+    case 3: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 3>), grid, dim3(64), 0, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr, ap); break;
+    default: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 4>), grid, dim3(64), 0, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr, ap); break;
+  }
+  return hipGetLastError();
+}
+
+template <int B>
+static hipError_t launch_decode_b(int ni, int mt, dim3 grid, hipStream_t st, const uint16_t* idx_k,
+                                  const int32_t* bt, int32_t mb, const uint16_t* idx_q,
+                                  const int32_t* sl, int32_t hkv, float* pooled,
+                                  uint32_t* ctr, const DecodeAppend& ap) {
+  switch (ni) {
+    case 1: return launch_decode_ni<B, 1>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr, ap);
+    case 2: return launch_decode_ni<B, 2>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr, ap);
+    case 4: return launch_decode_ni<B, 4>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr, ap);
+    case 8: return launch_decode_ni<B, 8>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr, ap);
+    default: return launch_decode_ni<B, 16>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr, ap);
+  }
+}
+
+hipError_t launch_index_score_decode(const Dims& d, const Cache& c, const uint16_t* idx_q,
+                                     const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                     float* pooled, uint32_t* counters, hipStream_t stream,
+                                     const DecodeAppend* append) {
+  const int B = d.block_size;
+  const int max_own = (max_seq_len - 1) / B;
+  // blocks 0 .. max_own-1 are scored; with an append, one more workgroup
+  // per sequence writes the current token
+  const int gx = append != nullptr ? max_own + 1 : (max_own > 0 ? max_own : 1);
+  DecodeAppend ap{};
+  if (append != nullptr) ap = *append;
+  const int mt = (d.num_kv_heads * d.num_idx_heads + 15) / 16;
+  dim3 grid(gx, batch);
+  if (B == 64)
+    return launch_decode_b<64>(d.num_idx_heads, mt, grid, stream, c.idx_k, c.block_table,
+                               c.max_blocks, idx_q, seq_lens, d.num_kv_heads, pooled, counters, ap);
+  return launch_decode_b<128>(d.num_idx_heads, mt, grid, stream, c.idx_k, c.block_table,
+                              c.max_blocks, idx_q, seq_lens, d.num_kv_heads, pooled, counters, ap);
+}
+
+}  // namespace msa

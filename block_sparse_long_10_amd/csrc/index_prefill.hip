@@ -1,0 +1,154 @@
+// Index branch of MSA, chunked prefill: per (tile, group) the tile's
+// queries x index heads (up to 512 rows) are held in registers as the A side
+// of v_mfma_f32_32x32x16_bf16 and every eligible key block is staged through
+// LDS (XOR-swizzled 16-byte chunks, double-buffered) as the B side; the 32x32
+// score tiles fold with v_max3 into one running max per lane and are reduced
+// across the workgroup once per block ("MiniMax wird dünn", section 1,
+// Schritt 1: Q_idx . K_idx^T, Block Max Pool; the prefill index branch still
+// scans the whole context, section 3).
+#include "chunk_map.h"
+#include "msa_device.h"
+#include "msa_launch.h"
+
+namespace msa {
+
+// --------------------------------------------------------------- prefill
+// Workgroup: 4 waves x 128 row slots (4 M tiles of 32) = 512 rows of one
+// (tile, group); rows are (query, index head) pairs, padding rows repeat row 0.
+// Keys: blocks [b_lo, b_hi) of the tile's eligible range, one block per step,
+// double-buffered in LDS.  Each wave streams a quarter of the next block with
+// 1 KB direct-to-LDS loads (lane l of a load fills token 8q + l/8, chunk slot
+// l%8 with source chunk (l%8) ^ (l/8): the XOR-swizzled image the MFMA B
+// operand reads without bank conflicts).  Per block, each wave folds its
+// 32x32 score tiles with v_max3 into one value per lane, reduces within DPP
+// rows, and one thread combines the 16 row maxima of the workgroup.
+template <int B>
+__global__ __launch_bounds__(256) void index_score_prefill_kernel(
+    const uint16_t* __restrict__ idx_k, const int32_t* __restrict__ block_table,
+    const uint16_t* __restrict__ idx_q, ChunkMap map, int32_t num_kv_heads,
+    int32_t num_idx_heads, int32_t max_blocks, int32_t blocks_per_split,
+    float* __restrict__ pooled) {
+  constexpr int NT = B / 32;                       // 32-token N tiles per block
+  constexpr int BLOCK_BYTES = B * 128;             // B tokens x 64 bf16
+  constexpr int WLOADS = BLOCK_BYTES / 1024 / 4;   // 1 KB loads per wave per block
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][BLOCK_BYTES];
+  __shared__ float wmax[2][16];
+
+  const int tile = blockIdx.x, g = blockIdx.y, split = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const TileLoc loc = locate_tile(map, tile);
+  const int own = loc.prior / B + loc.tile;
+  const int b_lo = split * blocks_per_split;
+  const int b_hi = min(b_lo + blocks_per_split, own);
+  if (b_lo >= b_hi) return;
+  const int q0 = loc.q0 + max(0, own * B - loc.prior);  // rows of q / idx_q
+  const int q1 = loc.q0 + min(loc.chunk, (own + 1) * B - loc.prior);
+  const int nrows = (q1 - q0) * num_idx_heads;
+
+  // A operand: row slot = wave*128 + mt*32 + (lane & 31); K = 64 in 4 steps of 16.
+  bf16x8 a[4][4];
+  const int half = lane >> 5;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    int r = wave * 128 + mt * 32 + (lane & 31);
+    if (r >= nrows) r = 0;
+    const int qi = q0 + r / num_idx_heads, h = r % num_idx_heads;
+    const uint16_t* p =
+        idx_q + (((size_t)qi * num_kv_heads + g) * num_idx_heads + h) * 64 + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) a[mt][ks] = load_bf16x8(p + ks * 16);
+  }
+
+  const int32_t* bt = block_table + (size_t)loc.seq * map.max_blocks;
+  const int src_off = (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) << 4);
+  auto issue = [&](int b, int buf) {
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(idx_k) + (size_t)bt[b] * BLOCK_BYTES;
+#pragma unroll
+    for (int i = 0; i < WLOADS; ++i) {
+      const int q = wave * WLOADS + i;
+      load_lds16(src + q * 1024 + src_off, &kbuf[buf][q * 1024]);
+    }
+  };
+
+  issue(b_lo, 0);
+  wait_vmem();
+  __syncthreads();
+  for (int b = b_lo; b < b_hi; ++b) {
+    const int buf = (b - b_lo) & 1;
+    // buf ^ 1 was last read in the previous step, which ended with a barrier
+    if (b + 1 < b_hi) issue(b + 1, buf ^ 1);
+    f32x16 run;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) run[v] = -INFINITY;
+#pragma unroll
+    for (int np = 0; np < NT / 2; ++np) {
+      bf16x8 bf[2][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int t = (2 * np + u) * 32 + (lane & 31);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int c = ks * 2 + half;
+          bf[u][ks] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(&kbuf[buf][t * 128 + ((c ^ (t & 7)) << 4)]));
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          acc0 = mfma32(a[mt][ks], bf[0][ks], acc0);
+          acc1 = mfma32(a[mt][ks], bf[1][ks], acc1);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) run[v] = fmaxf(fmaxf(run[v], acc0[v]), acc1[v]);
+      }
+    }
+    float m = run[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) m = fmaxf(m, run[v]);
+    m = row16_max(m);
+    if ((lane & 15) == 0) wmax[buf][wave * 4 + (lane >> 4)] = m;
+    wait_vmem();  // this wave's quarter of block b + 1 has landed
+    __syncthreads();
+    if (tid == 0) {
+      float r = wmax[buf][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) r = fmaxf(r, wmax[buf][i]);
+      pooled[((size_t)tile * num_kv_heads + g) * max_blocks + b] = r;
+    }
+  }
+}
+
+constexpr int kPrefillMaxBlocksPerSplit = 256;
+
+hipError_t launch_index_score_prefill(const Dims& d, const Cache& c, const uint16_t* idx_q,
+                                      const ChunkMap& map, int32_t num_tiles, int32_t max_own,
+                                      float* pooled, hipStream_t stream) {
+  const int B = d.block_size;
+  // split the key range so that the grid holds many workgroups per CU
+  const int units = num_tiles * d.num_kv_heads;
+  int splits = (4096 + units - 1) / units;
+  if (splits > max_own) splits = max_own > 0 ? max_own : 1;
+  int per = max_own > 0 ? (max_own + splits - 1) / splits : 1;
+  // cap the key range of one workgroup: with tiles of very different context
+  // lengths (batched prefill) long ranges would leave a few workgroups
+  // running long after the rest
+  if (per > kPrefillMaxBlocksPerSplit) {
+    per = kPrefillMaxBlocksPerSplit;
+    splits = (max_own + per - 1) / per;
+  }
+  dim3 grid(num_tiles, d.num_kv_heads, splits);
+  if (B == 64)
+    hipLaunchKernelGGL(index_score_prefill_kernel<64>, grid, dim3(256), 0, stream, c.idx_k,
+                       c.block_table, idx_q, map, d.num_kv_heads,
+                       d.num_idx_heads, c.max_blocks, per, pooled);
+  else
+    hipLaunchKernelGGL(index_score_prefill_kernel<128>, grid, dim3(256), 0, stream, c.idx_k,
+                       c.block_table, idx_q, map, d.num_kv_heads,
+                       d.num_idx_heads, c.max_blocks, per, pooled);
+  return hipGetLastError();
+}
+
+}  // namespace msa

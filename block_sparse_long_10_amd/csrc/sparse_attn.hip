@@ -25,7 +25,7 @@
 // softmax; the causal mask applies inside the tile's diagonal block only.
 #include "block_topk.h"
 #include "chunk_map.h"
-#include "decode_parts.h"
+#include "decode_attend.h"
 #include "msa_device.h"
 #include "msa_launch.h"
 
