@@ -516,7 +516,12 @@ __device__ __forceinline__ void topk_select(const Src& src, int own, int k, int*
   topk_write_sorted(sh, min(sh.n_chosen, keep), own, k, out_sel);
 }
 
-// TopK of scores[0 .. own) held in global memory.
+// TopK of scores[0 .. own) held in global memory.  Up to 8192 candidates
+// live in registers (32 per thread); WIDE kernels also keep up to 16384 there
+// (64 per thread), otherwise longer rows are re-read from memory.  Each
+// register variant is a separate copy of the selection code, so kernels on a
+// latency-critical path keep only the one they need.
+template <bool WIDE>
 __device__ __forceinline__ void block_topk(const float* __restrict__ scores, int own, int k,
                                            int* out_sel, TopkShared& sh) {
   const int keep = min(k - 1, own);
@@ -527,7 +532,7 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ scores, int
     RegKeys<32> src;
     src.load(scores, own);
     if (!topk_fast(src, own, keep, k, out_sel, sh)) topk_select(src, own, k, out_sel, sh);
-  } else if (own <= kTopkThreads * 64) {
+  } else if (WIDE && own <= kTopkThreads * 64) {
     RegKeys<64> src;
     src.load(scores, own);
     if (!topk_fast(src, own, keep, k, out_sel, sh)) topk_select(src, own, k, out_sel, sh);
@@ -540,21 +545,21 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ scores, int
 // TopK with forced blocks: blocks [0, n_sink) and the n_local blocks just
 // before the own block are kept unranked and count toward k; the other
 // eligible blocks form the contiguous range [lo, hi), ranked by block_topk as
-// if hi were the own block with a budget of k - (number forced).  tmp is an
-// LDS array of kMaxTopK entries.  Result as block_topk's (ascending, own
-// block included, -1 padded).
+// if hi were the own block with a budget of k - (number forced).  Without
+// forced blocks that is the plain selection, written straight to out_sel (one
+// copy of the selection code either way).  tmp is an LDS array of kMaxTopK
+// entries.  Result as block_topk's (ascending, own block included, -1
+// padded).
+template <bool WIDE>
 __device__ __forceinline__ void block_topk_forced(const float* __restrict__ scores, int own, int k,
                                                   int n_sink, int n_local, int* out_sel,
                                                   int* tmp, TopkShared& sh) {
-  if (n_sink == 0 && n_local == 0) {
-    block_topk(scores, own, k, out_sel, sh);
-    return;
-  }
   const int lo = min(n_sink, own);
   const int hi = max(own - n_local, lo);
   const int forced = lo + (own - hi);
-  const int kr = k - forced;                 // >= 1: the host checks sink + local <= k - 1
-  block_topk(scores + lo, hi - lo, kr, tmp, sh);
+  const int kr = k - forced;  // >= 1: the host checks sink + local <= k - 1
+  block_topk<WIDE>(scores + lo, hi - lo, kr, forced == 0 ? out_sel : tmp, sh);
+  if (forced == 0) return;  // uniform
   const int chosen = min(kr - 1, hi - lo);  // tmp[0 .. chosen) are relative block ids
   for (int i = threadIdx.x; i < k; i += kTopkThreads) {
     int b;

@@ -17,7 +17,7 @@ __global__ __launch_bounds__(256) void block_topk_prefill_kernel(
   const int tile = blockIdx.x, g = blockIdx.y;
   const TileLoc loc = locate_tile(map, tile);
   const size_t row = (size_t)tile * num_kv_heads + g;
-  block_topk_forced(pooled + row * max_blocks, loc.prior / B + loc.tile, top_k, n_sink, n_local,
+  block_topk_forced<true>(pooled + row * max_blocks, loc.prior / B + loc.tile, top_k, n_sink, n_local,
                     sel_s, tmp_s, sh);
   for (int i = threadIdx.x; i < top_k; i += blockDim.x) sel[row * top_k + i] = sel_s[i];
 }

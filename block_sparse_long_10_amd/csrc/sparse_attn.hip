@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(const float* __restric
   __shared__ int sel_s[kMaxTopK], tmp_s[kMaxTopK];
   const int g = blockIdx.x, s = blockIdx.y;
   const size_t sg = (size_t)s * num_kv_heads + g;
-  block_topk_forced(pooled + sg * max_blocks, (seq_lens[s] - 1) / B, top_k, n_sink, n_local, sel_s,
+  block_topk_forced<false>(pooled + sg * max_blocks, (seq_lens[s] - 1) / B, top_k, n_sink, n_local, sel_s,
                     tmp_s, sh);
   for (int i = threadIdx.x; i < top_k; i += 256) sel[sg * top_k + i] = sel_s[i];
 }
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
   const size_t sg = (size_t)s * num_kv_heads + g;
   int blk;
   if constexpr (FUSED_TOPK) {
-    block_topk_forced(pooled + sg * max_blocks, (L - 1) / B, top_k, n_sink, n_local, sel_s, tmp_s,
+    block_topk_forced<false>(pooled + sg * max_blocks, (L - 1) / B, top_k, n_sink, n_local, sel_s, tmp_s,
                       tsh);
     if (slot == 0)
       for (int i = tid; i < top_k; i += 256) sel[sg * top_k + i] = sel_s[i];
