@@ -83,23 +83,29 @@ __device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
   return umin_(v, (uint32_t)__shfl_xor((int)v, 32, kWave));
 }
 
-// Keys held in registers: item i = j*256 + tid lives in key[j].
+// Inverse of order_key for keys of finite floats (-0.0 comes back as +0.0).
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+constexpr uint32_t kKeyMinFinite = 0x00800000u;  // order_key(-FLT_MAX); -inf maps below it
+
+// Scores held in registers: item i = j*256 + tid lives in val[j] (-inf in
+// the slots past the row).  The fast path compares the floats themselves;
+// keys are formed only for thread maxima and candidates, and by the general
+// path through each() / chunks_in_order().
 template <int MAXV>
 struct RegKeys {
   static constexpr int kChunks = MAXV;
-  uint32_t key[MAXV];
+  float val[MAXV];
   int n;
   __device__ __forceinline__ void load(const float* __restrict__ s, int n_) {
     n = n_;
     const int tid = threadIdx.x;
-    float v[MAXV];
 #pragma unroll
     for (int j = 0; j < MAXV; ++j) {
       const int i = j * kTopkThreads + tid;
-      v[j] = i < n ? s[i] : 0.f;
+      val[j] = i < n ? s[i] : -INFINITY;
     }
-#pragma unroll
-    for (int j = 0; j < MAXV; ++j) key[j] = j * kTopkThreads + tid < n ? order_key(v[j]) : 0u;
   }
   template <class F>
   __device__ __forceinline__ void each(F&& f) const {
@@ -107,7 +113,7 @@ struct RegKeys {
 #pragma unroll
     for (int j = 0; j < MAXV; ++j) {
       const int i = j * kTopkThreads + tid;
-      if (i < n) f(i, key[j]);
+      if (i < n) f(i, order_key(val[j]));
     }
   }
   // f(i, key, valid) for chunks of 256 consecutive items in index order,
@@ -118,7 +124,7 @@ struct RegKeys {
 #pragma unroll
     for (int j = 0; j < MAXV; ++j) {
       const int i = j * kTopkThreads + tid;
-      if (!f(i, key[j], i < n)) break;
+      if (!f(i, i < n ? order_key(val[j]) : 0u, i < n)) break;
     }
   }
 };
@@ -305,15 +311,16 @@ template <int MAXV>
 __device__ __forceinline__ bool topk_fast(const RegKeys<MAXV>& src, int own, int keep, int k,
                                           int* out_sel, TopkShared& sh) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  // thread max (tree) and the range of the 256 thread maxima
-  uint32_t mx[MAXV];
+  // thread max (tree, on the floats; slots past the row hold -inf) and the
+  // range of the 256 thread maxima as keys
+  float mx[MAXV];
 #pragma unroll
-  for (int j = 0; j < MAXV; ++j) mx[j] = src.key[j];
+  for (int j = 0; j < MAXV; ++j) mx[j] = src.val[j];
 #pragma unroll
   for (int w = MAXV / 2; w >= 1; w /= 2)
 #pragma unroll
-    for (int j = 0; j < w; ++j) mx[j] = umax_(mx[j], mx[j + w]);
-  const uint32_t m = mx[0];
+    for (int j = 0; j < w; ++j) mx[j] = fmaxf(mx[j], mx[j + w]);
+  const uint32_t m = order_key(mx[0]);
   const uint32_t wmax = wave_umax(m), wmin = wave_umin(m);
   if (lane == 0) {
     sh.red_a[wave] = wmax;
@@ -356,11 +363,14 @@ __device__ __forceinline__ bool topk_fast(const RegKeys<MAXV>& src, int own, int
   }
   __syncthreads();
   const uint32_t edge = ((uint32_t)(sh.bstar + 1) << shift) - 1u;  // hi - key <= edge
-  const uint32_t t = umax_(hi - umin_(edge, hi - 1u), 1u);        // key 0 marks empty slots
-  // count, scan and gather the keys >= t
+  // the bound as a float (at least -FLT_MAX, so the -inf of empty slots
+  // never reaches it): key >= t  <=>  score >= tf for finite scores
+  const uint32_t t = umax_(hi - umin_(edge, hi - kKeyMinFinite), kKeyMinFinite);
+  const float tf = key_float(t);
+  // count, scan and gather the scores >= tf
   int cnt = 0;
 #pragma unroll
-  for (int j = 0; j < MAXV; ++j) cnt += src.key[j] >= t;
+  for (int j = 0; j < MAXV; ++j) cnt += src.val[j] >= tf;
   const int incl = wave_incl_scan(cnt);
   if (lane == kWave - 1) sh.wave_cnt[wave] = incl;
   __syncthreads();
@@ -374,8 +384,8 @@ __device__ __forceinline__ bool topk_fast(const RegKeys<MAXV>& src, int own, int
   if (total > kWave) return false;  // uniform
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
-    if (src.key[j] >= t) {
-      sh.cand_k[base] = src.key[j];
+    if (src.val[j] >= tf) {
+      sh.cand_k[base] = order_key(src.val[j]);
       sh.cand_i[base] = j * kTopkThreads + tid;
       ++base;
     }

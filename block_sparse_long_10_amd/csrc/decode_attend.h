@@ -10,6 +10,7 @@
 namespace msa {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxSlots = 64;  // top_k <= 64
 
 // Cross-workgroup hand-off without a cache write-back: every value another
 // workgroup reads is written with an agent-scope (sc1) store, which writes
@@ -60,9 +61,12 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ kc,
                                              int slot, __amdgpu_buffer_rsrc_t ro,
                                              __amdgpu_buffer_rsrc_t rml, AttendShared& sh) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  if (blk < 0) {
+  if (blk < 0) {  // empty slot: weight zero in the merge, output zeros
     for (int h = tid; h < group; h += 256)
       store_shared4(rml, (slot * group + h) * 16, f32x4{-INFINITY, 0.f, 0.f, 0.f});
+    for (int x = tid; x < group * 32; x += 256)
+      store_shared4(ro, ((slot * group + (x >> 5)) * 128 + 4 * (x & 31)) * 4,
+                    f32x4{0.f, 0.f, 0.f, 0.f});
     return;
   }
   const int n_valid = min(B, L - blk * B);
@@ -168,51 +172,81 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ kc,
 }
 
 // Log-sum-exp merge of the top_k partials of one (sequence, group) into
-// out_sg[h*128 ..] (256 threads): thread -> (head h, dims 4*d4 .. +3); the
-// partial loads of 16 slots are issued together and folded into a running
-// (max, sum, output).
+// out_sg[h*128 ..] (256 threads).  Every thread first issues the loads of its
+// (head h, dims 4*d4 .. +3) partial outputs, 16 slots at a time; meanwhile the
+// weights e^(m_k - M) / sum_k e^(m_k - M) l_k of every (head, slot) are
+// formed once in LDS, so the fold is one multiply-add per partial value.
+// Empty slots carry m = -inf (weight 0) and zero outputs.
+struct MergeShared {
+  float m[16][kMaxSlots], l[16][kMaxSlots];
+  float w[16][kMaxSlots];
+};
+
 __device__ __forceinline__ void merge_partials(__amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rml,
-                                               int top_k, int group, float* __restrict__ out_sg) {
+                                               int top_k, int group, float* __restrict__ out_sg,
+                                               MergeShared& ms) {
   constexpr int kChunk = 16;
-  for (int idx = threadIdx.x; idx < group * 32; idx += 256) {
-    const int h = idx >> 5, d4 = idx & 31;
-    float M = -INFINITY, den = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < top_k; k0 += kChunk) {
-      float m[kChunk], l[kChunk];
-      f32x4 o[kChunk];
-      // no branches around the loads (a join would wait for them): slots
-      // past top_k read beyond the buffer range, which returns zeros, and
-      // are masked afterwards
+  const int tid = threadIdx.x;
+  // item = (head h, dims 4*d4 .. +3): group*32 of them, one or two per thread
+  const int items = group * 32;
+  f32x4 o[kChunk];
+  // the first chunk of the thread's first item is loaded while the weights
+  // are formed (slots past top_k read beyond the buffer range: zeros)
+  {
+    const int h = tid >> 5, d4 = tid & 31;
 #pragma unroll
-      for (int k = 0; k < kChunk; ++k) {
-        const f32x4 v = load_shared4(rml, ((k0 + k) * group + h) * 16);
-        o[k] = load_shared4(ro, (((k0 + k) * group + h) * 128 + 4 * d4) * 4);
-        m[k] = k0 + k < top_k ? v[0] : -INFINITY;
-        l[k] = v[1];
-      }
-      // branch-free fold (selects, not products: an empty slot's partial
-      // output is stale memory)
-      float Mc = M;
-#pragma unroll
-      for (int k = 0; k < kChunk; ++k) Mc = fmaxf(Mc, m[k]);
-      const float r = M == -INFINITY ? 0.f : exp2f(M - Mc);
-      den *= r;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] *= r;
-#pragma unroll
-      for (int k = 0; k < kChunk; ++k) {
-        const bool live = m[k] != -INFINITY;
-        const float e = exp2f(live ? m[k] - Mc : -INFINITY);
-        den = live ? den + e * l[k] : den;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = live ? acc[j] + e * o[k][j] : acc[j];
-      }
-      M = Mc;
+    for (int k = 0; k < kChunk; ++k)
+      o[k] = load_shared4(ro, ((k * group + h) * 128 + 4 * d4) * 4);
+  }
+  for (int x = tid; x < group * top_k; x += 256) {
+    const int hh = x / top_k, k = x - hh * top_k;
+    const f32x4 v = load_shared4(rml, (k * group + hh) * 16);
+    ms.m[hh][k] = v[0];
+    ms.l[hh][k] = v[1];
+  }
+  __syncthreads();
+  if (tid < group) {
+    float M = -INFINITY;
+    for (int k = 0; k < top_k; ++k) M = fmaxf(M, ms.m[tid][k]);
+    float den = 0.f;
+    for (int k = 0; k < top_k; ++k) {
+      const float e = exp2f(ms.m[tid][k] - M);  // 0 for an empty slot
+      ms.w[tid][k] = e;
+      den += e * ms.l[tid][k];
     }
     const float inv = 1.f / den;
-    *reinterpret_cast<f32x4*>(out_sg + (size_t)h * 128 + 4 * d4) =
-        f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    for (int k = 0; k < top_k; ++k) ms.w[tid][k] *= inv;
+  }
+  __syncthreads();
+  auto fold = [&](int h, int k0, f32x4& acc) {
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) {
+      const float w = k0 + k < top_k ? ms.w[h][k0 + k] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = fmaf(w, o[k][j], acc[j]);
+    }
+  };
+  auto reload = [&](int h, int d4, int k0) {
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k)
+      o[k] = load_shared4(ro, (((k0 + k) * group + h) * 128 + 4 * d4) * 4);
+  };
+  if (items <= 256 && top_k <= kChunk) {  // one item and one chunk per thread (uniform)
+    if (tid >= items) return;
+    const int h = tid >> 5, d4 = tid & 31;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    fold(h, 0, acc);
+    *reinterpret_cast<f32x4*>(out_sg + (size_t)h * 128 + 4 * d4) = acc;
+    return;
+  }
+  for (int it = tid; it < items; it += 256) {
+    const int h = it >> 5, d4 = it & 31;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < top_k; k0 += kChunk) {
+      if (k0 > 0 || it != tid) reload(h, d4, k0);
+      fold(h, k0, acc);
+    }
+    *reinterpret_cast<f32x4*>(out_sg + (size_t)h * 128 + 4 * d4) = acc;
   }
 }
 

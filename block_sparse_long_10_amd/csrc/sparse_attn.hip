@@ -64,7 +64,13 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
     float* __restrict__ part_ml, uint32_t* __restrict__ counters, float* __restrict__ out) {
   __shared__ TopkShared tsh;
   __shared__ int sel_s[kMaxTopK], tmp_s[kMaxTopK];
-  __shared__ AttendShared ash;
+  // the merge runs after the block attention is done with its scratch
+  __shared__ union {
+    AttendShared ash;
+    MergeShared msh;
+  } scratch;
+  AttendShared& ash = scratch.ash;
+  MergeShared& msh = scratch.msh;
   __shared__ int is_last;
 
   const int slot = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
@@ -101,7 +107,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
                                      __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(top_k - 1);
   __syncthreads();
   if (!is_last) return;
-  merge_partials(ro, rml, top_k, group, out + ((size_t)s * Hq + (size_t)g * group) * 128);
+  merge_partials(ro, rml, top_k, group, out + ((size_t)s * Hq + (size_t)g * group) * 128, msh);
 }
 
 // Slot workgroups beyond which TopK runs in its own launch instead of being
