@@ -175,7 +175,8 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ kc,
 // out_sg[h*128 ..] (256 threads).  Every thread first issues the loads of its
 // (head h, dims 4*d4 .. +3) partial outputs, 16 slots at a time; meanwhile the
 // weights e^(m_k - M) / sum_k e^(m_k - M) l_k of every (head, slot) are
-// formed once in LDS, so the fold is one multiply-add per partial value.
+// formed once in LDS (up to 16 slots: one lane per (head, slot), reduced
+// within DPP rows), so the fold is one multiply-add per partial value.
 // Empty slots carry m = -inf (weight 0) and zero outputs.
 struct MergeShared {
   float m[16][kMaxSlots], l[16][kMaxSlots];
@@ -198,24 +199,40 @@ __device__ __forceinline__ void merge_partials(__amdgpu_buffer_rsrc_t ro, __amdg
     for (int k = 0; k < kChunk; ++k)
       o[k] = load_shared4(ro, ((k * group + h) * 128 + 4 * d4) * 4);
   }
-  for (int x = tid; x < group * top_k; x += 256) {
-    const int hh = x / top_k, k = x - hh * top_k;
+  if (top_k <= 16) {  // uniform: lane (h, k) of a DPP row of 16 forms weight (h, k)
+    const int hh = tid >> 4, k = tid & 15;
+    const bool live = hh < group && k < top_k;
+    // (rows past the group or slots past top_k read beyond the range: zeros)
     const f32x4 v = load_shared4(rml, (k * group + hh) * 16);
-    ms.m[hh][k] = v[0];
-    ms.l[hh][k] = v[1];
-  }
-  __syncthreads();
-  if (tid < group) {
-    float M = -INFINITY;
-    for (int k = 0; k < top_k; ++k) M = fmaxf(M, ms.m[tid][k]);
-    float den = 0.f;
-    for (int k = 0; k < top_k; ++k) {
-      const float e = exp2f(ms.m[tid][k] - M);  // 0 for an empty slot
-      ms.w[tid][k] = e;
-      den += e * ms.l[tid][k];
+    const float m = live ? v[0] : -INFINITY;
+    const float M = row16_max(m);
+    const float e = live ? exp2f(m - M) : 0.f;  // 0 for an empty slot
+    float den = e * v[1];
+    den += row_ror<8>(den);
+    den += row_ror<4>(den);
+    den += row_ror<2>(den);
+    den += row_ror<1>(den);
+    if (live) ms.w[hh][k] = e / den;
+  } else {
+    for (int x = tid; x < group * top_k; x += 256) {
+      const int hh = x / top_k, k = x - hh * top_k;
+      const f32x4 v = load_shared4(rml, (k * group + hh) * 16);
+      ms.m[hh][k] = v[0];
+      ms.l[hh][k] = v[1];
     }
-    const float inv = 1.f / den;
-    for (int k = 0; k < top_k; ++k) ms.w[tid][k] *= inv;
+    __syncthreads();
+    if (tid < group) {
+      float M = -INFINITY;
+      for (int k = 0; k < top_k; ++k) M = fmaxf(M, ms.m[tid][k]);
+      float den = 0.f;
+      for (int k = 0; k < top_k; ++k) {
+        const float e = exp2f(ms.m[tid][k] - M);  // 0 for an empty slot
+        ms.w[tid][k] = e;
+        den += e * ms.l[tid][k];
+      }
+      const float inv = 1.f / den;
+      for (int k = 0; k < top_k; ++k) ms.w[tid][k] *= inv;
+    }
   }
   __syncthreads();
   auto fold = [&](int h, int k0, f32x4& acc) {
