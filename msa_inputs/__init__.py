@@ -26,7 +26,8 @@ Paged layout (one page = one KV block of ``block_size`` tokens)
 ---------------------------------------------------------------
 * ``k``     bf16 ``[num_pages][Hkv][B][D]``   (token-major keys)
 * ``v``     bf16 ``[num_pages][Hkv][D][B]``   (values transposed within a page)
-* ``idx_k`` bf16 ``[num_pages][B][d_i]``      (one index-key head shared by all groups)
+* ``idx_k`` bf16 ``[num_pages][B][d_i]``      (one index-key head shared by all groups;
+  ``[num_pages][Hkv][B][d_i]`` when the shape asks for one head per group)
 * ``block_table`` int32 ``[batch][max_blocks]``: logical block -> physical page
 Pages never referenced by a block table ("poison pages") and the slots past a
 sequence's last token are filled with ``POISON`` so that any read outside the
@@ -61,6 +62,7 @@ class Shape:
     scale: Optional[float] = None  # softmax scale; None means 1/sqrt(head_dim)
     sink_blocks: int = 0           # blocks always kept from the start of the sequence
     local_blocks: int = 0          # blocks always kept just before the own block
+    idx_k_heads: int = 1           # index-key heads: 1 (shared) or num_kv_heads (per group)
 
     @property
     def group_size(self) -> int:
@@ -188,7 +190,11 @@ def build_paged_cache(shape: Shape, lengths: Sequence[int], seed: int,
     Hkv, D, di = shape.num_kv_heads, shape.head_dim, shape.idx_dim
     k = normal_bf16((num_pages, Hkv, B, D), seed, TENSOR_IDS["k"], device)
     v = normal_bf16((num_pages, Hkv, D, B), seed, TENSOR_IDS["v"], device)
-    idx_k = normal_bf16((num_pages, B, di), seed, TENSOR_IDS["idx_k"], device)
+    if shape.idx_k_heads > 1:
+        idx_k = normal_bf16((num_pages, shape.idx_k_heads, B, di), seed, TENSOR_IDS["idx_k"],
+                            device)
+    else:
+        idx_k = normal_bf16((num_pages, B, di), seed, TENSOR_IDS["idx_k"], device)
     if n_poison:
         pp = torch.as_tensor(poison_pages, dtype=torch.long, device=k.device)
         k[pp] = POISON
@@ -200,7 +206,7 @@ def build_paged_cache(shape: Shape, lengths: Sequence[int], seed: int,
             page = int(table[s, nblocks[s] - 1])
             k[page, :, tail:, :] = POISON
             v[page, :, :, tail:] = POISON
-            idx_k[page, tail:, :] = POISON
+            idx_k[page, ..., tail:, :] = POISON
     return PagedCache(k=k, v=v, idx_k=idx_k,
                       block_table=torch.from_numpy(table).to(k.device),
                       num_pages=num_pages, max_blocks=max_blocks,
@@ -237,7 +243,10 @@ def shift_blocks(shape: Shape, cache: PagedCache, idx_q: torch.Tensor,
             u = _unit(idx_q[s, g].float().sum(0))
             w = _unit(q[s, g * G:(g + 1) * G].float().sum(0))
             pages = cache.block_table[s, blocks].long()
-            cache.idx_k[pages] = (cache.idx_k[pages].float() + 2.0 * u).to(torch.bfloat16)
+            if cache.idx_k.dim() == 4:  # per-group index keys: this group's head only
+                cache.idx_k[pages, g] = (cache.idx_k[pages, g].float() + 2.0 * u).to(torch.bfloat16)
+            else:
+                cache.idx_k[pages] = (cache.idx_k[pages].float() + 2.0 * u).to(torch.bfloat16)
             cache.k[pages, g] = (cache.k[pages, g].float() + 2.0 * w).to(torch.bfloat16)
     return chosen
 

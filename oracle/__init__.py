@@ -37,7 +37,8 @@ class _Params(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("num_idx_heads", ctypes.c_int32),
                 ("idx_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("softmax_scale", ctypes.c_double),
-                ("sink_blocks", ctypes.c_int32), ("local_blocks", ctypes.c_int32)]
+                ("sink_blocks", ctypes.c_int32), ("local_blocks", ctypes.c_int32),
+                ("num_idx_k_heads", ctypes.c_int32)]
 
 
 class _Cache(ctypes.Structure):
@@ -114,7 +115,7 @@ class _Prepared:
         sh, cache = case.shape, case.cache
         self.params = _Params(sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.num_idx_heads,
                               sh.idx_dim, sh.block_size, sh.top_k, sh.softmax_scale,
-                              sh.sink_blocks, sh.local_blocks)
+                              sh.sink_blocks, sh.local_blocks, sh.idx_k_heads)
         if kv_pages is None:
             self.k = _host_u16(cache.k)
             self.v = _host_u16(cache.v)
@@ -270,12 +271,14 @@ def cache_append(shape, k: np.ndarray, v: np.ndarray, idx_k: np.ndarray, block_t
                  k_new, v_new, idx_new, start_pos) -> None:
     """Oracle cache append, in place on host arrays of bfloat16 bits (int16).
 
-    k [P][Hkv][B][D], v [P][Hkv][D][B], idx_k [P][B][d_i]; k_new, v_new
-    [batch][n_new][Hkv][D] and idx_new [batch][n_new][d_i] (tensors or
+    k [P][Hkv][B][D], v [P][Hkv][D][B], idx_k [P][B][d_i] (or [P][Hkv][B][d_i]
+    with per-group index keys); k_new, v_new [batch][n_new][Hkv][D] and
+    idx_new [batch][n_new][d_i] (or [batch][n_new][Hkv][d_i]) (tensors or
     arrays); start_pos [batch]: position of each sequence's first new token.
     """
     params = _Params(shape.num_q_heads, shape.num_kv_heads, shape.head_dim, shape.num_idx_heads,
-                     shape.idx_dim, shape.block_size, shape.top_k, shape.softmax_scale)
+                     shape.idx_dim, shape.block_size, shape.top_k, shape.softmax_scale,
+                     shape.sink_blocks, shape.local_blocks, shape.idx_k_heads)
     for a in (k, v, idx_k):
         assert a.dtype == np.int16 and a.flags["C_CONTIGUOUS"]
     bt = _host_i32(block_table)

@@ -28,6 +28,9 @@
  *   - blocks are ranked by (score descending, block index ascending);
  *   - query head j belongs to group j / (Hq / Hkv);
  *   - the index lists are returned sorted ascending, padded with -1;
+ *   - optional per-group index keys (num_idx_k_heads = Hkv, the ablation of
+ *     the single shared index-key head): group g scores its blocks against
+ *     its own index-key head g; 0 or 1 means the one shared head;
  *   - optional forced blocks (section 2: the dropped sliding-window branch is
  *     probably replaced by an attention sink or local attention): the first
  *     sink_blocks blocks and the local_blocks blocks just before the own
@@ -42,7 +45,8 @@
  * Paged cache layout (page = one block of B tokens):
  *   k      [num_pages][Hkv][B][D]      keys, token-major
  *   v      [num_pages][Hkv][D][B]      values, transposed within the page
- *   idx_k  [num_pages][B][d_i]         the single shared index-key head
+ *   idx_k  [num_pages][Hk][B][d_i]     index keys, Hk = 1 (the single shared
+ *                                      head) or Hkv (one head per group)
  *   block_table [batch][max_blocks]    logical block -> physical page
  */
 #include <math.h>
@@ -57,6 +61,7 @@ typedef struct {
   int32_t block_size, top_k;
   double softmax_scale;
   int32_t sink_blocks, local_blocks;  /* forced blocks (0, 0: none) */
+  int32_t num_idx_k_heads;            /* 0 or 1: one shared head; Hkv: one per group */
 } oracle_params;
 
 typedef struct {
@@ -90,11 +95,16 @@ static double value_at(const oracle_params *p, const oracle_cache *c, int32_t se
   return bf(c->v[((pg * H + g) * D + d) * B + t % B]);
 }
 
+static int32_t idx_k_heads(const oracle_params *p) {
+  return p->num_idx_k_heads > 1 ? p->num_idx_k_heads : 1;
+}
+
 static double index_key_at(const oracle_params *p, const oracle_cache *c,
-                           int32_t seq, int64_t t, int32_t d) {
-  const int32_t B = p->block_size, di = p->idx_dim;
+                           int32_t seq, int32_t g, int64_t t, int32_t d) {
+  const int32_t B = p->block_size, di = p->idx_dim, Hk = idx_k_heads(p);
+  const int32_t head = Hk > 1 ? g : 0;
   int64_t pg = page_of(c, seq, t, B);
-  return bf(c->idx_k[(pg * B + t % B) * di + d]);
+  return bf(c->idx_k[((pg * Hk + head) * B + t % B) * di + d]);
 }
 
 /*
@@ -112,7 +122,7 @@ static double block_score(const oracle_params *p, const oracle_cache *c,
   double *key = (double *)malloc(sizeof(double) * (size_t)B * di);
   double *qry = (double *)malloc(sizeof(double) * (size_t)(nrows > 0 ? nrows : 1) * di);
   for (int32_t r = 0; r < B; r++)
-    for (int32_t d = 0; d < di; d++) key[r * di + d] = index_key_at(p, c, seq, b * B + r, d);
+    for (int32_t d = 0; d < di; d++) key[r * di + d] = index_key_at(p, c, seq, g, b * B + r, d);
   for (int64_t i = q0; i < q1; i++)
     for (int32_t h = 0; h < ni; h++)
       for (int32_t d = 0; d < di; d++)
@@ -223,6 +233,7 @@ static int check(const oracle_params *p, const oracle_cache *c) {
     return -1;
   if (p->sink_blocks < 0 || p->local_blocks < 0 || p->sink_blocks + p->local_blocks > p->top_k - 1)
     return -1;
+  if (p->num_idx_k_heads > 1 && p->num_idx_k_heads != p->num_kv_heads) return -1;
   return 0;
 }
 
@@ -446,7 +457,8 @@ int msa_oracle_block_scores(const oracle_params *p, const oracle_cache *c, int32
  * section 1 "Schritt 1"; the real K/V are kept, section 2).  Token i of
  * sequence s sits at position t = start[s] + i and is stored in page
  * block_table[s][t / B], slot t % B, in the layouts above:
- *   k_new, v_new [batch][n_new][Hkv][D], idx_new [batch][n_new][d_i].
+ *   k_new, v_new [batch][n_new][Hkv][D], idx_new [batch][n_new][Hk][d_i]
+ *   (Hk index-key heads, 1 for the shared head).
  * The cache arrays are written in place; nothing else changes.
  */
 int msa_oracle_append(const oracle_params *p, uint16_t *k, uint16_t *v, uint16_t *idx_k,
@@ -454,6 +466,7 @@ int msa_oracle_append(const oracle_params *p, uint16_t *k, uint16_t *v, uint16_t
                       const uint16_t *v_new, const uint16_t *idx_new, const int32_t *start,
                       int32_t batch, int32_t n_new) {
   const int32_t B = p->block_size, D = p->head_dim, H = p->num_kv_heads, di = p->idx_dim;
+  const int32_t Hk = idx_k_heads(p);
   if (batch < 1 || n_new < 1 || B < 1) return -1;
   for (int32_t s = 0; s < batch; ++s) {
     for (int32_t i = 0; i < n_new; ++i) {
@@ -468,7 +481,9 @@ int msa_oracle_append(const oracle_params *p, uint16_t *k, uint16_t *v, uint16_t
           v[((pg * H + g) * D + d) * B + slot] = v_new[(src * H + g) * D + d];
         }
       }
-      for (int32_t d = 0; d < di; ++d) idx_k[(pg * B + slot) * di + d] = idx_new[src * di + d];
+      for (int32_t h = 0; h < Hk; ++h)
+        for (int32_t d = 0; d < di; ++d)
+          idx_k[((pg * Hk + h) * B + slot) * di + d] = idx_new[(src * Hk + h) * di + d];
     }
   }
   return 0;

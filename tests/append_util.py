@@ -18,12 +18,16 @@ def token_rows(cache, shape, seq: int, positions):
     slots = pos % B
     k = cache.k[pages, :, slots, :]
     v = cache.v[pages, :, :, slots]
-    idx = cache.idx_k[pages, slots, :]
+    if cache.idx_k.dim() == 4:  # per-group index keys: [n][Hkv][d_i]
+        idx = cache.idx_k[pages, :, slots, :]
+    else:
+        idx = cache.idx_k[pages, slots, :]
     return k.contiguous(), v.contiguous(), idx.contiguous()
 
 
 def new_token_batch(cache, shape, starts, n_new):
-    """k_new, v_new [batch][n_new][Hkv][D], idx_new [batch][n_new][d_i] holding the tokens
+    """k_new, v_new [batch][n_new][Hkv][D], idx_new [batch][n_new][d_i] (or
+    [batch][n_new][Hkv][d_i] with per-group index keys) holding the tokens
     start[s] .. start[s]+n_new-1 of every sequence."""
     rows = [token_rows(cache, shape, s, range(st, st + n_new)) for s, st in enumerate(starts)]
     return (torch.stack([r[0] for r in rows]), torch.stack([r[1] for r in rows]),
@@ -41,7 +45,10 @@ def holed_copy(cache, shape, starts, n_new):
         slots = pos % B
         c.k[pages, :, slots, :] = POISON
         c.v[pages, :, :, slots] = POISON
-        c.idx_k[pages, slots, :] = POISON
+        if c.idx_k.dim() == 4:
+            c.idx_k[pages, :, slots, :] = POISON
+        else:
+            c.idx_k[pages, slots, :] = POISON
     return c
 
 

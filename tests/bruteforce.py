@@ -17,17 +17,21 @@ def f64(t: torch.Tensor) -> np.ndarray:
 
 
 def logical(case, s: int, length: int):
-    """Gather sequence s's first ``length`` tokens: K,V [Hkv][L][D], IK [L][d_i]."""
+    """Gather sequence s's first ``length`` tokens: K,V [Hkv][L][D], IK [L][d_i]
+    (IK [Hkv][L][d_i] with per-group index keys)."""
     sh, cache = case.shape, case.cache
     B = sh.block_size
     nb = (length + B - 1) // B
     pages = cache.block_table[s, :nb].cpu().numpy().astype(np.int64)
     k = f64(cache.k)[pages]                      # [nb][Hkv][B][D]
     v = f64(cache.v)[pages]                      # [nb][Hkv][D][B]
-    ik = f64(cache.idx_k)[pages]                 # [nb][B][d_i]
+    ik = f64(cache.idx_k)[pages]                 # [nb][B][d_i] or [nb][Hkv][B][d_i]
     K = k.transpose(1, 0, 2, 3).reshape(sh.num_kv_heads, nb * B, sh.head_dim)[:, :length]
     V = v.transpose(1, 0, 3, 2).reshape(sh.num_kv_heads, nb * B, sh.head_dim)[:, :length]
-    IK = ik.reshape(nb * B, sh.idx_dim)[:length]
+    if ik.ndim == 4:
+        IK = ik.transpose(1, 0, 2, 3).reshape(ik.shape[1], nb * B, sh.idx_dim)[:, :length]
+    else:
+        IK = ik.reshape(nb * B, sh.idx_dim)[:length]
     return K, V, IK
 
 
@@ -69,7 +73,7 @@ def decode(case):
         K, V, IK = logical(case, s, L)
         own = (L - 1) // B
         qi = f64(case.idx_q[s])                          # [Hkv][n_i][d_i]
-        sc = qi @ IK.T                                   # [Hkv][n_i][L]
+        sc = qi @ IK.T if IK.ndim == 2 else qi @ IK.transpose(0, 2, 1)  # [Hkv][n_i][L]
         pooled = [pool_blocks(sc[g], own, B) for g in range(H)]
         sel = np.stack([topk_sorted(pooled[g], own, k, sh.sink_blocks, sh.local_blocks)
                         for g in range(H)])
@@ -100,7 +104,8 @@ def prefill(case):
         sel_t, pool_t = [], []
         for g in range(H):
             rows = qi[q0:q1, g].reshape(-1, sh.idx_dim)  # tile queries x heads
-            pooled = pool_blocks(rows @ IK.T, own, B)
+            ikg = IK if IK.ndim == 2 else IK[g]
+            pooled = pool_blocks(rows @ ikg.T, own, B)
             sel_t.append(topk_sorted(pooled, own, k, sh.sink_blocks, sh.local_blocks))
             pool_t.append(pooled)
         sel_t = np.stack(sel_t)

@@ -13,6 +13,7 @@ import oracle
 from msa_inputs import Shape, build_paged_cache, make_decode_case, make_prefill_case
 from tests.append_util import holed_copy, new_token_batch
 from tests.test_oracle_forced import FORCED
+from tests.test_oracle_groupkeys import GK
 from tests import bruteforce
 from tests.test_oracle_pins import TINY, TINY1, _by_sort
 from tests.test_oracle_pins import test_handworked_golden as _golden
@@ -49,6 +50,8 @@ MUTANTS = [
      "if (b < n_sink || b > own - n_local) {", False),
     ("sink blocks ignored", "if (b < n_sink || b >= own - n_local) {",
      "if (b < 0 || b >= own - n_local) {", False),
+    ("per-group index keys read the shared head", "const int32_t head = Hk > 1 ? g : 0;",
+     "const int32_t head = 0;", False),
     ("append ignores the block table",
      "const int64_t pg = block_table[(int64_t)s * max_blocks + t / B];",
      "const int64_t pg = t / B;", False),
@@ -85,6 +88,12 @@ def _pins_pass() -> bool:
         _append_pin()
         case = make_decode_case(FORCED, [37, 9, 1, 64], 81, shuffle_pages=True, poison_frac=0.2)
         np.testing.assert_array_equal(oracle.decode(case)["sel"], bruteforce.decode(case)["sel"])
+        case = make_decode_case(GK, [37, 9, 64], 111, shuffle_pages=True, poison_frac=0.2)
+        o, r = oracle.decode(case), bruteforce.decode(case)
+        for s, L in enumerate(case.lengths):
+            own = (L - 1) // GK.block_size
+            for g in range(GK.num_kv_heads):
+                np.testing.assert_array_equal(o["pooled"][s, g, :own], r["pooled"][s][g])
     except AssertionError:
         return False
     return True
