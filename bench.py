@@ -105,7 +105,8 @@ class _Binding:
     def params_of(self, sh):
         return self.msa.make_params(sh.num_q_heads, sh.num_kv_heads, sh.head_dim,
                                     sh.num_idx_heads, sh.idx_dim, sh.block_size, sh.top_k,
-                                    sh.softmax_scale, sh.sink_blocks, sh.local_blocks)
+                                    sh.softmax_scale, sh.sink_blocks, sh.local_blocks,
+                                    sh.idx_k_heads)
 
     def kv_of(self, case):
         c = case.cache

@@ -43,7 +43,8 @@ class Params(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("num_idx_heads", ctypes.c_int32),
                 ("idx_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
-                ("sink_blocks", ctypes.c_int32), ("local_blocks", ctypes.c_int32)]
+                ("sink_blocks", ctypes.c_int32), ("local_blocks", ctypes.c_int32),
+                ("num_idx_k_heads", ctypes.c_int32)]
 
 
 class PagedKV(ctypes.Structure):
@@ -135,17 +136,17 @@ def _stream(stream) -> ctypes.c_void_p:
 def make_params(num_q_heads: int, num_kv_heads: int, head_dim: int = 128, num_idx_heads: int = 4,
                 idx_dim: int = 64, block_size: int = 128, top_k: int = 16,
                 softmax_scale: Optional[float] = None, sink_blocks: int = 0,
-                local_blocks: int = 0) -> Params:
+                local_blocks: int = 0, num_idx_k_heads: int = 1) -> Params:
     if softmax_scale is None:
         softmax_scale = head_dim ** -0.5
     return Params(num_q_heads, num_kv_heads, head_dim, num_idx_heads, idx_dim, block_size, top_k,
-                  float(softmax_scale), sink_blocks, local_blocks)
+                  float(softmax_scale), sink_blocks, local_blocks, num_idx_k_heads)
 
 
 def make_kv(k: torch.Tensor, v: torch.Tensor, idx_k: torch.Tensor,
             block_table: torch.Tensor) -> PagedKV:
-    """Paged cache descriptor: k [P][Hkv][B][D], v [P][Hkv][D][B], idx_k [P][B][d_i] (bf16),
-    block_table int32 [batch][max_blocks]."""
+    """Paged cache descriptor: k [P][Hkv][B][D], v [P][Hkv][D][B], idx_k [P][B][d_i] or
+    [P][Hkv][B][d_i] (bf16), block_table int32 [batch][max_blocks]."""
     kv = PagedKV(_dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
                  _dev(idx_k, torch.bfloat16, "idx_k"), _dev(block_table, torch.int32, "block_table"),
                  int(k.shape[0]), int(block_table.shape[-1]))

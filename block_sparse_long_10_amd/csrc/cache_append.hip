@@ -5,7 +5,7 @@
 // the one the other kernels read:
 //   k     [page][Hkv][B][D]   token-major
 //   v     [page][Hkv][D][B]   transposed within the page
-//   idx_k [page][B][d_i]
+//   idx_k [page][Hk][B][d_i]  (Hk = 1, the shared head, or Hkv per group)
 //
 // One 256-thread workgroup per (sequence, touched block, group) writes the
 // new tokens that fall into one page: K rows and index-key rows are 16-byte
@@ -22,6 +22,7 @@ template <int B>
 __global__ __launch_bounds__(256) void cache_append_kernel(
     uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, uint16_t* __restrict__ ic,
     const int32_t* __restrict__ block_table, int32_t max_blocks, int32_t num_kv_heads,
+    int32_t idx_k_heads,
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const uint16_t* __restrict__ idx_new, const int32_t* __restrict__ start_pos, int32_t n_new) {
   __shared__ uint32_t vt[B * kVStride / 2];
@@ -42,12 +43,15 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
         *reinterpret_cast<const u32x4*>(k_new + ((tok0 + i) * num_kv_heads + g) * 128 + c * 8);
     *reinterpret_cast<u32x4*>(kc + ((page * num_kv_heads + g) * B + slot0 + i) * 128 + c * 8) = val;
   }
-  // index-key rows (one shared head): written once, by group 0
-  if (g == 0) {
+  // index-key rows: the shared head is written once, by group 0; per-group
+  // heads by their group
+  if (idx_k_heads > 1 || g == 0) {
+    const int h = idx_k_heads > 1 ? g : 0;
     for (int x = tid; x < n * 8; x += 256) {
       const int i = x >> 3, c = x & 7;
-      const u32x4 val = *reinterpret_cast<const u32x4*>(idx_new + (tok0 + i) * 64 + c * 8);
-      *reinterpret_cast<u32x4*>(ic + (page * B + slot0 + i) * 64 + c * 8) = val;
+      const u32x4 val =
+          *reinterpret_cast<const u32x4*>(idx_new + ((tok0 + i) * idx_k_heads + h) * 64 + c * 8);
+      *reinterpret_cast<u32x4*>(ic + ((page * idx_k_heads + h) * B + slot0 + i) * 64 + c * 8) = val;
     }
   }
   // V of group g: token-major rows into LDS, then dimension-major out
@@ -73,12 +77,12 @@ hipError_t launch_cache_append(const Dims& d, const CacheW& c, const uint16_t* k
   const dim3 grid((n_new + B - 1) / B + 1, d.num_kv_heads, batch);
   if (B == 64)
     hipLaunchKernelGGL(cache_append_kernel<64>, grid, dim3(256), 0, stream, c.k, c.v, c.idx_k,
-                       c.block_table, c.max_blocks, d.num_kv_heads, k_new, v_new, idx_new,
-                       start_pos, n_new);
+                       c.block_table, c.max_blocks, d.num_kv_heads, d.idx_k_heads, k_new, v_new,
+                       idx_new, start_pos, n_new);
   else
     hipLaunchKernelGGL(cache_append_kernel<128>, grid, dim3(256), 0, stream, c.k, c.v, c.idx_k,
-                       c.block_table, c.max_blocks, d.num_kv_heads, k_new, v_new, idx_new,
-                       start_pos, n_new);
+                       c.block_table, c.max_blocks, d.num_kv_heads, d.idx_k_heads, k_new, v_new,
+                       idx_new, start_pos, n_new);
   return hipGetLastError();
 }
 

@@ -22,7 +22,7 @@ namespace msa {
 // index branch never reads.
 template <int B>
 __device__ __forceinline__ void append_current_token(const DecodeAppend& ap, int s, int L,
-                                                     int num_kv_heads) {
+                                                     int num_kv_heads, int idx_k_heads) {
   const int lane = threadIdx.x;
   const int own = (L - 1) / B, slot = (L - 1) % B;
   const size_t page = (size_t)ap.cache.block_table[(size_t)s * ap.cache.max_blocks + own];
@@ -36,21 +36,25 @@ __device__ __forceinline__ void append_current_token(const DecodeAppend& ap, int
     const int g = x >> 7, d = x & 127;
     ap.cache.v[((page * num_kv_heads + g) * 128 + d) * B + slot] = ap.v_new[kv0 + x];
   }
-  if (lane < 8)
-    *reinterpret_cast<u32x4*>(ap.cache.idx_k + (page * B + slot) * 64 + lane * 8) =
-        *reinterpret_cast<const u32x4*>(ap.idx_new + (size_t)s * 64 + lane * 8);
+  for (int x = lane; x < idx_k_heads * 8; x += kWave) {  // index-key rows, 16-byte chunks
+    const int h = x >> 3, c = x & 7;
+    *reinterpret_cast<u32x4*>(ap.cache.idx_k + ((page * idx_k_heads + h) * B + slot) * 64 + c * 8) =
+        *reinterpret_cast<const u32x4*>(ap.idx_new + ((size_t)s * idx_k_heads + h) * 64 + c * 8);
+  }
 }
 
-template <int B, int NI, int MT>
+// PG: per-group index keys; workgroup (x, s, g) scores group g's n_i rows
+// against its own key head of the block (grid z = Hkv).
+template <int B, int NI, int MT, bool PG>
 __global__ __launch_bounds__(64) void index_score_decode_kernel(
     const uint16_t* __restrict__ idx_k, const int32_t* __restrict__ block_table,
     int32_t max_blocks, const uint16_t* __restrict__ idx_q, const int32_t* __restrict__ seq_lens,
-    int32_t num_kv_heads, float* __restrict__ pooled, uint32_t* __restrict__ counters,
-    DecodeAppend ap) {
+    int32_t num_kv_heads, int32_t idx_k_heads, float* __restrict__ pooled,
+    uint32_t* __restrict__ counters, DecodeAppend ap) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[B * 128];
-  const int s = blockIdx.y;
+  const int s = blockIdx.y, gz = blockIdx.z;
   const int lane = threadIdx.x;
-  if (counters != nullptr && blockIdx.x == 0 && lane < num_kv_heads)
+  if (counters != nullptr && blockIdx.x == 0 && gz == 0 && lane < num_kv_heads)
     counters[s * num_kv_heads + lane] = 0u;
   const int L = seq_lens[s];
   // with an append, workgroup 0 (dispatched first, so its latency hides
@@ -59,7 +63,7 @@ __global__ __launch_bounds__(64) void index_score_decode_kernel(
   int b = blockIdx.x;
   if (ap.k_new != nullptr) {
     if (b == 0) {
-      append_current_token<B>(ap, s, L, num_kv_heads);
+      if (gz == 0) append_current_token<B>(ap, s, L, num_kv_heads, idx_k_heads);
       return;
     }
     --b;
@@ -67,36 +71,50 @@ __global__ __launch_bounds__(64) void index_score_decode_kernel(
   const int own = (L - 1) / B;
   if (b >= own) return;
   float* out = pooled + (size_t)s * num_kv_heads * max_blocks + b;
-  index_block_scores<B, NI, MT>(idx_k, block_table[(size_t)s * max_blocks + b],
-                                idx_q + (size_t)s * num_kv_heads * NI * 64, num_kv_heads, stage,
-                                [&](int g, float v) { out[(size_t)g * max_blocks] = v; });
+  const int32_t page = block_table[(size_t)s * max_blocks + b];
+  if constexpr (PG) {
+    index_block_scores<B, NI, 1>(idx_k, page * idx_k_heads + gz,
+                                 idx_q + ((size_t)s * num_kv_heads + gz) * NI * 64, 1, stage,
+                                 [&](int, float v) { out[(size_t)gz * max_blocks] = v; });
+  } else {
+    index_block_scores<B, NI, MT>(idx_k, page, idx_q + (size_t)s * num_kv_heads * NI * 64,
+                                  num_kv_heads, stage,
+                                  [&](int g, float v) { out[(size_t)g * max_blocks] = v; });
+  }
 }
 
 template <int B, int NI>
-static hipError_t launch_decode_ni(int mt, dim3 grid, hipStream_t st, const uint16_t* idx_k,
-                                   const int32_t* bt, int32_t mb, const uint16_t* idx_q,
-                                   const int32_t* sl, int32_t hkv, float* pooled,
-                                   uint32_t* ctr, const DecodeAppend& ap) {
-  switch (mt) {
-    case 1: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 1>), grid, dim3(64), 0, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr, ap); break;
-    case 2: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 2>), grid, dim3(64), 0, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr, ap); break;
-    case 3: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 3>), grid, dim3(64), 0, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr, ap); break;
-    default: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 4>), grid, dim3(64), 0, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr, ap); break;
+static hipError_t launch_decode_ni(int mt, bool pg, dim3 grid, hipStream_t st,
+                                   const uint16_t* idx_k, const int32_t* bt, int32_t mb,
+                                   const uint16_t* idx_q, const int32_t* sl, int32_t hkv,
+                                   int32_t hk, float* pooled, uint32_t* ctr,
+                                   const DecodeAppend& ap) {
+#define MSA_IDX_ARGS idx_k, bt, mb, idx_q, sl, hkv, hk, pooled, ctr, ap
+  if (pg) {
+    hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 1, true>), grid, dim3(64), 0, st, MSA_IDX_ARGS);
+    return hipGetLastError();
   }
+  switch (mt) {
+    case 1: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 1, false>), grid, dim3(64), 0, st, MSA_IDX_ARGS); break;
+    case 2: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 2, false>), grid, dim3(64), 0, st, MSA_IDX_ARGS); break;
+    case 3: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 3, false>), grid, dim3(64), 0, st, MSA_IDX_ARGS); break;
+    default: hipLaunchKernelGGL((index_score_decode_kernel<B, NI, 4, false>), grid, dim3(64), 0, st, MSA_IDX_ARGS); break;
+  }
+#undef MSA_IDX_ARGS
   return hipGetLastError();
 }
 
 template <int B>
-static hipError_t launch_decode_b(int ni, int mt, dim3 grid, hipStream_t st, const uint16_t* idx_k,
-                                  const int32_t* bt, int32_t mb, const uint16_t* idx_q,
-                                  const int32_t* sl, int32_t hkv, float* pooled,
-                                  uint32_t* ctr, const DecodeAppend& ap) {
+static hipError_t launch_decode_b(int ni, int mt, bool pg, dim3 grid, hipStream_t st,
+                                  const uint16_t* idx_k, const int32_t* bt, int32_t mb,
+                                  const uint16_t* idx_q, const int32_t* sl, int32_t hkv, int32_t hk,
+                                  float* pooled, uint32_t* ctr, const DecodeAppend& ap) {
   switch (ni) {
-    case 1: return launch_decode_ni<B, 1>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr, ap);
-    case 2: return launch_decode_ni<B, 2>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr, ap);
-    case 4: return launch_decode_ni<B, 4>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr, ap);
-    case 8: return launch_decode_ni<B, 8>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr, ap);
-    default: return launch_decode_ni<B, 16>(mt, grid, st, idx_k, bt, mb, idx_q, sl, hkv, pooled, ctr, ap);
+    case 1: return launch_decode_ni<B, 1>(mt, pg, grid, st, idx_k, bt, mb, idx_q, sl, hkv, hk, pooled, ctr, ap);
+    case 2: return launch_decode_ni<B, 2>(mt, pg, grid, st, idx_k, bt, mb, idx_q, sl, hkv, hk, pooled, ctr, ap);
+    case 4: return launch_decode_ni<B, 4>(mt, pg, grid, st, idx_k, bt, mb, idx_q, sl, hkv, hk, pooled, ctr, ap);
+    case 8: return launch_decode_ni<B, 8>(mt, pg, grid, st, idx_k, bt, mb, idx_q, sl, hkv, hk, pooled, ctr, ap);
+    default: return launch_decode_ni<B, 16>(mt, pg, grid, st, idx_k, bt, mb, idx_q, sl, hkv, hk, pooled, ctr, ap);
   }
 }
 
@@ -112,12 +130,15 @@ hipError_t launch_index_score_decode(const Dims& d, const Cache& c, const uint16
   DecodeAppend ap{};
   if (append != nullptr) ap = *append;
   const int mt = (d.num_kv_heads * d.num_idx_heads + 15) / 16;
-  dim3 grid(gx, batch);
+  const bool pg = d.idx_k_heads > 1;
+  dim3 grid(gx, batch, pg ? d.num_kv_heads : 1);
   if (B == 64)
-    return launch_decode_b<64>(d.num_idx_heads, mt, grid, stream, c.idx_k, c.block_table,
-                               c.max_blocks, idx_q, seq_lens, d.num_kv_heads, pooled, counters, ap);
-  return launch_decode_b<128>(d.num_idx_heads, mt, grid, stream, c.idx_k, c.block_table,
-                              c.max_blocks, idx_q, seq_lens, d.num_kv_heads, pooled, counters, ap);
+    return launch_decode_b<64>(d.num_idx_heads, mt, pg, grid, stream, c.idx_k, c.block_table,
+                               c.max_blocks, idx_q, seq_lens, d.num_kv_heads, d.idx_k_heads,
+                               pooled, counters, ap);
+  return launch_decode_b<128>(d.num_idx_heads, mt, pg, grid, stream, c.idx_k, c.block_table,
+                              c.max_blocks, idx_q, seq_lens, d.num_kv_heads, d.idx_k_heads, pooled,
+                              counters, ap);
 }
 
 }  // namespace msa

@@ -26,7 +26,7 @@ template <int B>
 __global__ __launch_bounds__(256) void index_score_prefill_kernel(
     const uint16_t* __restrict__ idx_k, const int32_t* __restrict__ block_table,
     const uint16_t* __restrict__ idx_q, ChunkMap map, int32_t num_kv_heads,
-    int32_t num_idx_heads, int32_t max_blocks, int32_t blocks_per_split,
+    int32_t num_idx_heads, int32_t idx_k_heads, int32_t max_blocks, int32_t blocks_per_split,
     float* __restrict__ pooled) {
   constexpr int NT = B / 32;                       // 32-token N tiles per block
   constexpr int BLOCK_BYTES = B * 128;             // B tokens x 64 bf16
@@ -62,7 +62,9 @@ __global__ __launch_bounds__(256) void index_score_prefill_kernel(
   const int32_t* bt = block_table + (size_t)loc.seq * map.max_blocks;
   const int src_off = (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) << 4);
   auto issue = [&](int b, int buf) {
-    const uint8_t* src = reinterpret_cast<const uint8_t*>(idx_k) + (size_t)bt[b] * BLOCK_BYTES;
+    // the block's index keys: the shared head, or group g's own head
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(idx_k) +
+                         ((size_t)bt[b] * idx_k_heads + (idx_k_heads > 1 ? g : 0)) * BLOCK_BYTES;
 #pragma unroll
     for (int i = 0; i < WLOADS; ++i) {
       const int q = wave * WLOADS + i;
@@ -143,11 +145,11 @@ hipError_t launch_index_score_prefill(const Dims& d, const Cache& c, const uint1
   if (B == 64)
     hipLaunchKernelGGL(index_score_prefill_kernel<64>, grid, dim3(256), 0, stream, c.idx_k,
                        c.block_table, idx_q, map, d.num_kv_heads,
-                       d.num_idx_heads, c.max_blocks, per, pooled);
+                       d.num_idx_heads, d.idx_k_heads, c.max_blocks, per, pooled);
   else
     hipLaunchKernelGGL(index_score_prefill_kernel<128>, grid, dim3(256), 0, stream, c.idx_k,
                        c.block_table, idx_q, map, d.num_kv_heads,
-                       d.num_idx_heads, c.max_blocks, per, pooled);
+                       d.num_idx_heads, d.idx_k_heads, c.max_blocks, per, pooled);
   return hipGetLastError();
 }
 

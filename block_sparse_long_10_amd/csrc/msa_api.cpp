@@ -51,6 +51,8 @@ msa_status check_params(const msa_params* p) {
     return fail(MSA_ERR_UNSUPPORTED, "num_kv_heads * num_idx_heads must be <= 64");
   if (p->num_q_heads / p->num_kv_heads > 16)
     return fail(MSA_ERR_UNSUPPORTED, "group size num_q_heads/num_kv_heads must be <= 16");
+  if (p->num_idx_k_heads != 0 && p->num_idx_k_heads != 1 && p->num_idx_k_heads != p->num_kv_heads)
+    return fail(MSA_ERR_UNSUPPORTED, "num_idx_k_heads must be 0, 1 or num_kv_heads");
   return MSA_OK;
 }
 
@@ -86,7 +88,8 @@ msa_paged_kv read_view(const msa_paged_kv_mut* kv) {
 msa::Dims dims_of(const msa_params* p) {
   return msa::Dims{p->num_q_heads, p->num_kv_heads, p->head_dim,   p->num_idx_heads,
                    p->idx_dim,     p->block_size,   p->top_k,      p->softmax_scale,
-                   p->sink_blocks, p->local_blocks};
+                   p->sink_blocks, p->local_blocks,
+                   p->num_idx_k_heads > 1 ? p->num_idx_k_heads : 1};
 }
 
 msa::Cache cache_of(const msa_paged_kv* kv) {

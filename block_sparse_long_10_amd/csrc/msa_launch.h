@@ -12,6 +12,7 @@ struct Dims {
   int32_t num_q_heads, num_kv_heads, head_dim, num_idx_heads, idx_dim, block_size, top_k;
   float softmax_scale;
   int32_t sink_blocks, local_blocks;  // forced blocks of the selection
+  int32_t idx_k_heads;                // 1 (shared index-key head) or Hkv (one per group)
 };
 
 struct Cache {

@@ -24,6 +24,11 @@
  * block are always kept and never ranked; they count toward top_k, so TopK
  * chooses top_k - 1 - (number forced) of the other blocks before the own one.
  * sink_blocks = local_blocks = 0 is the plain method.
+ * Per-group index keys (num_idx_k_heads = num_kv_heads) replace the page's
+ * single shared index-key head by one head per KV group, each group scoring
+ * against its own: an ablation of "K_idx hat nur einen Head"; the index
+ * cache is then [num_pages][Hkv][B][d_i] and appended index keys carry Hkv
+ * heads ([..][Hkv][d_i]).
  *
  * Conventions for every entry point
  * ---------------------------------
@@ -44,13 +49,15 @@
  *   num_kv_heads * num_idx_heads <= 64, group size num_q_heads/num_kv_heads
  *   in 1..16.  Other values return MSA_ERR_UNSUPPORTED.  sink_blocks and
  *   local_blocks must be >= 0 with sink_blocks + local_blocks <= top_k - 1
- *   (else MSA_ERR_INVALID_ARGUMENT).
+ *   (else MSA_ERR_INVALID_ARGUMENT); num_idx_k_heads must be 0, 1 or
+ *   num_kv_heads (else MSA_ERR_UNSUPPORTED).
  *
  * Paged KV cache (one page holds one KV block of block_size tokens)
  * -----------------------------------------------------------------
  *   k      bf16 [num_pages][Hkv][B][D]   keys, token-major within a page
  *   v      bf16 [num_pages][Hkv][D][B]   values, transposed within a page
  *   idx_k  bf16 [num_pages][B][d_i]      the single shared index-key head
+ *          ([num_pages][Hkv][B][d_i] with per-group index keys)
  *   block_table int32 [batch][max_blocks_per_seq]: logical block b of
  *          sequence s lives in page block_table[s*max_blocks_per_seq + b]
  * The caller has already written the current token's (decode) or the
@@ -87,6 +94,8 @@ typedef struct {
   int32_t sink_blocks;   /* blocks 0..sink_blocks-1 always kept (0: none)   */
   int32_t local_blocks;  /* the local_blocks blocks just before the own block
                             always kept (0: none)                          */
+  int32_t num_idx_k_heads; /* index-key heads: 0 or 1 = the single shared head;
+                              num_kv_heads = one per group (ablation)       */
 } msa_params;
 
 typedef struct {

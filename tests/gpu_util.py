@@ -28,7 +28,8 @@ OUT_ROW_TOL = 2e-3
 def params_of(shape):
     return msa.make_params(shape.num_q_heads, shape.num_kv_heads, shape.head_dim,
                            shape.num_idx_heads, shape.idx_dim, shape.block_size, shape.top_k,
-                           shape.softmax_scale, shape.sink_blocks, shape.local_blocks)
+                           shape.softmax_scale, shape.sink_blocks, shape.local_blocks,
+                           shape.idx_k_heads)
 
 
 def kv_of(case):

@@ -78,6 +78,7 @@ def decode_status(p, kv, batch=2, max_seq_len=1000, ws_bytes=None, **null):
     (dict(softmax_scale=float("inf")), INVALID, "finite"),
     (dict(sink_blocks=-1), INVALID, "sink"),
     (dict(sink_blocks=8, local_blocks=8), INVALID, "top_k - 1"),
+    (dict(num_idx_k_heads=3), UNSUPPORTED, "num_idx_k_heads"),
 ])
 def test_decode_rejects_bad_params(change, status, msg):
     assert decode_status(good_params(**change), fake_kv()) == status
