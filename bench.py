@@ -368,6 +368,53 @@ def run_varlen_bench(args, torch, msa, mi, gu):
             "index_tflops_effective": round(index_flops / (ms * 1e-3) / 1e12, 1)}
 
 
+def run_group_keys_bench(args, torch, msa, mi, gu):
+    """Ablation of the shared index-key head: decode_b1_L1M with one index-key
+    head per KV group (8 x 128 MiB of index keys per layer), two buffer sets
+    of index keys rotated (the K/V pages are shared)."""
+    base = mi.make_workload(DECODE_WORKLOAD, "cuda")
+    sh = mi.Shape(num_q_heads=64, num_kv_heads=8, idx_k_heads=8)
+    log("[bench] ablation: per-group index keys at 1M")
+    c = base.cache
+    sets = []
+    for r in range(2):
+        ik = mi.normal_bf16((c.num_pages, 8, sh.block_size, sh.idx_dim), 300 + r,
+                            mi.TENSOR_IDS["idx_k"], "cuda")
+        sets.append(msa.make_kv(c.k, c.v, ik, c.block_table))
+    p = gu.params_of(sh)
+    batch, maxL, mb = base.batch, max(base.lengths), c.max_blocks
+    out = torch.empty(batch, sh.num_q_heads, sh.head_dim, device="cuda")
+    ws = torch.empty(msa.msa_decode_workspace_bytes(p, batch, mb), dtype=torch.uint8,
+                     device="cuda")
+    pooled = torch.empty(batch, sh.num_kv_heads, mb, device="cuda")
+
+    def timed(fn, n, warm):
+        for i in range(warm):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    n = max(20, args.steps // 4)
+    ms_step = timed(lambda i: msa.msa_decode(p, sets[i % 2], base.q, base.idx_q, base.seq_lens,
+                                             batch, maxL, out, None, ws), n, 5)
+    ms_index = timed(lambda i: msa.msa_index_score_decode(p, sets[i % 2], base.idx_q,
+                                                          base.seq_lens, batch, maxL, pooled),
+                     n, 5)
+    own = (maxL - 1) // sh.block_size
+    idx_bytes = own * sh.block_size * sh.idx_dim * 2 * 8
+    return {"workload": DECODE_WORKLOAD + " with 8 index-key heads",
+            "us_per_step": round(ms_step * 1e3, 2),
+            "index_kernel_us": round(ms_index * 1e3, 2),
+            "index_key_bytes": idx_bytes,
+            "index_gbps": round(idx_bytes / (ms_index * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(case, budget_s):
     """The oracle on the host cores: whole decode steps of the same workload
     (index scores of every block, TopK, attention), repeated for about
@@ -501,6 +548,8 @@ def main():
                     help="layers of the multi-layer decode leg (0 = skip)")
     ap.add_argument("--layer-tokens", type=int, default=20,
                     help="tokens timed in the multi-layer decode leg")
+    ap.add_argument("--no-ablation", action="store_true",
+                    help="skip the per-group index-key ablation leg")
     ap.add_argument("--varlen-chunk", type=int, default=512,
                     help="tokens per sequence of the batched prefill leg (0 = skip)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
@@ -539,6 +588,7 @@ def main():
 
     dec = run_decode_bench(args, torch, msa, mi, gu)
     lay = run_layers_bench(args, torch, msa, mi, dec) if args.layers > 0 else None
+    gk = run_group_keys_bench(args, torch, msa, mi, gu) if not args.no_ablation else None
     pre = None if args.no_prefill else run_prefill_bench(args, torch, msa, mi, gu)
     var = (run_varlen_bench(args, torch, msa, mi, gu)
            if not args.no_prefill and args.varlen_chunk > 0 else None)
@@ -607,6 +657,8 @@ def main():
         result["multi_layer_decode"] = lay
     if var is not None:
         result["batched_prefill"] = var
+    if gk is not None:
+        result["ablation_group_index_keys"] = gk
     if args.cpu_budget > 0:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     else:
