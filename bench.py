@@ -415,6 +415,40 @@ def run_group_keys_bench(args, torch, msa, mi, gu):
             "index_gbps": round(idx_bytes / (ms_index * 1e-3) / 1e9, 1)}
 
 
+def practical_peaks(torch):
+    """What library kernels reach on this machine, for context beside the
+    datasheet peaks: a 2 GiB device-to-device copy (bytes read + written per
+    second) and an 8192^3 bf16 matrix product (through torch)."""
+    log("[bench] practical peaks: device copy and bf16 GEMM")
+    n = 1 << 30  # bf16 elements: 2 GiB
+    a = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+
+    def timed(fn, reps, warm):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_copy = timed(lambda: b.copy_(a), 10, 2)
+    del a, b
+    m = 8192
+    x = torch.randn(m, m, device="cuda", dtype=torch.bfloat16)
+    y = torch.randn(m, m, device="cuda", dtype=torch.bfloat16)
+    ms_mm = timed(lambda: torch.matmul(x, y), 10, 3)
+    del x, y
+    return {"hbm_copy_gbps": round(2 * 2 * n / (ms_copy * 1e-3) / 1e9, 1),
+            "bf16_gemm_tflops": round(2 * m ** 3 / (ms_mm * 1e-3) / 1e12, 1),
+            "note": "torch device copy (read + write bytes) and torch.matmul 8192^3 bf16"}
+
+
 def cpu_baseline(case, budget_s):
     """The oracle on the host cores: whole decode steps of the same workload
     (index scores of every block, TopK, attention), repeated for about
@@ -589,6 +623,7 @@ def main():
     dec = run_decode_bench(args, torch, msa, mi, gu)
     lay = run_layers_bench(args, torch, msa, mi, dec) if args.layers > 0 else None
     gk = run_group_keys_bench(args, torch, msa, mi, gu) if not args.no_ablation else None
+    peaks = practical_peaks(torch) if not args.no_ablation else None
     pre = None if args.no_prefill else run_prefill_bench(args, torch, msa, mi, gu)
     var = (run_varlen_bench(args, torch, msa, mi, gu)
            if not args.no_prefill and args.varlen_chunk > 0 else None)
@@ -659,6 +694,8 @@ def main():
         result["batched_prefill"] = var
     if gk is not None:
         result["ablation_group_index_keys"] = gk
+    if peaks is not None:
+        result["library_reference"] = peaks
     if args.cpu_budget > 0:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     else:
