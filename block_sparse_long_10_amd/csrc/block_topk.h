@@ -253,14 +253,17 @@ __device__ __forceinline__ void bitonic_merge(uint32_t& v) {
   if constexpr (K >= 4) bitonic_stage<K, 2>(v);
   bitonic_stage<K, 1>(v);
 }
-// Sort the 64 lane values of a wave descending: lane 0 largest.
+// Sort the lane values of each group of W lanes (W = 16, 32 or 64)
+// descending: lane 0 of the wave holds the largest of lanes 0 .. W-1.  (The
+// other groups end up sorted too, in alternating directions.)
+template <int W = 64>
 __device__ __forceinline__ void wave_sort_desc(uint32_t& v) {
   bitonic_merge<2>(v);
   bitonic_merge<4>(v);
   bitonic_merge<8>(v);
   bitonic_merge<16>(v);
-  bitonic_merge<32>(v);
-  bitonic_merge<64>(v);
+  if constexpr (W >= 32) bitonic_merge<32>(v);
+  if constexpr (W >= 64) bitonic_merge<64>(v);
 }
 
 // The same for (key, index) pairs ordered by key descending, then index
@@ -284,14 +287,16 @@ __device__ __forceinline__ void bitonic_merge2(uint32_t& key, uint32_t& idx) {
   if constexpr (K >= 4) bitonic_stage2<K, 2>(key, idx);
   bitonic_stage2<K, 1>(key, idx);
 }
-// Sort 64 (key, index) pairs of a wave into selection order: lane 0 first.
+// Sort the (key, index) pairs of each group of W lanes into selection order:
+// lane 0 first.
+template <int W = 64>
 __device__ __forceinline__ void wave_sort_pairs(uint32_t& key, uint32_t& idx) {
   bitonic_merge2<2>(key, idx);
   bitonic_merge2<4>(key, idx);
   bitonic_merge2<8>(key, idx);
   bitonic_merge2<16>(key, idx);
-  bitonic_merge2<32>(key, idx);
-  bitonic_merge2<64>(key, idx);
+  if constexpr (W >= 32) bitonic_merge2<32>(key, idx);
+  if constexpr (W >= 64) bitonic_merge2<64>(key, idx);
 }
 
 // Wave inclusive prefix sum with DPP: row shifts, then row broadcasts.
@@ -394,10 +399,14 @@ __device__ __forceinline__ bool topk_fast(const RegKeys<MAXV>& src, int own, int
   if (wave == 0) {
     // the 64 slots in selection order (empty ones sort last), then the first
     // `keep` indices ascending: sort ~index descending (others sort last)
+    // (sort networks only as wide as needed: the candidates, then the winners)
     uint32_t key = sh.cand_k[lane], idx = (uint32_t)sh.cand_i[lane];
-    wave_sort_pairs(key, idx);
+    if (total <= 32) wave_sort_pairs<32>(key, idx);
+    else wave_sort_pairs<64>(key, idx);
     uint32_t v = lane < keep ? ~idx : 0u;
-    wave_sort_desc(v);
+    if (keep <= 16) wave_sort_desc<16>(v);
+    else if (keep <= 32) wave_sort_desc<32>(v);
+    else wave_sort_desc<64>(v);
     if (lane < keep) out_sel[lane] = (int)~v;
     if (lane == 0) out_sel[keep] = own;
     for (int i = keep + 1 + lane; i < k; i += kWave) out_sel[i] = -1;
