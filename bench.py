@@ -521,11 +521,11 @@ def summarize_kernel_trace(trace_csv, out_txt, command):
         groups.setdefault((name, wg), []).append(us)
     lines = ["rocprofv3 kernel trace (MSA kernels), per kernel and launch grid", "",
              "command:", "  " + command, "",
-             "%-44s %-18s %6s %12s %12s %12s" % ("kernel", "workgroups", "calls", "avg us",
+             "%-60s %-18s %6s %12s %12s %12s" % ("kernel", "workgroups", "calls", "avg us",
                                                   "min us", "max us")]
     for (name, wg), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
-        lines.append("%-44s %-18s %6d %12.3f %12.3f %12.3f" % (
-            name[:44], "%dx%dx%d" % wg, len(v), sum(v) / len(v), min(v), max(v)))
+        lines.append("%-60s %-18s %6d %12.3f %12.3f %12.3f" % (
+            name, "%dx%dx%d" % wg, len(v), sum(v) / len(v), min(v), max(v)))
     with open(out_txt, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
