@@ -6,6 +6,9 @@ against an index-key head of its own.
 * decode and prefill against the numpy brute force with per-group keys;
 * when every group's key head is a copy of one head, the results equal the
   shared-head method's bit for bit (pooled scores, selections, outputs);
+* a group reads only its own key head: redrawing another group's head leaves
+  the group's pooled scores, selection and output unchanged, redrawing its own
+  head changes its pooled scores;
 * appends with per-group index keys restore the generated cache.
 """
 import numpy as np
@@ -46,6 +49,26 @@ def test_identical_group_heads_equal_the_shared_head():
     np.testing.assert_array_equal(oa["sel"], ob["sel"])
     np.testing.assert_array_equal(oa["pooled"], ob["pooled"])
     np.testing.assert_array_equal(oa["out"], ob["out"])
+
+
+def test_group_reads_only_its_own_key_head():
+    case = make_decode_case(GK, [60, 23, 41], 118, shuffle_pages=True)
+    base = oracle.decode(case)
+    G = GK.num_q_heads // GK.num_kv_heads
+    rng = np.random.default_rng(119)
+    for h in range(GK.num_kv_heads):
+        alt = make_decode_case(GK, [60, 23, 41], 118, shuffle_pages=True)
+        redraw = torch.from_numpy(rng.standard_normal(alt.cache.idx_k[:, h].shape)).to(torch.bfloat16)
+        alt.cache.idx_k[:, h] = redraw
+        res = oracle.decode(alt)
+        for g in range(GK.num_kv_heads):
+            heads = slice(g * G, (g + 1) * G)
+            if g == h:
+                assert not np.array_equal(res["pooled"][:, g], base["pooled"][:, g])
+            else:
+                np.testing.assert_array_equal(res["pooled"][:, g], base["pooled"][:, g])
+                np.testing.assert_array_equal(res["sel"][:, g], base["sel"][:, g])
+                np.testing.assert_array_equal(res["out"][:, heads], base["out"][:, heads])
 
 
 def test_append_group_keys_restores_the_cache():
