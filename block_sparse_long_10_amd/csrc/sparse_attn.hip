@@ -73,7 +73,12 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
   MergeShared& msh = scratch.msh;
   __shared__ int is_last;
 
-  const int slot = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  // Workgroups are dispatched round-robin over the XCDs, each with its own
+  // L2.  Taking the group from the low digits of the (slot, group) index puts
+  // a group's slot workgroups on the same XCD(s), where they share one L2 copy
+  // of the group's pooled scores (grid: top_k x num_kv_heads x batch).
+  const int lin = blockIdx.x + blockIdx.y * gridDim.x;
+  const int g = lin % num_kv_heads, slot = lin / num_kv_heads, s = blockIdx.z;
   const int tid = threadIdx.x;
   const int Hq = num_kv_heads * group;
   const int L = seq_lens[s];
