@@ -158,8 +158,20 @@ def run_decode_bench(args, torch, msa, mi, gu):
         msa.msa_decode_append(p, kvm[i % len(sets)], kn, vn, xn, c.q, c.idx_q, c.seq_lens, batch,
                               maxL, out, sel, ws)
 
+    def per_step(fn, n):
+        # events between consecutive steps on the launch stream: one interval per step
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        evs[0].record()
+        for i in range(n):
+            fn(i)
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        return sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(n))
+
     log("[bench] decode: %d warmup + %d timed steps" % (args.warmup, args.steps))
     ms_step = timed(step, args.steps, args.warmup)
+    log("[bench] decode: per-step intervals (one event marker each)")
+    ms_each = per_step(step, args.steps)
     log("[bench] decode index kernel alone")
     ms_index = timed(index_only, args.steps, args.warmup)
     log("[bench] decode with the fused append")
@@ -172,7 +184,7 @@ def run_decode_bench(args, torch, msa, mi, gu):
     return {
         "ms_step": ms_step, "ms_index": ms_index, "index_bytes": index_bytes,
         "step_bytes": step_bytes, "case": base, "sets": sets, "p": p, "kvs": kvs,
-        "ms_append_step": ms_append_step,
+        "ms_append_step": ms_append_step, "ms_each": ms_each,
     }
 
 
@@ -255,6 +267,24 @@ def run_layers_bench(args, torch, msa, mi, dec):
             "note": "per-layer index keys, queries and index queries; K/V pages shared"}
 
 
+def prefill_algorithmic_flops(sh, P, C):
+    """Index flops: every (query, eligible key) pair x all index rows x d_i
+    multiply-adds; attention flops: QK and PV over the kept tokens visible to
+    each query (exact causal)."""
+    B, rows = sh.block_size, sh.num_kv_heads * sh.num_idx_heads
+    nt = (P + C + B - 1) // B - P // B
+    pairs = 0
+    attn_pairs = 0
+    for t in range(nt):
+        own = P // B + t
+        q0, q1 = max(0, own * B - P), min(C, (own + 1) * B - P)
+        pairs += (q1 - q0) * own * B
+        kept = min(sh.top_k - 1, own) * B
+        for i in range(q0, q1):
+            attn_pairs += kept + (P + i - own * B + 1)
+    return pairs * rows * sh.idx_dim * 2, attn_pairs * sh.num_q_heads * sh.head_dim * 4
+
+
 def run_prefill_bench(args, torch, msa, mi, gu):
     log("[bench] generating %s" % PREFILL_WORKLOAD)
     case = mi.make_workload(PREFILL_WORKLOAD, "cuda")
@@ -298,20 +328,7 @@ def run_prefill_bench(args, torch, msa, mi, gu):
     kvm = msa.make_kv_mut(case.cache.k, case.cache.v, case.cache.idx_k, case.cache.block_table)
     ms_append = timed(lambda: msa.msa_cache_append(p, kvm, k_new, v_new, x_new, start, 1, C), n, w)
     append_bytes = 2 * C * (2 * sh.num_kv_heads * sh.head_dim * 2 + sh.idx_dim * 2)
-    # algorithmic flops: every (query, eligible key) pair x all index rows x d_i
-    # multiply-adds; attention over the kept tokens visible to each query
-    B, rows = sh.block_size, sh.num_kv_heads * sh.num_idx_heads
-    pairs = 0
-    attn_pairs = 0
-    for t in range(nt):
-        own = P // B + t
-        q0, q1 = max(0, own * B - P), min(C, (own + 1) * B - P)
-        pairs += (q1 - q0) * own * B
-        kept = min(sh.top_k - 1, own) * B
-        for i in range(q0, q1):
-            attn_pairs += kept + (P + i - own * B + 1)
-    index_flops = pairs * rows * sh.idx_dim * 2
-    attn_flops = attn_pairs * sh.num_q_heads * sh.head_dim * 4
+    index_flops, attn_flops = prefill_algorithmic_flops(sh, P, C)
     return {"case": case, "ms_chunk": ms_chunk, "ms_index": ms_index, "ms_topk": ms_topk,
             "ms_attn": ms_attn, "index_flops": index_flops, "attn_flops": attn_flops,
             "ms_append": ms_append, "append_bytes": append_bytes}
@@ -415,11 +432,51 @@ def run_group_keys_bench(args, torch, msa, mi, gu):
             "index_gbps": round(idx_bytes / (ms_index * 1e-3) / 1e9, 1)}
 
 
+def _timed_ms(torch, fn, reps, warm):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def measured_peaks(torch, msa):
+    """The practical roofs, from the library's measurement kernels: a plain
+    non-temporal read stream over 2 GiB (far beyond the 256 MB Infinity
+    Cache) and a loop of independent bf16 MFMA chains; the best launch shape
+    of a small sweep each."""
+    log("[bench] practical peaks: read stream and bf16 MFMA loop")
+    nbytes = 1 << 31
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    read = []
+    for wg in (2048, 4096, 8192, 16384, 32768):
+        ms = _timed_ms(torch, lambda: msa.msa_probe_read_stream(src, wg, sink), 10, 2)
+        read.append((nbytes / (ms * 1e-3) / 1e9, wg))
+    del src
+    iters = 4096
+    mfma = []
+    for wg in (1024, 2048, 4096):
+        ms = _timed_ms(torch, lambda: msa.msa_probe_mfma_bf16(iters, wg, sink), 5, 1)
+        mfma.append((32768.0 * 16 * iters * wg / (ms * 1e-3) / 1e12, wg))
+    (gbps, rwg), (tflops, mwg) = max(read), max(mfma)
+    return {"hbm_read_stream_gbps": round(gbps, 1), "read_stream_workgroups": rwg,
+            "mfma_bf16_tflops": round(tflops, 1), "mfma_workgroups": mwg,
+            "note": "msa_probe_read_stream over 2 GiB, msa_probe_mfma_bf16 (4 chains of "
+                    "v_mfma_f32_32x32x16_bf16 per wave); best of a launch-shape sweep"}
+
+
 def practical_peaks(torch):
     """What library kernels reach on this machine, for context beside the
     datasheet peaks: a 2 GiB device-to-device copy (bytes read + written per
     second) and an 8192^3 bf16 matrix product (through torch)."""
-    log("[bench] practical peaks: device copy and bf16 GEMM")
+    log("[bench] library reference: device copy and bf16 GEMM")
     n = 1 << 30  # bf16 elements: 2 GiB
     a = torch.empty(n, dtype=torch.bfloat16, device="cuda")
     b = torch.empty_like(a)
@@ -503,6 +560,76 @@ def traffic_probe(args, torch, msa, mi, gu):
                                    max(base.lengths), pooled)
     torch.cuda.synchronize()
     log("[bench] traffic probe done; kernel source hash %s" % kernel_source_hash())
+
+
+MFMA_PROBE_ITERS, MFMA_PROBE_WORKGROUPS = 1024, 1024
+
+
+def mfma_probe(args, torch, msa, mi, gu):
+    """Launches for the MFMA counter run: the MFMA issue loop (known flops,
+    the calibration of SQ_INSTS_VALU_MFMA_MOPS_BF16), then one index, TopK and
+    attention launch of prefill_P1M_C8k."""
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    msa.msa_probe_mfma_bf16(MFMA_PROBE_ITERS, MFMA_PROBE_WORKGROUPS, sink)
+    torch.cuda.synchronize()
+    case = mi.make_workload(PREFILL_WORKLOAD, "cuda")
+    sh = case.shape
+    p, kv = gu.params_of(sh), gu.kv_of(case)
+    P, C, mb, nt = case.prior_len, case.chunk_len, case.cache.max_blocks, case.num_tiles
+    out = torch.empty(C, sh.num_q_heads, sh.head_dim, device="cuda")
+    sel = torch.empty(nt, sh.num_kv_heads, sh.top_k, dtype=torch.int32, device="cuda")
+    pooled = torch.empty(nt, sh.num_kv_heads, mb, device="cuda")
+    msa.msa_index_score_prefill(p, kv, case.idx_q, P, C, pooled)
+    msa.msa_block_topk_prefill(p, P, C, mb, pooled, sel)
+    msa.msa_sparse_attn_prefill(p, kv, case.q, P, C, sel, out)
+    torch.cuda.synchronize()
+    log("[bench] mfma probe done")
+
+
+def summarize_mfma(counter_csv, out_txt, command):
+    """MFMA work and busy fraction per kernel from a counter run of
+    --mfma-probe (SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES,
+    GRBM_GUI_ACTIVE): counted flops = MOPS x 512, checked on the issue loop
+    whose flops are known; busy = busy cycles / (active cycles x SIMDs).  The
+    per-dispatch GRBM_GUI_ACTIVE is the sum over the XCDs' GRBM instances, so
+    it is divided by the XCD count (Num_Xcc of the run's agent info)."""
+    import csv
+    import msa_inputs as mi
+    n_xcc, n_simd = 8, 1024
+    agent_csv = os.path.join(os.path.dirname(counter_csv), "run_agent_info.csv")
+    if os.path.exists(agent_csv):
+        for r in csv.DictReader(open(agent_csv)):
+            if r.get("Name", "").startswith("gfx"):
+                n_xcc, n_simd = int(r["Num_Xcc"]), int(r["Simd_Count"])
+    w = mi.WORKLOADS[PREFILL_WORKLOAD]
+    index_flops, attn_flops = prefill_algorithmic_flops(w.shape, w.prior_len, w.chunk_len)
+    known = {"mfma_loop_kernel": 32768.0 * 16 * MFMA_PROBE_ITERS * MFMA_PROBE_WORKGROUPS,
+             "index_score_prefill_kernel": float(index_flops),
+             "prefill_attn_kernel": float(attn_flops)}
+    rows = {}
+    for r in csv.DictReader(open(counter_csv)):
+        name = next((k for k in known if k in r["Kernel_Name"]), None)
+        if name is None:
+            continue
+        d = rows.setdefault((name, r["Dispatch_Id"]), {
+            "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    lines = ["rocprofv3 MFMA counters (one dispatch each)", "", "command:", "  " + command, "",
+             "counted TFLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; algorithmic TFLOP as the "
+             "bench counts them (exact causal);",
+             "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / %d XCDs x %d SIMDs)"
+             % (n_xcc, n_simd), "",
+             "%-30s %12s %12s %8s %10s %10s" % ("kernel", "counted TF", "algo TF", "ratio",
+                                                "busy %", "us")]
+    for (name, _), d in sorted(rows.items()):
+        counted = d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        active = d.get("GRBM_GUI_ACTIVE", 0.0) / n_xcc
+        busy = 100.0 * d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / max(1.0, active * n_simd)
+        lines.append("%-30s %12.4f %12.4f %8.3f %10.1f %10.1f" % (
+            name, counted / 1e12, known[name] / 1e12, counted / known[name], busy, d["us"]))
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def summarize_kernel_trace(trace_csv, out_txt, command):
@@ -593,6 +720,11 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=4,
                     metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON", "CMD"),
                     help="write the profiles/ traffic summary of two counter runs")
+    ap.add_argument("--summarize-mfma", nargs=3, metavar=("COUNTER_CSV", "OUT_TXT", "CMD"),
+                    help="write the profiles/ summary of an MFMA counter run")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="for rocprofv3 counter runs: the MFMA issue loop (calibration), then "
+                         "one index, TopK and attention launch of the 1M prefill; no timing")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for rocprofv3 counter runs: one 128 MiB device copy (the "
                          "calibration), then 8 decode index-kernel launches; no timing")
@@ -602,6 +734,9 @@ def main():
         return
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -619,11 +754,15 @@ def main():
     if args.traffic_probe:
         traffic_probe(args, torch, msa, mi, gu)
         return
+    if args.mfma_probe:
+        mfma_probe(args, torch, msa, mi, gu)
+        return
 
     dec = run_decode_bench(args, torch, msa, mi, gu)
     lay = run_layers_bench(args, torch, msa, mi, dec) if args.layers > 0 else None
     gk = run_group_keys_bench(args, torch, msa, mi, gu) if not args.no_ablation else None
-    peaks = practical_peaks(torch) if not args.no_ablation else None
+    peaks = practical_peaks(torch)
+    roofs = measured_peaks(torch, msa)
     pre = None if args.no_prefill else run_prefill_bench(args, torch, msa, mi, gu)
     var = (run_varlen_bench(args, torch, msa, mi, gu)
            if not args.no_prefill and args.varlen_chunk > 0 else None)
@@ -655,6 +794,11 @@ def main():
         "decode_step_gbps": round(step_gbps, 1),
         "decode_step_bytes": dec["step_bytes"],
         "decode_append_us_per_step": round(dec["ms_append_step"] * 1e3, 3),
+        "decode_us_per_step_percentiles": dict(
+            {q: round(dec["ms_each"][min(len(dec["ms_each"]) - 1, int(f * len(dec["ms_each"])))]
+                      * 1e3, 3) for q, f in (("p10", 0.1), ("p50", 0.5), ("p90", 0.9))},
+            note="per-call intervals between event markers on the launch stream; each "
+                 "includes one marker, which back-to-back steps (value) do not"),
         "roofline": {
             "kernel": "index_score_decode",
             "bound": "hbm",
@@ -665,7 +809,10 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": dec["index_bytes"],
             "avg_launch_us": round(dec["ms_index"] * 1e3, 3),
+            "practical_peak": roofs["hbm_read_stream_gbps"],
+            "frac_of_practical": round(index_gbps / roofs["hbm_read_stream_gbps"], 4),
         },
+        "practical_peaks": roofs,
     }
     if pre is not None:
         pc = pre["case"]
@@ -685,6 +832,11 @@ def main():
                                     / BF16_PEAK_TFLOPS, 4),
             "index_flops": pre["index_flops"], "attn_flops": pre["attn_flops"],
             "peak_tflops": BF16_PEAK_TFLOPS,
+            "practical_peak_tflops": roofs["mfma_bf16_tflops"],
+            "index_frac_of_practical": round(pre["index_flops"] / (pre["ms_index"] * 1e-3) / 1e12
+                                             / roofs["mfma_bf16_tflops"], 4),
+            "attn_frac_of_practical": round(pre["attn_flops"] / (pre["ms_attn"] * 1e-3) / 1e12
+                                            / roofs["mfma_bf16_tflops"], 4),
             "chunk_append_us": round(pre["ms_append"] * 1e3, 2),
             "chunk_append_gbps": round(pre["append_bytes"] / (pre["ms_append"] * 1e-3) / 1e9, 1),
         }
@@ -694,8 +846,7 @@ def main():
         result["batched_prefill"] = var
     if gk is not None:
         result["ablation_group_index_keys"] = gk
-    if peaks is not None:
-        result["library_reference"] = peaks
+    result["library_reference"] = peaks
     if args.cpu_budget > 0:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     else:

@@ -21,7 +21,8 @@ __all__ = [
     "msa_prefill_workspace_bytes", "msa_prefill_chunk", "msa_index_score_prefill",
     "msa_block_topk_prefill", "msa_sparse_attn_prefill", "msa_last_error", "msa_version",
     "PagedKVMut", "make_kv_mut", "msa_cache_append", "msa_decode_append",
-    "msa_prefill_varlen_workspace_bytes", "msa_prefill_varlen",
+    "msa_prefill_varlen_workspace_bytes", "msa_prefill_varlen", "msa_probe_read_stream",
+    "msa_probe_mfma_bf16",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -94,6 +95,8 @@ def lib():
                                                   sz, vp]),
             "msa_last_error": (ctypes.c_char_p, []),
             "msa_version": (ctypes.c_char_p, []),
+            "msa_probe_read_stream": (ctypes.c_int, [vp, sz, i32, vp, vp]),
+            "msa_probe_mfma_bf16": (ctypes.c_int, [i32, i32, vp, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -281,3 +284,16 @@ def msa_prefill_varlen(params: Params, kv: PagedKV, q, idx_q, prior_lens, chunk_
                                     _dev(out, torch.float32, "out"), _dev(sel, torch.int32, "sel"),
                                     _dev(workspace, None, "workspace"), ws_bytes,
                                     _stream(stream)))
+
+
+# ------------------------------------------------------------ measurement
+def msa_probe_read_stream(src: torch.Tensor, workgroups: int, sink: torch.Tensor,
+                          stream=None) -> None:
+    """One non-temporal read pass over src (any dtype, contiguous GPU tensor)."""
+    _check(lib().msa_probe_read_stream(_dev(src, None, "src"), src.numel() * src.element_size(),
+                                       workgroups, _dev(sink, None, "sink"), _stream(stream)))
+
+
+def msa_probe_mfma_bf16(iters: int, workgroups: int, sink: torch.Tensor, stream=None) -> None:
+    """32768 * 16 * iters * workgroups flops of v_mfma_f32_32x32x16_bf16."""
+    _check(lib().msa_probe_mfma_bf16(iters, workgroups, _dev(sink, None, "sink"), _stream(stream)))

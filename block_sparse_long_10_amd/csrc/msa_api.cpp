@@ -13,6 +13,7 @@
 
 #include "msa.h"
 #include "msa_launch.h"
+#include "msa_probes.h"
 
 namespace {
 
@@ -492,3 +493,28 @@ msa_status msa_prefill_varlen(const msa_params* params, const msa_paged_kv* kv, 
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------ measurement
+extern "C" msa_status msa_probe_read_stream(const void* src, size_t bytes, int32_t workgroups,
+                                            uint32_t* sink, void* stream) {
+  if (src == nullptr || sink == nullptr)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "src and sink must not be NULL");
+  if (bytes < 16 || bytes % 16 != 0)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "bytes must be a positive multiple of 16");
+  if (workgroups < 1 || workgroups > 65536)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "workgroups must be in [1, 65536]");
+  return hip_status(msa::launch_read_stream(src, bytes, workgroups, sink,
+                                            static_cast<hipStream_t>(stream)),
+                    "read stream launch");
+}
+
+extern "C" msa_status msa_probe_mfma_bf16(int32_t iters, int32_t workgroups, float* sink,
+                                          void* stream) {
+  if (sink == nullptr) return fail(MSA_ERR_INVALID_ARGUMENT, "sink must not be NULL");
+  if (iters < 1 || iters > (1 << 24))
+    return fail(MSA_ERR_INVALID_ARGUMENT, "iters must be in [1, 2^24]");
+  if (workgroups < 1 || workgroups > 65536)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "workgroups must be in [1, 65536]");
+  return hip_status(msa::launch_mfma_loop(iters, workgroups, sink, static_cast<hipStream_t>(stream)),
+                    "mfma loop launch");
+}

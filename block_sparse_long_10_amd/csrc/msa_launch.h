@@ -86,6 +86,11 @@ hipError_t launch_chunk_map(const int32_t* prior_lens, const int32_t* chunk_lens
                             int32_t block_size, int32_t num_tiles, int32_t* tile_seq,
                             int32_t* tile_start, int32_t* q_start, hipStream_t stream);
 
+// Measurement kernels (peak_probes.hip).
+hipError_t launch_read_stream(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink,
+                              hipStream_t stream);
+hipError_t launch_mfma_loop(int32_t iters, int32_t workgroups, float* sink, hipStream_t stream);
+
 // Step 1, prefill: pooled[u][g][b] for b < own(u) = prior/B + t; max_own is
 // the largest own block of the call.
 hipError_t launch_index_score_prefill(const Dims& d, const Cache& c, const uint16_t* idx_q,

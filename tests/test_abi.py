@@ -13,15 +13,18 @@ from block_sparse_long_10_amd import Params, PagedKV
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "msa.h")
+HEADERS = [HEADER, os.path.join(ROOT, "include", "msa_probes.h")]
 
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
 FAKE = 0x10000  # a non-null address; never dereferenced by a rejected call
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(msa_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(msa_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
@@ -30,7 +33,8 @@ def test_header_declares_the_entry_points():
               "msa_prefill_workspace_bytes", "msa_last_error", "msa_index_score_decode",
               "msa_index_score_prefill", "msa_block_topk_prefill", "msa_sparse_attn_prefill",
               "msa_cache_append", "msa_decode_append", "msa_prefill_varlen",
-              "msa_prefill_varlen_workspace_bytes"]:
+              "msa_prefill_varlen_workspace_bytes", "msa_probe_read_stream",
+              "msa_probe_mfma_bf16"]:
         assert n in names
 
 
@@ -206,3 +210,27 @@ def test_varlen_prefill_rejects_bad_arguments():
     assert need > 0
     assert st([10, 300], [5, 40], wsb=need - 1) == WORKSPACE
     assert L.msa_prefill_varlen_workspace_bytes(ctypes.byref(p), arr([10]), arr([0]), 1, 40) == 0
+
+
+@pytest.mark.parametrize("args,msg", [
+    ((None, 1024, 8, FAKE), "NULL"),
+    ((FAKE, 1024, 8, None), "NULL"),
+    ((FAKE, 0, 8, FAKE), "multiple of 16"),
+    ((FAKE, 1000, 8, FAKE), "multiple of 16"),
+    ((FAKE, 1024, 0, FAKE), "workgroups"),
+    ((FAKE, 1024, 65537, FAKE), "workgroups"),
+])
+def test_read_stream_probe_rejects_bad_arguments(args, msg):
+    assert msa.lib().msa_probe_read_stream(*args, None) == INVALID
+    assert msg in msa.msa_last_error()
+
+
+@pytest.mark.parametrize("args,msg", [
+    ((0, 8, FAKE), "iters"),
+    ((1 << 25, 8, FAKE), "iters"),
+    ((16, 0, FAKE), "workgroups"),
+    ((16, 8, None), "NULL"),
+])
+def test_mfma_probe_rejects_bad_arguments(args, msg):
+    assert msa.lib().msa_probe_mfma_bf16(*args, None) == INVALID
+    assert msg in msa.msa_last_error()
