@@ -188,6 +188,46 @@ def run_decode_bench(args, torch, msa, mi, gu):
     }
 
 
+OTHER_DECODE_WORKLOADS = (("decode_b1_L4k", 4), ("decode_b8_L128k", 4), ("decode_paged_b32", 2))
+
+
+def run_other_decode_bench(args, torch, msa, mi, gu):
+    """Step time of the other decode workloads (parity cases; reported for
+    context): rotated buffer sets as for the headline, so that the index keys
+    are not served from the Infinity Cache where they exceed it."""
+    res = {}
+    for name, rot in OTHER_DECODE_WORKLOADS:
+        log("[bench] decode %s x%d buffer sets" % (name, rot))
+        base = mi.make_workload(name, "cuda")
+        sets = [base] + [clone_decode_case(base) for _ in range(rot - 1)]
+        sh = base.shape
+        p = gu.params_of(sh)
+        kvs = [gu.kv_of(c) for c in sets]
+        batch, maxL, mb = base.batch, max(base.lengths), base.cache.max_blocks
+        out = torch.empty(batch, sh.num_q_heads, sh.head_dim, device="cuda")
+        sel = torch.empty(batch, sh.num_kv_heads, sh.top_k, dtype=torch.int32, device="cuda")
+        ws = torch.empty(msa.msa_decode_workspace_bytes(p, batch, mb), dtype=torch.uint8,
+                         device="cuda")
+
+        calls = [0]
+
+        def step():
+            i = calls[0] % len(sets)
+            calls[0] += 1
+            c = sets[i]
+            msa.msa_decode(p, kvs[i], c.q, c.idx_q, c.seq_lens, batch, maxL, out, sel, ws)
+
+        ms = _timed_ms(torch, step, 50, 5)
+        idx_b, kv_b, small = decode_algorithmic_bytes(base)
+        total = idx_b + kv_b + small
+        res[name] = {"batch": batch, "context_tokens": int(sum(base.lengths)),
+                     "us_per_step": round(ms * 1e3, 3), "algorithmic_bytes": total,
+                     "gbps": round(total / (ms * 1e-3) / 1e9, 1), "rotated_buffer_sets": rot}
+        del sets, kvs, base, out, sel, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def current_token_rows(torch, case):
     """k, v [batch][Hkv][D] and idx_k [batch][d_i] of each sequence's current
     token, read out of its page (the rows a decode-with-append call writes)."""
@@ -709,6 +749,8 @@ def main():
                     help="layers of the multi-layer decode leg (0 = skip)")
     ap.add_argument("--layer-tokens", type=int, default=20,
                     help="tokens timed in the multi-layer decode leg")
+    ap.add_argument("--no-other-decode", action="store_true",
+                    help="skip the step times of the other decode workloads")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the per-group index-key ablation leg")
     ap.add_argument("--varlen-chunk", type=int, default=512,
@@ -761,6 +803,7 @@ def main():
     dec = run_decode_bench(args, torch, msa, mi, gu)
     lay = run_layers_bench(args, torch, msa, mi, dec) if args.layers > 0 else None
     gk = run_group_keys_bench(args, torch, msa, mi, gu) if not args.no_ablation else None
+    other = run_other_decode_bench(args, torch, msa, mi, gu) if not args.no_other_decode else None
     peaks = practical_peaks(torch)
     roofs = measured_peaks(torch, msa)
     pre = None if args.no_prefill else run_prefill_bench(args, torch, msa, mi, gu)
@@ -846,6 +889,8 @@ def main():
         result["batched_prefill"] = var
     if gk is not None:
         result["ablation_group_index_keys"] = gk
+    if other is not None:
+        result["other_decode_workloads"] = other
     result["library_reference"] = peaks
     if args.cpu_budget > 0:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)

@@ -190,10 +190,13 @@ __device__ __forceinline__ void merge_partials(__amdgpu_buffer_rsrc_t ro, __amdg
   const int tid = threadIdx.x;
   // item = (head h, dims 4*d4 .. +3): group*32 of them, one or two per thread
   const int items = group * 32;
+  // one item and one chunk per thread (uniform): the thread's partials are
+  // loaded while the weights are formed (slots past top_k read beyond the
+  // buffer range: zeros); otherwise they are loaded chunk by chunk after
+  // (so that only one chunk of registers is ever live)
+  const bool single = items <= 256 && top_k <= kChunk;
   f32x4 o[kChunk];
-  // the first chunk of the thread's first item is loaded while the weights
-  // are formed (slots past top_k read beyond the buffer range: zeros)
-  {
+  if (single) {
     const int h = tid >> 5, d4 = tid & 31;
 #pragma unroll
     for (int k = 0; k < kChunk; ++k)
@@ -235,33 +238,35 @@ __device__ __forceinline__ void merge_partials(__amdgpu_buffer_rsrc_t ro, __amdg
     }
   }
   __syncthreads();
-  auto fold = [&](int h, int k0, f32x4& acc) {
-#pragma unroll
-    for (int k = 0; k < kChunk; ++k) {
-      const float w = k0 + k < top_k ? ms.w[h][k0 + k] : 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = fmaf(w, o[k][j], acc[j]);
-    }
-  };
-  auto reload = [&](int h, int d4, int k0) {
-#pragma unroll
-    for (int k = 0; k < kChunk; ++k)
-      o[k] = load_shared4(ro, (((k0 + k) * group + h) * 128 + 4 * d4) * 4);
-  };
-  if (items <= 256 && top_k <= kChunk) {  // one item and one chunk per thread (uniform)
+  if (single) {
     if (tid >= items) return;
     const int h = tid >> 5, d4 = tid & 31;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    fold(h, 0, acc);
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) {
+      const float w = k < top_k ? ms.w[h][k] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = fmaf(w, o[k][j], acc[j]);
+    }
     *reinterpret_cast<f32x4*>(out_sg + (size_t)h * 128 + 4 * d4) = acc;
     return;
   }
+  // general case (group 16, or more than 16 slots): small chunks
+  constexpr int kLoopChunk = 4;
   for (int it = tid; it < items; it += 256) {
     const int h = it >> 5, d4 = it & 31;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < top_k; k0 += kChunk) {
-      if (k0 > 0 || it != tid) reload(h, d4, k0);
-      fold(h, k0, acc);
+    for (int k0 = 0; k0 < top_k; k0 += kLoopChunk) {
+      f32x4 ol[kLoopChunk];
+#pragma unroll
+      for (int k = 0; k < kLoopChunk; ++k)
+        ol[k] = load_shared4(ro, (((k0 + k) * group + h) * 128 + 4 * d4) * 4);
+#pragma unroll
+      for (int k = 0; k < kLoopChunk; ++k) {
+        const float w = k0 + k < top_k ? ms.w[h][k0 + k] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = fmaf(w, ol[k][j], acc[j]);
+      }
     }
     *reinterpret_cast<f32x4*>(out_sg + (size_t)h * 128 + 4 * d4) = acc;
   }
