@@ -7,6 +7,9 @@
 // becomes an order-preserving 32-bit key (-0.0 folded into +0.0), held in
 // registers when own <= 256*MAXV (all loads issued at once; empty slots hold
 // key 0, below every finite score), otherwise re-read from global memory.
+// The general path below always re-reads them (it runs only when the fast
+// path fails), so the registers of the fast path are free for the caller's
+// other phases.
 //
 // Fast path (registers): each thread takes the max of its keys; an LDS
 // histogram of the 256 thread maxima gives T, the lowest key of the bin that
@@ -550,11 +553,13 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ scores, int
   } else if (own <= kTopkThreads * 32) {
     RegKeys<32> src;
     src.load(scores, own);
-    if (!topk_fast(src, own, keep, k, out_sel, sh)) topk_select(src, own, k, out_sel, sh);
+    if (!topk_fast(src, own, keep, k, out_sel, sh))
+      topk_select(GlobalKeys{scores, own}, own, k, out_sel, sh);
   } else if (WIDE && own <= kTopkThreads * 64) {
     RegKeys<64> src;
     src.load(scores, own);
-    if (!topk_fast(src, own, keep, k, out_sel, sh)) topk_select(src, own, k, out_sel, sh);
+    if (!topk_fast(src, own, keep, k, out_sel, sh))
+      topk_select(GlobalKeys{scores, own}, own, k, out_sel, sh);
   } else {
     GlobalKeys src{scores, own};
     topk_select(src, own, k, out_sel, sh);
