@@ -487,19 +487,33 @@ def _timed_ms(torch, fn, reps, warm):
 
 def measured_peaks(torch, msa):
     """The practical roofs, from the library's measurement kernels: a plain
-    non-temporal read stream over 2 GiB (far beyond the 256 MB Infinity
-    Cache) and a loop of independent bf16 MFMA chains; the best launch shape
-    of a small sweep each."""
+    non-temporal read stream (one wave per 16 KiB chunk, as the decode index
+    kernel streams its pages) over 2 GiB, far beyond the 256 MB Infinity
+    Cache, and over 128 MiB rotated across four buffers (the size of the
+    1M-token index-key stream, launch ramp and tail included); and a loop of
+    independent bf16 MFMA chains.  The best launch shape of a small sweep."""
     log("[bench] practical peaks: read stream and bf16 MFMA loop")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     nbytes = 1 << 31
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     src.fill_(1)
-    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     read = []
-    for wg in (2048, 4096, 8192, 16384, 32768):
+    for wg in (8192, 32768, 131072):
         ms = _timed_ms(torch, lambda: msa.msa_probe_read_stream(src, wg, sink), 10, 2)
         read.append((nbytes / (ms * 1e-3) / 1e9, wg))
     del src
+    small = 128 << 20
+    bufs = [torch.empty(small, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    for b in bufs:
+        b.fill_(1)
+    calls = [0]
+
+    def rotated():
+        msa.msa_probe_read_stream(bufs[calls[0] % 4], small // 16384, sink)
+        calls[0] += 1
+
+    ms_small = _timed_ms(torch, rotated, 40, 8)
+    del bufs
     iters = 4096
     mfma = []
     for wg in (1024, 2048, 4096):
@@ -507,9 +521,11 @@ def measured_peaks(torch, msa):
         mfma.append((32768.0 * 16 * iters * wg / (ms * 1e-3) / 1e12, wg))
     (gbps, rwg), (tflops, mwg) = max(read), max(mfma)
     return {"hbm_read_stream_gbps": round(gbps, 1), "read_stream_workgroups": rwg,
+            "hbm_read_stream_128mib_gbps": round(small / (ms_small * 1e-3) / 1e9, 1),
             "mfma_bf16_tflops": round(tflops, 1), "mfma_workgroups": mwg,
-            "note": "msa_probe_read_stream over 2 GiB, msa_probe_mfma_bf16 (4 chains of "
-                    "v_mfma_f32_32x32x16_bf16 per wave); best of a launch-shape sweep"}
+            "note": "msa_probe_read_stream over 2 GiB, and over 128 MiB rotated over 4 "
+                    "buffers (one 16 KiB chunk per workgroup); msa_probe_mfma_bf16 (4 chains "
+                    "of v_mfma_f32_32x32x16_bf16 per wave); best of a launch-shape sweep"}
 
 
 def practical_peaks(torch):
@@ -804,11 +820,13 @@ def main():
     lay = run_layers_bench(args, torch, msa, mi, dec) if args.layers > 0 else None
     gk = run_group_keys_bench(args, torch, msa, mi, gu) if not args.no_ablation else None
     other = run_other_decode_bench(args, torch, msa, mi, gu) if not args.no_other_decode else None
-    peaks = practical_peaks(torch)
-    roofs = measured_peaks(torch, msa)
     pre = None if args.no_prefill else run_prefill_bench(args, torch, msa, mi, gu)
     var = (run_varlen_bench(args, torch, msa, mi, gu)
            if not args.no_prefill and args.varlen_chunk > 0 else None)
+    # after the prefill legs: the MFMA loop and the library GEMM heat the chip,
+    # and the prefill index kernel is power-limited
+    peaks = practical_peaks(torch)
+    roofs = measured_peaks(torch, msa)
 
     case = dec["case"]
     sh = case.shape
@@ -852,8 +870,9 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": dec["index_bytes"],
             "avg_launch_us": round(dec["ms_index"] * 1e3, 3),
-            "practical_peak": roofs["hbm_read_stream_gbps"],
-            "frac_of_practical": round(index_gbps / roofs["hbm_read_stream_gbps"], 4),
+            "practical_peak": roofs["hbm_read_stream_128mib_gbps"],
+            "frac_of_practical": round(index_gbps / roofs["hbm_read_stream_128mib_gbps"], 4),
+            "practical_peak_note": "read stream of the same size (128 MiB)",
         },
         "practical_peaks": roofs,
     }

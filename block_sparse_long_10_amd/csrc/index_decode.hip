@@ -56,22 +56,26 @@ __global__ __launch_bounds__(64) void index_score_decode_kernel(
   const int lane = threadIdx.x;
   if (counters != nullptr && blockIdx.x == 0 && gz == 0 && lane < num_kv_heads)
     counters[s * num_kv_heads + lane] = 0u;
-  const int L = seq_lens[s];
   // with an append, workgroup 0 (dispatched first, so its latency hides
   // behind the scoring) writes the current token and block b is scored by
   // workgroup b + 1
   int b = blockIdx.x;
   if (ap.k_new != nullptr) {
     if (b == 0) {
-      if (gz == 0) append_current_token<B>(ap, s, L, num_kv_heads, idx_k_heads);
+      if (gz == 0) append_current_token<B>(ap, s, seq_lens[s], num_kv_heads, idx_k_heads);
       return;
     }
     --b;
   }
-  const int own = (L - 1) / B;
-  if (b >= own) return;
-  float* out = pooled + (size_t)s * num_kv_heads * max_blocks + b;
+  // the page id is read together with the length (one round trip): every
+  // launched b is below (max_seq_len - 1) / B < max_blocks, so the entry
+  // exists; the exit test reads both, which keeps the two loads side by side
+  // (a negative page id, outside the contract, is never dereferenced)
   const int32_t page = block_table[(size_t)s * max_blocks + b];
+  const int L = seq_lens[s];
+  const int own = (L - 1) / B;
+  if (b >= own || page < 0) return;
+  float* out = pooled + (size_t)s * num_kv_heads * max_blocks + b;
   if constexpr (PG) {
     index_block_scores<B, NI, 1>(idx_k, page * idx_k_heads + gz,
                                  idx_q + ((size_t)s * num_kv_heads + gz) * NI * 64, 1, stage,

@@ -501,8 +501,8 @@ extern "C" msa_status msa_probe_read_stream(const void* src, size_t bytes, int32
     return fail(MSA_ERR_INVALID_ARGUMENT, "src and sink must not be NULL");
   if (bytes < 16 || bytes % 16 != 0)
     return fail(MSA_ERR_INVALID_ARGUMENT, "bytes must be a positive multiple of 16");
-  if (workgroups < 1 || workgroups > 65536)
-    return fail(MSA_ERR_INVALID_ARGUMENT, "workgroups must be in [1, 65536]");
+  if (workgroups < 1 || workgroups > (1 << 20))
+    return fail(MSA_ERR_INVALID_ARGUMENT, "workgroups must be in [1, 2^20]");
   return hip_status(msa::launch_read_stream(src, bytes, workgroups, sink,
                                             static_cast<hipStream_t>(stream)),
                     "read stream launch");

@@ -8,23 +8,25 @@ namespace msa {
 
 constexpr uint32_t kProbeMagic = 0x9E3779B9u;
 
-// Grid-stride pass over n16 16-byte words; eight loads in flight per
-// iteration.  Consecutive threads read consecutive words, so one wave load
-// instruction covers 1 KiB.
-__global__ __launch_bounds__(256) void read_stream_kernel(const u32x4* __restrict__ src,
-                                                          size_t n16, uint32_t* __restrict__ sink) {
-  constexpr int kInFlight = 8;
-  const size_t stride = (size_t)gridDim.x * 256;
-  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+// One wave per workgroup; workgroup w reads the 16 KiB chunks w, w + grid,
+// ... with sixteen 1 KiB wave loads in flight (consecutive lanes read
+// consecutive 16-byte words), then the words past the last whole chunk.
+__global__ __launch_bounds__(64) void read_stream_kernel(const u32x4* __restrict__ src,
+                                                         size_t n16, uint32_t* __restrict__ sink) {
+  constexpr int kLoads = 16;
+  const size_t nchunk = n16 / (kLoads * 64);
   u32x4 acc = {0u, 0u, 0u, 0u};
-  for (; i + (kInFlight - 1) * stride < n16; i += kInFlight * stride) {
-    u32x4 v[kInFlight];
+  for (size_t c = blockIdx.x; c < nchunk; c += gridDim.x) {
+    const u32x4* p = src + c * (kLoads * 64) + threadIdx.x;
+    u32x4 v[kLoads];
 #pragma unroll
-    for (int u = 0; u < kInFlight; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+    for (int u = 0; u < kLoads; ++u) v[u] = __builtin_nontemporal_load(p + u * 64);
 #pragma unroll
-    for (int u = 0; u < kInFlight; ++u) acc ^= v[u];
+    for (int u = 0; u < kLoads; ++u) acc ^= v[u];
   }
-  for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(src + i);
+  for (size_t i = nchunk * (kLoads * 64) + (size_t)blockIdx.x * 64 + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * 64)
+    acc ^= __builtin_nontemporal_load(src + i);
   const uint32_t v = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
   if (v == kProbeMagic) sink[0] = v;
 }
@@ -53,7 +55,7 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int32_t iters, float* __
 
 hipError_t launch_read_stream(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink,
                               hipStream_t stream) {
-  hipLaunchKernelGGL(read_stream_kernel, dim3(workgroups), dim3(256), 0, stream,
+  hipLaunchKernelGGL(read_stream_kernel, dim3(workgroups), dim3(64), 0, stream,
                      static_cast<const u32x4*>(src), bytes / 16, sink);
   return hipGetLastError();
 }

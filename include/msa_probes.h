@@ -29,10 +29,13 @@ extern "C" {
 #endif
 
 /* Reads `bytes` (a multiple of 16, >= 16) from device memory `src` once,
- * with `workgroups` 256-thread workgroups (1 .. 65536) in a grid-stride
- * loop; every wave load instruction covers 1 KiB of consecutive bytes.  The
- * data are folded into a value that is written to sink[0] (device, 4 bytes)
- * only if it equals an improbable constant, so no write traffic arises. */
+ * with `workgroups` one-wave workgroups (1 .. 1048576): workgroup
+ * w streams the 16 KiB chunks w, w + workgroups, ... with sixteen 1 KiB wave
+ * loads in flight (the pattern of the decode index kernel, which streams one
+ * 16 KiB page of index keys per wave), then the bytes past the last whole
+ * chunk.  The data are folded into a value that is written to sink[0]
+ * (device, 4 bytes) only if it equals an improbable constant, so no write
+ * traffic arises. */
 msa_status msa_probe_read_stream(const void *src, size_t bytes, int32_t workgroups,
                                  uint32_t *sink, void *stream);
 

@@ -218,7 +218,7 @@ def test_varlen_prefill_rejects_bad_arguments():
     ((FAKE, 0, 8, FAKE), "multiple of 16"),
     ((FAKE, 1000, 8, FAKE), "multiple of 16"),
     ((FAKE, 1024, 0, FAKE), "workgroups"),
-    ((FAKE, 1024, 65537, FAKE), "workgroups"),
+    ((FAKE, 1024, (1 << 20) + 1, FAKE), "workgroups"),
 ])
 def test_read_stream_probe_rejects_bad_arguments(args, msg):
     assert msa.lib().msa_probe_read_stream(*args, None) == INVALID
