@@ -3,21 +3,21 @@
 // own block always kept ("TopK" of the index branch in "MiniMax wird dünn",
 // section 1, Schritt 1).
 //
-// One 256-thread workgroup selects from scores[0 .. own).  Every score
-// becomes an order-preserving 32-bit key (-0.0 folded into +0.0), held in
-// registers when own <= 256*MAXV (all loads issued at once; empty slots hold
-// key 0, below every finite score), otherwise re-read from global memory.
-// The general path below always re-reads them (it runs only when the fast
-// path fails), so the registers of the fast path are free for the caller's
-// other phases.
+// One 256-thread workgroup selects from scores[0 .. own).  A score's rank is
+// that of its order-preserving 32-bit key (-0.0 folded into +0.0).
 //
-// Fast path (registers): each thread takes the max of its keys; an LDS
-// histogram of the 256 thread maxima gives T, the lowest key of the bin that
-// completes k' = k-1 maxima; those k' distinct scores reach T, so it bounds
-// the k'-th best score from below.  The few keys >= T are gathered to LDS
-// (DPP prefix-sum offsets), ranked by counting against each other, and the
-// winners are put in block order by a wave-wide DPP bitonic sort.  If more
-// than 64 keys reach T (heavy ties), the general path below runs instead:
+// Fast path (own <= 256*MAXV): the scores are loaded into registers, all
+// loads at once (-inf in the slots past the row).  Each thread takes the max
+// of its scores; an LDS histogram of the 256 thread maxima gives T, the
+// lowest key of the bin that completes k' = k-1 maxima; those k' distinct
+// scores reach T, so it bounds the k'-th best score from below.  The few
+// scores >= T are gathered to LDS (DPP prefix-sum offsets), sorted by
+// (score, index) with a wave-wide DPP bitonic sort, and the winners put in
+// block order by a second one; each sort network is only as wide as its
+// count.  If more than 64 scores reach T (heavy ties), or the row is longer
+// than the registers hold, the general path runs instead, on keys re-read
+// from memory (so the fast path's registers are free for the caller's other
+// phases):
 //   1. key range [lo, hi] (DPP/shuffle wave reductions + LDS);
 //   2. LDS histogram of bin = (hi - key) >> shift, at most 256 bins; the bin
 //      is monotone in the key, so every item of a lower bin outranks every
@@ -92,13 +92,11 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 }
 constexpr uint32_t kKeyMinFinite = 0x00800000u;  // order_key(-FLT_MAX); -inf maps below it
 
-// Scores held in registers: item i = j*256 + tid lives in val[j] (-inf in
-// the slots past the row).  The fast path compares the floats themselves;
-// keys are formed only for thread maxima and candidates, and by the general
-// path through each() / chunks_in_order().
+// Scores held in registers for the fast path: item i = j*256 + tid lives in
+// val[j] (-inf in the slots past the row).  The fast path compares the
+// floats themselves and forms keys only for thread maxima and candidates.
 template <int MAXV>
 struct RegKeys {
-  static constexpr int kChunks = MAXV;
   float val[MAXV];
   int n;
   __device__ __forceinline__ void load(const float* __restrict__ s, int n_) {
@@ -110,29 +108,10 @@ struct RegKeys {
       val[j] = i < n ? s[i] : -INFINITY;
     }
   }
-  template <class F>
-  __device__ __forceinline__ void each(F&& f) const {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < MAXV; ++j) {
-      const int i = j * kTopkThreads + tid;
-      if (i < n) f(i, order_key(val[j]));
-    }
-  }
-  // f(i, key, valid) for chunks of 256 consecutive items in index order,
-  // called by all threads; stops when f returns false (a uniform decision).
-  template <class F>
-  __device__ __forceinline__ void chunks_in_order(F&& f) const {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < MAXV; ++j) {
-      const int i = j * kTopkThreads + tid;
-      if (!f(i, i < n ? order_key(val[j]) : 0u, i < n)) break;
-    }
-  }
 };
 
-// Keys re-read from global memory (very long contexts).
+// Keys re-read from global memory: the general path (heavy ties, or rows
+// longer than the registers hold).
 struct GlobalKeys {
   const float* __restrict__ s;
   int n;
