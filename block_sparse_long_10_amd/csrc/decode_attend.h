@@ -39,11 +39,16 @@ __device__ __forceinline__ f32x4 load_shared4(__amdgpu_buffer_rsrc_t r, uint32_t
 }
 
 // ------------------------------------------------------- block attention
-// Per-wave partials combined in LDS.
+// Per-wave partials combined in LDS: (max, sum) here, the outputs in a
+// region sized by the group, w_o[wave][head][kWoStride] (heads < group), which
+// the caller may reuse once the partial is stored.
 struct AttendShared {
   float w_m[4][16], w_l[4][16];
-  float w_o[4][16][128 + 4];
 };
+constexpr int kWoStride = 128 + 4;  // floats per (wave, head) row: conflict-free reads
+__host__ __device__ constexpr size_t attend_wo_bytes(int group) {
+  return (size_t)4 * group * kWoStride * sizeof(float);
+}
 
 // Attention of the G heads of group g of sequence s over kept block blk
 // (blk < 0: an empty slot) by a 256-thread workgroup: 4 waves x 32 tokens,
@@ -59,7 +64,8 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ kc,
                                              int blk, int L, const uint16_t* __restrict__ q_sg,
                                              int num_kv_heads, int g, int group, float scale_log2,
                                              int slot, __amdgpu_buffer_rsrc_t ro,
-                                             __amdgpu_buffer_rsrc_t rml, AttendShared& sh) {
+                                             __amdgpu_buffer_rsrc_t rml, AttendShared& sh,
+                                             float* __restrict__ w_o) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   if (blk < 0) {  // empty slot: weight zero in the merge, output zeros
     for (int h = tid; h < group; h += 256)
@@ -145,10 +151,13 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ kc,
     sh.w_m[wave][lane] = m_w;
     sh.w_l[wave][lane] = l_w;
   }
+  if (r16 < group) {
+    float* row = w_o + (wave * group + r16) * kWoStride;
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sh.w_o[wave][r16][16 * mt + 4 * q4 + j] = o[mt][j];
+      for (int j = 0; j < 4; ++j) row[16 * mt + 4 * q4 + j] = o[mt][j];
+  }
   __syncthreads();
   // combine the waves: thread -> (head h, dims 4*d4 .. +3)
   for (int idx = tid; idx < group * 32; idx += 256) {
@@ -164,7 +173,7 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ kc,
       const float e = exp2f(sh.w_m[w][h] - M);
       l += e * sh.w_l[w][h];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] += e * sh.w_o[w][h][4 * d4 + j];
+      for (int j = 0; j < 4; ++j) acc[j] += e * w_o[(w * group + h) * kWoStride + 4 * d4 + j];
     }
     store_shared4(ro, ((slot * group + h) * 128 + 4 * d4) * 4, acc);
     if (d4 == 0) store_shared4(rml, (slot * group + h) * 16, f32x4{M, l, 0.f, 0.f});

@@ -23,6 +23,8 @@
 // (K token-major, V^T dimension-major, XOR-swizzled 16-byte chunks) and
 // consumed 32 keys at a time with v_mfma_f32_32x32x16_bf16 and an online
 // softmax; the causal mask applies inside the tile's diagonal block only.
+#include <algorithm>
+
 #include "block_topk.h"
 #include "chunk_map.h"
 #include "decode_attend.h"
@@ -64,14 +66,13 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
     float* __restrict__ part_ml, uint32_t* __restrict__ counters, float* __restrict__ out) {
   __shared__ TopkShared tsh;
   __shared__ int sel_s[kMaxTopK], tmp_s[kMaxTopK];
-  // the merge runs after the block attention is done with its scratch
-  __shared__ union {
-    AttendShared ash;
-    MergeShared msh;
-  } scratch;
-  AttendShared& ash = scratch.ash;
-  MergeShared& msh = scratch.msh;
+  __shared__ AttendShared ash;
   __shared__ int is_last;
+  // dynamic LDS: the per-wave outputs of the block attention (sized by the
+  // group), then the merge's scratch (the merge runs after a barrier that
+  // follows the last read of the outputs)
+  extern __shared__ __attribute__((aligned(16))) float dyn_lds[];
+  MergeShared& msh = *reinterpret_cast<MergeShared*>(dyn_lds);
 
   // Workgroups are dispatched round-robin over the XCDs, each with its own
   // L2.  Taking the group from the low digits of the (slot, group) index puts
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
   const __amdgpu_buffer_rsrc_t rml = buffer_of(part_ml + sg * top_k * group * 4, ml_bytes);
   const int32_t page = blk >= 0 ? block_table[(size_t)s * max_blocks + blk] : 0;
   attend_block<B>(kc, vc, page, blk, L, q + ((size_t)s * Hq + (size_t)g * group) * 128,
-                  num_kv_heads, g, group, scale_log2, slot, ro, rml, ash);
+                  num_kv_heads, g, group, scale_log2, slot, ro, rml, ash, dyn_lds);
 
   // hand-off: stores complete, then count this slot in; the last slot
   // workgroup reads the partials with agent-scope loads issued after its
@@ -128,23 +129,26 @@ hipError_t launch_decode_attn(const Dims& d, const Cache& c, const uint16_t* q,
   const dim3 grid_sg(d.num_kv_heads, batch);
   const dim3 grid_attn(d.top_k, d.num_kv_heads, batch);
   const bool fused = (size_t)d.top_k * d.num_kv_heads * batch <= kFusedTopkMaxWorkgroups;
+  // the dynamic LDS (block outputs, then merge scratch) is sized by the group:
+  // at group 8 it is half the size of group 16's, so more workgroups fit a CU
+  const size_t dyn = std::max(attend_wo_bytes(G), sizeof(MergeShared));
 #define MSA_ATTN_ARGS c.k, c.v, c.block_table, c.max_blocks, q, seq_lens, pooled, sel, \
     d.num_kv_heads, G, d.top_k, d.sink_blocks, d.local_blocks, sl2, part_o, part_ml, counters, out
   if (d.block_size == 64) {
     if (fused) {
-      hipLaunchKernelGGL((decode_attn_kernel<64, true>), grid_attn, dim3(256), 0, stream, MSA_ATTN_ARGS);
+      hipLaunchKernelGGL((decode_attn_kernel<64, true>), grid_attn, dim3(256), dyn, stream, MSA_ATTN_ARGS);
     } else {
       hipLaunchKernelGGL(decode_topk_kernel<64>, grid_sg, dim3(256), 0, stream, pooled, seq_lens,
                          d.num_kv_heads, c.max_blocks, d.top_k, d.sink_blocks, d.local_blocks, sel);
-      hipLaunchKernelGGL((decode_attn_kernel<64, false>), grid_attn, dim3(256), 0, stream, MSA_ATTN_ARGS);
+      hipLaunchKernelGGL((decode_attn_kernel<64, false>), grid_attn, dim3(256), dyn, stream, MSA_ATTN_ARGS);
     }
   } else {
     if (fused) {
-      hipLaunchKernelGGL((decode_attn_kernel<128, true>), grid_attn, dim3(256), 0, stream, MSA_ATTN_ARGS);
+      hipLaunchKernelGGL((decode_attn_kernel<128, true>), grid_attn, dim3(256), dyn, stream, MSA_ATTN_ARGS);
     } else {
       hipLaunchKernelGGL(decode_topk_kernel<128>, grid_sg, dim3(256), 0, stream, pooled, seq_lens,
                          d.num_kv_heads, c.max_blocks, d.top_k, d.sink_blocks, d.local_blocks, sel);
-      hipLaunchKernelGGL((decode_attn_kernel<128, false>), grid_attn, dim3(256), 0, stream, MSA_ATTN_ARGS);
+      hipLaunchKernelGGL((decode_attn_kernel<128, false>), grid_attn, dim3(256), dyn, stream, MSA_ATTN_ARGS);
     }
   }
 #undef MSA_ATTN_ARGS
