@@ -50,7 +50,9 @@
  *   in 1..16.  Other values return MSA_ERR_UNSUPPORTED.  sink_blocks and
  *   local_blocks must be >= 0 with sink_blocks + local_blocks <= top_k - 1
  *   (else MSA_ERR_INVALID_ARGUMENT); num_idx_k_heads must be 0, 1 or
- *   num_kv_heads (else MSA_ERR_UNSUPPORTED).
+ *   num_kv_heads (else MSA_ERR_UNSUPPORTED).  The prefill calls also need
+ *   block_size * num_idx_heads <= 512 (one tile's query x index-head rows in
+ *   one workgroup), else MSA_ERR_UNSUPPORTED.
  *
  * Paged KV cache (one page holds one KV block of block_size tokens)
  * -----------------------------------------------------------------
