@@ -9,11 +9,9 @@ namespace msa {
 constexpr int kWave = 64;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8*(l/16)+j], B[8*(l/16)+j][l%16]
 // (j = 0..7) and D[4*(l/16)+j][l%16] (j = 0..3).
@@ -28,10 +26,6 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
-// Streaming 16-byte load: the data is read once, keep it out of the caches.
-__device__ __forceinline__ bf16x8 load_bf16x8_stream(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
 }
 // Direct global -> LDS copy of 16 bytes per lane (gfx950
 // global_load_lds_dwordx4): lane l's bytes land at lds_base + 16*l; the LDS
@@ -51,9 +45,6 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
   return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-}
-__device__ __forceinline__ bf16x8 join_bf16x4(u32x2 lo, u32x2 hi) {
-  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
 // Round-to-nearest-even float -> bfloat16 bits (inputs are finite).
@@ -111,9 +102,5 @@ __device__ __forceinline__ float wave_min(float v) {
 }
 
 __device__ __forceinline__ float max4(f32x4 v) { return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])); }
-
-// Device-scope release/acquire fences around the "last workgroup" hand-off.
-__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 }  // namespace msa
