@@ -6,6 +6,7 @@
 * dense causal GQA attention (torch's scaled_dot_product_attention in
   float64) when k covers every block;
 * the softmax normalisation invariant (constant values);
+* the causal limit: later blocks whose index keys would win are never kept;
 * decode == prefill with a one-token chunk; page-shuffle and in-group head
   permutation invariance;
 * a hand-worked example with the diagram's structure (tests/golden).
@@ -69,6 +70,30 @@ def test_prefill_matches_bruteforce(P, C, seed):
         for g in range(TINY.num_kv_heads):
             np.testing.assert_array_equal(o["pooled"][tau, g, :own], r["pooled"][tau][g])
     np.testing.assert_allclose(o["out"], r["out"], rtol=1e-12, atol=1e-12)
+
+
+def test_selection_never_beyond_the_causal_limit():
+    """Index keys of the chunk's later blocks are set to the tile queries'
+    direction, so they would outrank every earlier block if a tile could see
+    them: each tile still keeps only blocks up to its own diagonal block, and
+    its pooled scores past that block stay unscored."""
+    P, C = 24, 40
+    case = make_prefill_case(TINY, P, C, 44, shuffle_pages=True)
+    B = TINY.block_size
+    c = case.cache
+    direction = case.idx_q.float().sum(dim=(0, 1, 2))  # [d_i]
+    direction = (8.0 * direction / direction.norm()).to(torch.bfloat16)
+    for b in range(P // B + 1, (P + C - 1) // B + 1):
+        page = int(c.block_table[0, b])
+        c.idx_k[page] = direction
+    o = oracle.prefill(case)
+    r = bruteforce.prefill(case)
+    np.testing.assert_array_equal(o["sel"], r["sel"])
+    for tau in range(case.num_tiles):
+        own = P // B + tau
+        kept = o["sel"][tau]
+        assert kept.max() == own and (kept[kept >= 0] <= own).all()
+        assert np.isneginf(o["pooled"][tau, :, own:]).all()
 
 
 def test_prefill_tile_subset_equals_full():
