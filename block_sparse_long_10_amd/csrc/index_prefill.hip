@@ -97,6 +97,9 @@ __global__ __launch_bounds__(256) void index_score_prefill_kernel(
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
+        // M tiles holding only padding rows (partial tiles of unaligned
+        // chunks) are skipped: their rows would only repeat row 0
+        if (wave * 128 + mt * 32 >= nrows) continue;  // uniform
         f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
