@@ -745,6 +745,29 @@ def summarize_kernel_trace(trace_csv, out_txt, command):
     print("\n".join(lines))
 
 
+def summarize_kernel_stats(stats_csv, out_txt, command):
+    """Write the MSA kernels' rows of a rocprofv3 --stats run (its own
+    per-kernel call counts and durations, over every launch grid)."""
+    import csv
+    rows = []
+    for r in csv.DictReader(open(stats_csv)):
+        if "msa::" not in r["Name"]:
+            continue
+        name = r["Name"].split("(")[0].replace("void ", "")
+        rows.append((float(r["TotalDurationNs"]), name, int(r["Calls"]),
+                     float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                     float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    lines = ["rocprofv3 --stats (MSA kernels; all launch grids of a kernel together)", "",
+             "command:", "  " + command, "",
+             "%-60s %6s %12s %12s %12s %8s" % ("kernel", "calls", "avg us", "min us", "max us",
+                                              "% time")]
+    for _, name, calls, avg, mn, mx, pct in sorted(rows, reverse=True):
+        lines.append("%-60s %6d %12.3f %12.3f %12.3f %8.2f" % (name, calls, avg, mn, mx, pct))
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_traffic(fetch_csv, write_csv, out_json, command):
     """HBM bytes per launch of the decode index kernel from FETCH_SIZE and
     WRITE_SIZE runs of --traffic-probe, each scaled by what the counter reads
@@ -809,6 +832,8 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=4,
                     metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON", "CMD"),
                     help="write the profiles/ traffic summary of two counter runs")
+    ap.add_argument("--summarize-kernel-stats", nargs=3, metavar=("STATS_CSV", "OUT_TXT", "CMD"),
+                    help="write the profiles/ summary of a rocprofv3 --stats run")
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("COUNTER_CSV", "OUT_TXT", "CMD"),
                     help="write the profiles/ summary of an MFMA counter run")
     ap.add_argument("--mfma-probe", action="store_true",
@@ -826,6 +851,9 @@ def main():
         return
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma)
+        return
+    if args.summarize_kernel_stats:
+        summarize_kernel_stats(*args.summarize_kernel_stats)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
