@@ -13,17 +13,20 @@
 namespace msa {
 
 // --------------------------------------------------------------- prefill
+// Longest key-block range of one workgroup.
+constexpr int kPrefillMaxBlocksPerSplit = 256;
+
 // Workgroup: 4 waves x 128 row slots (4 M tiles of 32) = 512 rows of one
 // (tile, group); rows are (query, index head) pairs, padding rows repeat row 0.
 // Keys: blocks [b_lo, b_hi) of the tile's eligible range, one block per step,
-// double-buffered in LDS.  Each wave streams a quarter of the next block with
+// double-buffered in LDS (two buffers, alternated by unrolling the loop by two).  Each wave streams a quarter of the next block with
 // 1 KB direct-to-LDS loads (lane l of a load fills token 8q + l/8, chunk slot
 // l%8 with source chunk (l%8) ^ (l/8): the XOR-swizzled image the MFMA B
 // operand reads without bank conflicts).  Per block, each wave folds its
 // 32x32 score tiles with v_max3 into one value per lane, reduces within DPP
 // rows, and one thread combines the 16 row maxima of the workgroup.
 template <int B>
-__global__ __launch_bounds__(256) void index_score_prefill_kernel(
+__global__ __launch_bounds__(256, 3) void index_score_prefill_kernel(
     const uint16_t* __restrict__ idx_k, const int32_t* __restrict__ block_table,
     const uint16_t* __restrict__ idx_q, ChunkMap map, int32_t num_kv_heads,
     int32_t num_idx_heads, int32_t idx_k_heads, int32_t max_blocks, int32_t blocks_per_split,
@@ -31,8 +34,15 @@ __global__ __launch_bounds__(256) void index_score_prefill_kernel(
   constexpr int NT = B / 32;                       // 32-token N tiles per block
   constexpr int BLOCK_BYTES = B * 128;             // B tokens x 64 bf16
   constexpr int WLOADS = BLOCK_BYTES / 1024 / 4;   // 1 KB loads per wave per block
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][BLOCK_BYTES];
-  __shared__ float wmax[2][16];
+  // the two key buffers are separate objects, each addressed at compile time:
+  // reads of one then provably miss the direct loads into the other, and need
+  // not wait for them
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[BLOCK_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[BLOCK_BYTES];
+  __shared__ float wmax0[16], wmax1[16];
+  // physical pages of the workgroup's key blocks, read once up front so that
+  // no block-table load sits in front of each block's key loads
+  __shared__ int32_t pages[kPrefillMaxBlocksPerSplit];
 
   const int tile = blockIdx.x, g = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -60,25 +70,27 @@ __global__ __launch_bounds__(256) void index_score_prefill_kernel(
   }
 
   const int32_t* bt = block_table + (size_t)loc.seq * map.max_blocks;
-  const int src_off = (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) << 4);
-  auto issue = [&](int b, int buf) {
+  for (int i = tid; i < b_hi - b_lo; i += 256) pages[i] = bt[b_lo + i];
+  __syncthreads();
+  const uint32_t src_off = (uint32_t)((lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) << 4));
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto issue = [&](int b, uint8_t* dst) {
     // the block's index keys: the shared head, or group g's own head
+    const int page = __builtin_amdgcn_readfirstlane(pages[b - b_lo]);
     const uint8_t* src = reinterpret_cast<const uint8_t*>(idx_k) +
-                         ((size_t)bt[b] * idx_k_heads + (idx_k_heads > 1 ? g : 0)) * BLOCK_BYTES;
+                         ((size_t)page * idx_k_heads + (idx_k_heads > 1 ? g : 0)) * BLOCK_BYTES;
 #pragma unroll
     for (int i = 0; i < WLOADS; ++i) {
-      const int q = wave * WLOADS + i;
-      load_lds16(src + q * 1024 + src_off, &kbuf[buf][q * 1024]);
+      const int q = wave_u * WLOADS + i;
+      load_lds16(src + (size_t)q * 1024 + src_off, dst + q * 1024);
     }
   };
 
-  issue(b_lo, 0);
-  wait_vmem();
-  __syncthreads();
-  for (int b = b_lo; b < b_hi; ++b) {
-    const int buf = (b - b_lo) & 1;
-    // buf ^ 1 was last read in the previous step, which ended with a barrier
-    if (b + 1 < b_hi) issue(b + 1, buf ^ 1);
+  // Scores of block b (staged in cur) folded into its pooled maximum, with
+  // block b + 1 streaming into nxt meanwhile.
+  auto step = [&](int b, const uint8_t* cur, uint8_t* nxt, float* wm) {
+    // nxt was last read in the previous step, which ended with a barrier
+    if (b + 1 < b_hi) issue(b + 1, nxt);
     f32x16 run;
 #pragma unroll
     for (int v = 0; v < 16; ++v) run[v] = -INFINITY;
@@ -92,7 +104,7 @@ __global__ __launch_bounds__(256) void index_score_prefill_kernel(
         for (int ks = 0; ks < 4; ++ks) {
           const int c = ks * 2 + half;
           bf[u][ks] = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(&kbuf[buf][t * 128 + ((c ^ (t & 7)) << 4)]));
+              bf16x8, *reinterpret_cast<const u32x4*>(cur + t * 128 + ((c ^ (t & 7)) << 4)));
         }
       }
 #pragma unroll
@@ -114,19 +126,25 @@ __global__ __launch_bounds__(256) void index_score_prefill_kernel(
 #pragma unroll
     for (int v = 1; v < 16; ++v) m = fmaxf(m, run[v]);
     m = row16_max(m);
-    if ((lane & 15) == 0) wmax[buf][wave * 4 + (lane >> 4)] = m;
+    if ((lane & 15) == 0) wm[wave * 4 + (lane >> 4)] = m;
     wait_vmem();  // this wave's quarter of block b + 1 has landed
     __syncthreads();
     if (tid == 0) {
-      float r = wmax[buf][0];
+      float r = wm[0];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) r = fmaxf(r, wmax[buf][i]);
+      for (int i = 1; i < 16; ++i) r = fmaxf(r, wm[i]);
       pooled[((size_t)tile * num_kv_heads + g) * max_blocks + b] = r;
     }
-  }
-}
+  };
 
-constexpr int kPrefillMaxBlocksPerSplit = 256;
+  issue(b_lo, kbuf0);
+  wait_vmem();
+  __syncthreads();
+  for (int b = b_lo; b < b_hi; b += 2) {
+    step(b, kbuf0, kbuf1, wmax0);
+    if (b + 1 >= b_hi) break;
+    step(b + 1, kbuf1, kbuf0, wmax1);
+  }}
 
 hipError_t launch_index_score_prefill(const Dims& d, const Cache& c, const uint16_t* idx_q,
                                       const ChunkMap& map, int32_t num_tiles, int32_t max_own,

@@ -206,6 +206,11 @@ __device__ __forceinline__ float truncated_rest(float a) {
   return a - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) & 0xFFFF0000u);
 }
 
+// A wave-uniform float moved to a scalar register.
+__device__ __forceinline__ float uniform_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
 template <int B>
 __global__ __launch_bounds__(512) void prefill_attn_kernel(
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
@@ -216,11 +221,16 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   constexpr int VROW = 2 * B;              // V^T row: B keys
   constexpr int VCH = B / 8;               // 16-byte chunks per V^T row
   constexpr int VBYTES = 128 * VROW;
-  constexpr int SLOT = KBYTES + VBYTES;
   constexpr int KI = KBYTES / 1024 / kPrefillWaves;  // 1 KB wave loads per block, K
   constexpr int VI = VBYTES / 1024 / kPrefillWaves;  // and V^T
   constexpr int VRPI = 1024 / VROW;                  // V^T rows per wave load
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[2][SLOT];
+  // the two ring slots are separate objects, each addressed at compile time:
+  // reads of one slot then provably miss the direct loads into the other,
+  // and need not wait for them
+  __shared__ __attribute__((aligned(1024))) uint8_t kslot0[KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kslot1[KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vslot0[VBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vslot1[VBYTES];
   __shared__ int32_t pages[64], blocks[64];
 
   // workgroup -> (unit, row group); unit = tile * Hkv + g
@@ -264,29 +274,35 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = load_bf16x8(qp + ks * 16);
   }
-  // the wave's query positions, for the causal diagonal block
-  const float pos_min = wave_min((float)pos), pos_max = wave_max((float)pos);
+  // the wave's query positions, for the causal diagonal block (wave-uniform:
+  // held in scalar registers)
+  const float pos_min = uniform_f32(wave_min((float)pos));
+  const float pos_max = uniform_f32(wave_max((float)pos));
 
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(kc);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vc);
-  auto issue = [&](int j) {
-    const size_t ph = (size_t)pages[j] * num_kv_heads + g;
+  // Block j's K and V^T into a ring slot: a wave-uniform page base plus
+  // 32-bit lane offsets, recomputed per block from an opaque copy of the lane
+  // index so that no per-lane address stays live across the block loop.
+  auto issue = [&](int j, uint8_t* kdst, uint8_t* vdst) {
+    const size_t ph = (size_t)__builtin_amdgcn_readfirstlane(pages[j]) * num_kv_heads + g;
     const uint8_t* kg = kbase + ph * KBYTES;
     const uint8_t* vg = vbase + ph * VBYTES;
-    uint8_t* dst = ring[j & 1];
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
       const int ins = wave * KI + i;
-      const int key = ins * 4 + (lane >> 4);
-      const int c = (lane & 15) ^ kswz(key);
-      load_lds16(kg + key * 256 + c * 16, dst + ins * 1024);
+      const int key = ins * 4 + (ln >> 4);
+      const int c = (ln & 15) ^ kswz(key);
+      load_lds16(kg + (uint32_t)(key * 256 + c * 16), kdst + ins * 1024);
     }
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
       const int ins = wave * VI + i;
-      const int dd = ins * VRPI + lane / VCH;
-      const int c = (lane % VCH) ^ (dd & (VCH - 1));
-      load_lds16(vg + dd * VROW + c * 16, dst + KBYTES + ins * 1024);
+      const int dd = ins * VRPI + ln / VCH;
+      const int c = (ln % VCH) ^ (dd & (VCH - 1));
+      load_lds16(vg + (uint32_t)(dd * VROW + c * 16), vdst + ins * 1024);
     }
   };
 
@@ -294,45 +310,116 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) o[mt] = f32x16{};
   float m_run = -1e30f, l_run = 0.f;  // m_run: row max in log2 units (lagging)
+  constexpr int NS = B / 32;           // 32-key steps per block
+  const int m = lane & 31;
 
-  if (nsel > 0) issue(0);
-  for (int j = 0; j < nsel; ++j) {
-    wait_vmem();
-    __syncthreads();
-    if (j + 1 < nsel) issue(j + 1);
-    const uint8_t* ks_ = ring[j & 1];
-    const uint8_t* vs_ = ks_ + KBYTES;
-    const bool diag = blocks[j] == own;
-    const int key0 = own * B;
-    const int m = lane & 31;
-    auto load_k = [&](int s, bf16x8* kf) {
-      const int key = s * 32 + kmap(m);
+  // Row maximum of a score tile in log2 units (both lane halves of a row).
+  auto tile_max = [&](const f32x16& acc) {
+    float mx = acc[0];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const int c = ks * 2 + half;
+    for (int v = 1; v < 16; ++v) mx = __builtin_fmaxf(mx, acc[v]);
+    return half_swap_max(mx) * scale_log2;
+  };
+  // Raise the running max only when a row's max exceeds it by more than the
+  // slack; the output and the sum are rescaled then (exact: both always
+  // refer to the same running max).
+  auto raise_max = [&](float mx) {
+    if (__ballot(mx > m_run + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[mt][v] *= alpha;
+      m_run = m_new;
+    }
+  };
+  // P = exp2(S scale - m) of a score tile, added to the row sum and split into
+  // bfloat16 hi + lo, hi the truncation of P: P - hi - lo < 2^-16 P.
+  auto probabilities = [&](const f32x16& acc, bf16x8* phi, bf16x8* plo) {
+    float p[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      p[v] = __builtin_amdgcn_exp2f(fmaf(acc[v], scale_log2, -m_run));
+      l_run += p[v];
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const float* pp = p + 8 * s2;
+      phi[s2] = __builtin_bit_cast(
+          bf16x8, u32x4{upper_pair(pp[0], pp[1]), upper_pair(pp[2], pp[3]),
+                        upper_pair(pp[4], pp[5]), upper_pair(pp[6], pp[7])});
+      plo[s2] = __builtin_bit_cast(
+          bf16x8, u32x4{upper_pair(truncated_rest(pp[0]), truncated_rest(pp[1])),
+                        upper_pair(truncated_rest(pp[2]), truncated_rest(pp[3])),
+                        upper_pair(truncated_rest(pp[4]), truncated_rest(pp[5])),
+                        upper_pair(truncated_rest(pp[6]), truncated_rest(pp[7]))});
+    }
+  };
+  // O^T += V^T P^T over 32 keys (two K steps of 16), hi and lo parts.
+  auto accumulate_pv = [&](const bf16x8 (&vf)[2][4], const bf16x8* phi, const bf16x8* plo) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        o[mt] = mfma32(vf[s2][mt], phi[s2], o[mt]);
+        o[mt] = mfma32(vf[s2][mt], plo[s2], o[mt]);
+      }
+  };
+
+  // LDS byte addresses of this lane's operand rows.  K: chunk ks of key
+  // 32 s + kmap(m) sits at s*8192 + (k_lane ^ 32 ks); V^T: keys 32 s + 16 s2 +
+  // 8 half.. of dimension 32 mt + m sit at 32 mt VROW + (v_lane ^ 16 (4 s +
+  // 2 s2)).  (The swizzles XOR only address bits 4..7, and rows are 256 or 128
+  // bytes, so the XOR and the row/step/slot offsets commute.)
+  const uint32_t k_lane = (uint32_t)(kmap(m) * 256 + ((half ^ kswz(kmap(m))) << 4));
+  const uint32_t v_lane = (uint32_t)(m * VROW + (((m & (VCH - 1)) ^ half) << 4));
+
+  // attention of the wave's rows over kept block j, staged in ks_ and vs_
+  auto attend = [&](int j, const uint8_t* ks_, const uint8_t* vs_) {
+    // (per-step addresses start from opaque copies of the lane offsets, so
+    // that the compiler does not hold every step's addresses across the loop)
+    auto load_k = [&](int s, bf16x8* kf) {
+      uint32_t a = k_lane;
+      asm volatile("" : "+v"(a));
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
         kf[ks] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(ks_ + key * 256 + ((c ^ kswz(key)) << 4)));
+            bf16x8, *reinterpret_cast<const u32x4*>(ks_ + (a ^ (uint32_t)(ks << 5)) + s * 8192));
+    };
+    auto load_v = [&](int s, bf16x8 (&vf)[2][4]) {
+      uint32_t a = v_lane;
+      asm volatile("" : "+v"(a));
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const uint32_t a2 = a ^ (uint32_t)((s * 4 + 2 * s2) << 4);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          vf[s2][mt] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(vs_ + a2 + mt * 32 * VROW));
       }
     };
-    bf16x8 kf[2][8];
-    load_k(0, kf[0]);
-#pragma unroll
-    for (int s = 0; s < B / 32; ++s) {
-      if (diag && (float)(key0 + 32 * s) > pos_max) break;  // wave sees none of these keys
+    // S^T = K Q^T of 32 keys x the wave's 32 rows
+    auto scores = [&](const bf16x8* kf) {
       f32x16 acc = {};
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) acc = mfma32(kf[s & 1][ks], qf[ks], acc);
-      if (s + 1 < B / 32) load_k(s + 1, kf[(s + 1) & 1]);
+      for (int ks = 0; ks < 8; ++ks) acc = mfma32(kf[ks], qf[ks], acc);
+      return acc;
+    };
+    // on the diagonal block the causal mask applies, and 32-key steps past
+    // the wave's last query are skipped
+    const bool diag = __builtin_amdgcn_readfirstlane(blocks[j]) == own;
+    const int key0 = own * B;
+    bf16x8 kf[8];
+    load_k(0, kf);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (diag && (float)(key0 + 32 * s) > pos_max) break;  // wave sees none of these keys
+      f32x16 acc = scores(kf);
+      if (s + 1 < NS) load_k(s + 1, kf);
       bf16x8 vf[2][4];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const int dd = mt * 32 + m;
-          const int vch = s * 4 + 2 * s2 + half;  // keys 32*s + 16*s2 + 8*half ...
-          vf[s2][mt] = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(vs_ + dd * VROW + ((vch ^ (dd & (VCH - 1))) << 4)));
-        }
+      load_v(s, vf);
       if (diag && (float)(key0 + 32 * s + 31) > pos_min) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -340,45 +427,27 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
           if (key0 + kk > pos) acc[v] = -INFINITY;
         }
       }
-      float mx = acc[0];
-#pragma unroll
-      for (int v = 1; v < 16; ++v) mx = __builtin_fmaxf(mx, acc[v]);
-      mx = half_swap_max(mx) * scale_log2;
-      if (__ballot(mx > m_run + kRescaleSlack) != 0) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) o[mt][v] *= alpha;
-        m_run = m_new;
-      }
-      float p[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        p[v] = __builtin_amdgcn_exp2f(fmaf(acc[v], scale_log2, -m_run));
-        l_run += p[v];
-      }
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        // P = hi + lo in bfloat16, hi the truncation of P: P - hi - lo < 2^-16 P
-        const float* pp = p + 8 * s2;
-        const bf16x8 phi = __builtin_bit_cast(
-            bf16x8, u32x4{upper_pair(pp[0], pp[1]), upper_pair(pp[2], pp[3]),
-                          upper_pair(pp[4], pp[5]), upper_pair(pp[6], pp[7])});
-        const bf16x8 plo = __builtin_bit_cast(
-            bf16x8, u32x4{upper_pair(truncated_rest(pp[0]), truncated_rest(pp[1])),
-                          upper_pair(truncated_rest(pp[2]), truncated_rest(pp[3])),
-                          upper_pair(truncated_rest(pp[4]), truncated_rest(pp[5])),
-                          upper_pair(truncated_rest(pp[6]), truncated_rest(pp[7]))});
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          o[mt] = mfma32(vf[s2][mt], phi, o[mt]);
-          o[mt] = mfma32(vf[s2][mt], plo, o[mt]);
-        }
-      }
+      raise_max(tile_max(acc));
+      bf16x8 phi[2], plo[2];
+      probabilities(acc, phi, plo);
+      accumulate_pv(vf, phi, plo);
     }
+  };
+
+  // Two blocks per trip, one per slot: block j + 1 streams into the other
+  // slot while block j is computed; the barrier before each block also
+  // closes every wave's reads of the slot the next load overwrites.
+  if (nsel > 0) issue(0, kslot0, vslot0);
+  for (int j = 0; j < nsel; j += 2) {
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 < nsel) issue(j + 1, kslot1, vslot1);
+    attend(j, kslot0, vslot0);
+    if (j + 1 >= nsel) break;
+    wait_vmem();
+    __syncthreads();
+    if (j + 2 < nsel) issue(j + 2, kslot0, vslot0);
+    attend(j + 1, kslot1, vslot1);
   }
   const float l_row = half_swap_sum(l_run);
   if (!row_ok) return;
