@@ -48,6 +48,9 @@ __device__ __forceinline__ void index_block_scores(const uint16_t* __restrict__ 
     for (int ks = 0; ks < 2; ++ks) a[mt][ks] = load_bf16x8(p + ks * 32);
   }
   wait_vmem();  // the LDS image and the queries are in place (one wave: no barrier)
+  // nothing that reads the queries may be scheduled above the wait (a select
+  // hoisted between the key loads makes the compiler wait for all of them)
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll

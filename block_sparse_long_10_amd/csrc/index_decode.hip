@@ -8,6 +8,8 @@
 // sequence (32 at 8 groups x 4 heads) are the M side of a
 // v_mfma_f32_16x16x32_bf16 so the 64-term dots run on the matrix cores and
 // the kernel stays bound by HBM.
+#include <algorithm>
+
 #include "index_block.h"
 #include "msa_device.h"
 #include "msa_launch.h"
@@ -87,6 +89,73 @@ __global__ __launch_bounds__(64) void index_score_decode_kernel(
   }
 }
 
+// Batches whose full (block, sequence) grid is mostly empty (lengths far
+// below the longest): a compact grid of resident single-wave workgroups walks
+// the real items only.  Item order: per sequence, its append item (with an
+// append) and then its blocks 0 .. own-1; each workgroup finds the sequence of
+// an item from an in-wave scan of the lengths (batch <= 64) and prefetches the
+// page id of its next item while it scores the current one.
+template <int B, int NI, int MT>
+__global__ __launch_bounds__(64) void index_score_decode_compact_kernel(
+    const uint16_t* __restrict__ idx_k, const int32_t* __restrict__ block_table,
+    int32_t max_blocks, const uint16_t* __restrict__ idx_q, const int32_t* __restrict__ seq_lens,
+    int32_t batch, int32_t num_kv_heads, int32_t idx_k_heads, float* __restrict__ pooled,
+    uint32_t* __restrict__ counters, DecodeAppend ap) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[B * 128];
+  const int lane = threadIdx.x;
+  if (counters != nullptr && blockIdx.x == 0)
+    for (int x = lane; x < batch * num_kv_heads; x += kWave) counters[x] = 0u;
+  const int n_app = ap.k_new != nullptr ? 1 : 0;
+  const int L = lane < batch ? seq_lens[lane] : 1;
+  const int items = lane < batch ? (L - 1) / B + n_app : 0;
+  int incl = items;  // inclusive scan over the sequences
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int t = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += t;
+  }
+  const int excl = incl - items;
+  const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
+  // (sequence, item index within it) of item w: the last sequence whose
+  // first item is at or before w
+  auto locate = [&](int w, int& s, int& i) {
+    const uint64_t m = __ballot(lane < batch && excl <= w);
+    s = 63 - __builtin_clzll(m);
+    i = w - __builtin_amdgcn_readlane(excl, s);
+  };
+  auto page_of = [&](int s, int i) {
+    return i >= n_app ? block_table[(size_t)s * max_blocks + (i - n_app)] : 0;
+  };
+  int w = blockIdx.x;
+  if (w >= total) return;
+  int s, i;
+  locate(w, s, i);
+  int32_t page = page_of(s, i);
+  for (;;) {
+    const int wn = w + (int)gridDim.x;
+    int sn = 0, in = 0;
+    int32_t page_n = 0;
+    if (wn < total) {  // next item's page id, in flight while this item runs
+      locate(wn, sn, in);
+      page_n = page_of(sn, in);
+    }
+    if (i < n_app) {
+      append_current_token<B>(ap, s, __builtin_amdgcn_readlane(L, s), num_kv_heads, idx_k_heads);
+    } else if (page >= 0) {
+      const int b = i - n_app;
+      float* out = pooled + (size_t)s * num_kv_heads * max_blocks + b;
+      index_block_scores<B, NI, MT>(idx_k, __builtin_amdgcn_readfirstlane(page),
+                                    idx_q + (size_t)s * num_kv_heads * NI * 64, num_kv_heads,
+                                    stage, [&](int g, float v) { out[(size_t)g * max_blocks] = v; });
+    }
+    if (wn >= total) break;
+    w = wn;
+    s = sn;
+    i = in;
+    page = page_n;
+  }
+}
+
 template <int B, int NI>
 static hipError_t launch_decode_ni(int mt, bool pg, dim3 grid, hipStream_t st,
                                    const uint16_t* idx_k, const int32_t* bt, int32_t mb,
@@ -108,6 +177,36 @@ static hipError_t launch_decode_ni(int mt, bool pg, dim3 grid, hipStream_t st,
   return hipGetLastError();
 }
 
+template <int B, int NI>
+static hipError_t launch_compact_ni(int mt, int wgs, hipStream_t st, const uint16_t* idx_k,
+                                   const int32_t* bt, int32_t mb, const uint16_t* idx_q,
+                                   const int32_t* sl, int32_t batch, int32_t hkv, int32_t hk,
+                                   float* pooled, uint32_t* ctr, const DecodeAppend& ap) {
+#define MSA_IDX_ARGS idx_k, bt, mb, idx_q, sl, batch, hkv, hk, pooled, ctr, ap
+  switch (mt) {
+    case 1: hipLaunchKernelGGL((index_score_decode_compact_kernel<B, NI, 1>), dim3(wgs), dim3(64), 0, st, MSA_IDX_ARGS); break;
+    case 2: hipLaunchKernelGGL((index_score_decode_compact_kernel<B, NI, 2>), dim3(wgs), dim3(64), 0, st, MSA_IDX_ARGS); break;
+    case 3: hipLaunchKernelGGL((index_score_decode_compact_kernel<B, NI, 3>), dim3(wgs), dim3(64), 0, st, MSA_IDX_ARGS); break;
+    default: hipLaunchKernelGGL((index_score_decode_compact_kernel<B, NI, 4>), dim3(wgs), dim3(64), 0, st, MSA_IDX_ARGS); break;
+  }
+#undef MSA_IDX_ARGS
+  return hipGetLastError();
+}
+
+template <int B>
+static hipError_t launch_compact_b(int ni, int mt, int wgs, hipStream_t st, const uint16_t* idx_k,
+                                   const int32_t* bt, int32_t mb, const uint16_t* idx_q,
+                                   const int32_t* sl, int32_t batch, int32_t hkv, int32_t hk,
+                                   float* pooled, uint32_t* ctr, const DecodeAppend& ap) {
+  switch (ni) {
+    case 1: return launch_compact_ni<B, 1>(mt, wgs, st, idx_k, bt, mb, idx_q, sl, batch, hkv, hk, pooled, ctr, ap);
+    case 2: return launch_compact_ni<B, 2>(mt, wgs, st, idx_k, bt, mb, idx_q, sl, batch, hkv, hk, pooled, ctr, ap);
+    case 4: return launch_compact_ni<B, 4>(mt, wgs, st, idx_k, bt, mb, idx_q, sl, batch, hkv, hk, pooled, ctr, ap);
+    case 8: return launch_compact_ni<B, 8>(mt, wgs, st, idx_k, bt, mb, idx_q, sl, batch, hkv, hk, pooled, ctr, ap);
+    default: return launch_compact_ni<B, 16>(mt, wgs, st, idx_k, bt, mb, idx_q, sl, batch, hkv, hk, pooled, ctr, ap);
+  }
+}
+
 template <int B>
 static hipError_t launch_decode_b(int ni, int mt, bool pg, dim3 grid, hipStream_t st,
                                   const uint16_t* idx_k, const int32_t* bt, int32_t mb,
@@ -122,6 +221,15 @@ static hipError_t launch_decode_b(int ni, int mt, bool pg, dim3 grid, hipStream_
   }
 }
 
+// Full grids above this many workgroups take the compact kernel (batches of
+// 2..64 sequences); 160 KiB of LDS per CU bounds the resident workgroups.
+constexpr size_t kCompactMinGrid = 10240;
+constexpr int kLdsPerCu = 160 * 1024;
+// Workgroups per resident slot: the dispatcher refills slots as workgroups
+// finish, so a few per slot even out the per-item latency (1, 2, 4, 8 per
+// slot on the 32-sequence paged batch: 133, 124.5, 123, 125.5 us per step).
+constexpr int kCompactPerSlot = 4;
+
 hipError_t launch_index_score_decode(const Dims& d, const Cache& c, const uint16_t* idx_q,
                                      const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
                                      float* pooled, uint32_t* counters, hipStream_t stream,
@@ -135,6 +243,20 @@ hipError_t launch_index_score_decode(const Dims& d, const Cache& c, const uint16
   if (append != nullptr) ap = *append;
   const int mt = (d.num_kv_heads * d.num_idx_heads + 15) / 16;
   const bool pg = d.idx_k_heads > 1;
+  // Large batches of up to 64 sequences (where lengths can differ widely):
+  // the compact grid, kCompactPerSlot workgroups per slot the LDS keeps
+  // resident.
+  const size_t full = (size_t)gx * batch;
+  if (!pg && batch > 1 && batch <= 64 && full > kCompactMinGrid) {
+    const int wgs = (int)std::min<size_t>(full, (size_t)kCompactPerSlot * 256 * (kLdsPerCu / (B * 128)));
+    if (B == 64)
+      return launch_compact_b<64>(d.num_idx_heads, mt, wgs, stream, c.idx_k, c.block_table,
+                                  c.max_blocks, idx_q, seq_lens, batch, d.num_kv_heads,
+                                  d.idx_k_heads, pooled, counters, ap);
+    return launch_compact_b<128>(d.num_idx_heads, mt, wgs, stream, c.idx_k, c.block_table,
+                                 c.max_blocks, idx_q, seq_lens, batch, d.num_kv_heads,
+                                 d.idx_k_heads, pooled, counters, ap);
+  }
   dim3 grid(gx, batch, pg ? d.num_kv_heads : 1);
   if (B == 64)
     return launch_decode_b<64>(d.num_idx_heads, mt, pg, grid, stream, c.idx_k, c.block_table,

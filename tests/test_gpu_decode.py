@@ -72,6 +72,29 @@ def test_decode_small_ragged(lengths, seed):
     print("worst row err %.3g, selections %s" % (worst, {k: kinds.count(k) for k in set(kinds)}))
 
 
+def _log_uniform_lengths(n, lo, hi, seed, fixed):
+    rng = np.random.default_rng(seed)
+    drawn = np.exp(rng.uniform(np.log(lo), np.log(hi), n - len(fixed))).astype(int)
+    return list(fixed) + [int(x) for x in drawn]
+
+
+# Batches of 2..64 sequences whose full (block, sequence) grid exceeds 10240
+# workgroups take the compact index kernel (a walk over the real blocks found
+# from a scan of the lengths): 48 x 255 and 64 x 187 blocks here, with empty
+# and one-block sequences among them.
+@pytest.mark.parametrize("shape,n,hi,fixed,seed", [
+    (SMALL, 48, 16384, [1, 64, 65, 16384, 2], 104),
+    (Shape(num_q_heads=32, num_kv_heads=8, num_idx_heads=4, block_size=64, top_k=8), 64, 12000,
+     [12000, 1, 128, 129], 105),
+])
+def test_decode_compact_grid(shape, n, hi, fixed, seed):
+    lengths = _log_uniform_lengths(n, 1, hi, seed, fixed)
+    _announce("compact grid: %d sequences up to %d tokens" % (n, max(lengths)))
+    case = make_decode_case(shape, lengths, seed, device=DEV, shuffle_pages=True, poison_frac=0.05)
+    _, _, worst, kinds = _full_check(case)
+    print("worst row err %.3g, selections %s" % (worst, {k: kinds.count(k) for k in set(kinds)}))
+
+
 @pytest.mark.parametrize("shape", [
     Shape(num_q_heads=8, num_kv_heads=8, num_idx_heads=1, block_size=128, top_k=16),
     Shape(num_q_heads=12, num_kv_heads=4, num_idx_heads=2, block_size=128, top_k=5),
