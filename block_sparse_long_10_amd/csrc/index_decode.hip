@@ -3,8 +3,9 @@
 // "MiniMax wird dünn", section 1, Schritt 1.
 //
 // One pass over every cached index key of every sequence: the keys are
-// streamed from HBM exactly once, one KV block per single-wave workgroup,
-// through LDS (index_block_scores); all Hkv*n_i index-query rows of a
+// streamed from HBM exactly once, one KV block per single-wave workgroup (or,
+// for batches whose full grid is mostly empty, a compact grid of workgroups
+// walking the real blocks), through LDS (index_block_scores); all Hkv*n_i index-query rows of a
 // sequence (32 at 8 groups x 4 heads) are the M side of a
 // v_mfma_f32_16x16x32_bf16 so the 64-term dots run on the matrix cores and
 // the kernel stays bound by HBM.

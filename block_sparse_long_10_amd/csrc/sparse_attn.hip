@@ -18,7 +18,7 @@
 // workgroup of each (sequence, group) to finish merges the partials by
 // log-sum-exp.  No workgroup ever waits for another.
 //
-// Prefill: one workgroup per (tile, group, 128 query rows); rows are
+// Prefill: one workgroup per (tile, group, 256 query rows); rows are
 // (query, head) pairs of the group.  Kept blocks are staged whole through LDS
 // (K token-major, V^T dimension-major, XOR-swizzled 16-byte chunks) and
 // consumed 32 keys at a time with v_mfma_f32_32x32x16_bf16 and an online
