@@ -1,7 +1,7 @@
 // Index branch of MSA, chunked prefill: per (tile, group) the tile's
 // queries x index heads (up to 512 rows) are held in registers as the A side
-// of v_mfma_f32_32x32x16_bf16 and every eligible key block is staged through
-// LDS (XOR-swizzled 16-byte chunks, double-buffered) as the B side; the 32x32
+// of v_mfma_f32_16x16x32_bf16 and every eligible key block is staged through
+// LDS (XOR-swizzled 16-byte chunks, double-buffered) as the B side; the 16x16
 // score tiles fold with v_max3 into one running max per lane and are reduced
 // across the workgroup once per block ("MiniMax wird dünn", section 1,
 // Schritt 1: Q_idx . K_idx^T, Block Max Pool; the prefill index branch still
@@ -16,17 +16,21 @@ namespace msa {
 // Longest key-block range of one workgroup.
 constexpr int kPrefillMaxBlocksPerSplit = 256;
 
-// Workgroup: 4 waves x 128 row slots (4 M tiles of 32) = 512 rows of one
+// Workgroup: 4 waves x 128 row slots (8 M tiles of 16) = 512 rows of one
 // (tile, group); rows are (query, index head) pairs, padding rows repeat row 0.
 // Keys: blocks [b_lo, b_hi) of the tile's eligible range, one block per step,
-// double-buffered in LDS (two buffers, alternated by unrolling the loop by two).  Each wave streams a quarter of the next block with
-// 1 KB direct-to-LDS loads (lane l of a load fills token 8q + l/8, chunk slot
-// l%8 with source chunk (l%8) ^ (l/8): the XOR-swizzled image the MFMA B
-// operand reads without bank conflicts).  Per block, each wave folds its
-// 32x32 score tiles with v_max3 into one value per lane, reduces within DPP
-// rows, and one thread combines the 16 row maxima of the workgroup.
+// double-buffered in LDS (two buffers, alternated by unrolling the loop by
+// two).  Each wave streams a quarter of the next block with 1 KB
+// direct-to-LDS loads (lane l of a load fills token 8q + l/8, chunk slot l%8
+// with source chunk (l%8) ^ (l/8): the XOR-swizzled image the MFMA B operand
+// reads without bank conflicts).  Per block, each wave folds its 16x16 score
+// tiles with v_max3 into four values per lane and reduces them over the wave;
+// one thread combines the four wave maxima.  (The 16x16x32 shape needs 106
+// VGPRs, against 163 for 32x32x16 tiles, so four workgroups fit a CU instead
+// of three; the kernel is power-bound, and the smaller shape also moves fewer
+// accumulator registers per flop.)
 template <int B>
-__global__ __launch_bounds__(256, 3) void index_score_prefill_kernel(
+__global__ __launch_bounds__(256, 4) void index_score_prefill_kernel(
     const uint16_t* __restrict__ idx_k, const int32_t* __restrict__ block_table,
     const uint16_t* __restrict__ idx_q, ChunkMap map, int32_t num_kv_heads,
     int32_t num_idx_heads, int32_t idx_k_heads, int32_t max_blocks, int32_t blocks_per_split,
@@ -39,7 +43,7 @@ __global__ __launch_bounds__(256, 3) void index_score_prefill_kernel(
   // not wait for them
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[BLOCK_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[BLOCK_BYTES];
-  __shared__ float wmax0[16], wmax1[16];
+  __shared__ float wmax0[4], wmax1[4];
   // physical pages of the workgroup's key blocks, read once up front so that
   // no block-table load sits in front of each block's key loads
   __shared__ int32_t pages[kPrefillMaxBlocksPerSplit];
@@ -55,18 +59,18 @@ __global__ __launch_bounds__(256, 3) void index_score_prefill_kernel(
   const int q1 = loc.q0 + min(loc.chunk, (own + 1) * B - loc.prior);
   const int nrows = (q1 - q0) * num_idx_heads;
 
-  // A operand: row slot = wave*128 + mt*32 + (lane & 31); K = 64 in 4 steps of 16.
-  bf16x8 a[4][4];
-  const int half = lane >> 5;
+  // A operand: row slot = wave*128 + mt*16 + (lane & 15); K = 64 in 2 steps of 32.
+  bf16x8 a[8][2];
+  const int q4 = lane >> 4;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    int r = wave * 128 + mt * 32 + (lane & 31);
+  for (int mt = 0; mt < 8; ++mt) {
+    int r = wave * 128 + mt * 16 + (lane & 15);
     if (r >= nrows) r = 0;
     const int qi = q0 + r / num_idx_heads, h = r % num_idx_heads;
     const uint16_t* p =
-        idx_q + (((size_t)qi * num_kv_heads + g) * num_idx_heads + h) * 64 + half * 8;
+        idx_q + (((size_t)qi * num_kv_heads + g) * num_idx_heads + h) * 64 + q4 * 8;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) a[mt][ks] = load_bf16x8(p + ks * 16);
+    for (int ks = 0; ks < 2; ++ks) a[mt][ks] = load_bf16x8(p + ks * 32);
   }
 
   const int32_t* bt = block_table + (size_t)loc.seq * map.max_blocks;
@@ -91,48 +95,37 @@ __global__ __launch_bounds__(256, 3) void index_score_prefill_kernel(
   auto step = [&](int b, const uint8_t* cur, uint8_t* nxt, float* wm) {
     // nxt was last read in the previous step, which ended with a barrier
     if (b + 1 < b_hi) issue(b + 1, nxt);
-    f32x16 run;
+    f32x4 run = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-    for (int v = 0; v < 16; ++v) run[v] = -INFINITY;
-#pragma unroll
-    for (int np = 0; np < NT / 2; ++np) {
-      bf16x8 bf[2][4];
+    for (int np = 0; np < B / 32; ++np) {
+      bf16x8 bf[2][2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int t = (2 * np + u) * 32 + (lane & 31);
+        const int t = (2 * np + u) * 16 + (lane & 15);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int c = ks * 2 + half;
+        for (int ks = 0; ks < 2; ++ks) {
+          const int c = ks * 4 + q4;
           bf[u][ks] = __builtin_bit_cast(
               bf16x8, *reinterpret_cast<const u32x4*>(cur + t * 128 + ((c ^ (t & 7)) << 4)));
         }
       }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        // M tiles holding only padding rows (partial tiles of unaligned
-        // chunks) are skipped: their rows would only repeat row 0
-        if (wave * 128 + mt * 32 >= nrows) continue;  // uniform
-        f32x16 acc0 = {}, acc1 = {};
+      for (int mt = 0; mt < 8; ++mt) {
+        if (wave * 128 + mt * 16 >= nrows) continue;  // uniform
+        f32x4 acc0 = mfma16(a[mt][0], bf[0][0], f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 acc1 = mfma16(a[mt][0], bf[1][0], f32x4{0.f, 0.f, 0.f, 0.f});
+        acc0 = mfma16(a[mt][1], bf[0][1], acc0);
+        acc1 = mfma16(a[mt][1], bf[1][1], acc1);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          acc0 = mfma32(a[mt][ks], bf[0][ks], acc0);
-          acc1 = mfma32(a[mt][ks], bf[1][ks], acc1);
-        }
-#pragma unroll
-        for (int v = 0; v < 16; ++v) run[v] = fmaxf(fmaxf(run[v], acc0[v]), acc1[v]);
+        for (int v = 0; v < 4; ++v) run[v] = fmaxf(fmaxf(run[v], acc0[v]), acc1[v]);
       }
     }
-    float m = run[0];
-#pragma unroll
-    for (int v = 1; v < 16; ++v) m = fmaxf(m, run[v]);
-    m = row16_max(m);
-    if ((lane & 15) == 0) wm[wave * 4 + (lane >> 4)] = m;
+    const float m = wave_max(max4(run));
+    if (lane == 0) wm[wave] = m;
     wait_vmem();  // this wave's quarter of block b + 1 has landed
     __syncthreads();
     if (tid == 0) {
-      float r = wm[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) r = fmaxf(r, wm[i]);
+      const float r = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
       pooled[((size_t)tile * num_kv_heads + g) * max_blocks + b] = r;
     }
   };
