@@ -237,7 +237,7 @@ def current_token_rows(torch, case):
     rows = torch.arange(case.batch, device=c.k.device)
     pages = c.block_table.long()[rows, pos // B]
     slots = pos % B
-    return (c.k[pages, :, slots, :].contiguous(), c.v[pages, :, :, slots].contiguous(),
+    return (c.k[pages, :, slots, :].contiguous(), c.v[pages, :, slots, :].contiguous(),
             c.idx_k[pages, slots, :].contiguous())
 
 
@@ -362,7 +362,7 @@ def run_prefill_bench(args, torch, msa, mi, gu):
     pages = case.cache.block_table[0].long()[pos // B]
     slots = pos % B
     k_new = case.cache.k[pages, :, slots, :].contiguous().unsqueeze(0)
-    v_new = case.cache.v[pages, :, :, slots].contiguous().unsqueeze(0)
+    v_new = case.cache.v[pages, :, slots, :].contiguous().unsqueeze(0)
     x_new = case.cache.idx_k[pages, slots, :].contiguous().unsqueeze(0)
     start = torch.tensor([P], dtype=torch.int32, device="cuda")
     kvm = msa.make_kv_mut(case.cache.k, case.cache.v, case.cache.idx_k, case.cache.block_table)

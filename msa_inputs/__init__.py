@@ -25,7 +25,7 @@ stream, so page tables and lengths are identical on every device.
 Paged layout (one page = one KV block of ``block_size`` tokens)
 ---------------------------------------------------------------
 * ``k``     bf16 ``[num_pages][Hkv][B][D]``   (token-major keys)
-* ``v``     bf16 ``[num_pages][Hkv][D][B]``   (values transposed within a page)
+* ``v``     bf16 ``[num_pages][Hkv][B][D]``   (token-major values)
 * ``idx_k`` bf16 ``[num_pages][B][d_i]``      (one index-key head shared by all groups;
   ``[num_pages][Hkv][B][d_i]`` when the shape asks for one head per group)
 * ``block_table`` int32 ``[batch][max_blocks]``: logical block -> physical page
@@ -189,7 +189,7 @@ def build_paged_cache(shape: Shape, lengths: Sequence[int], seed: int,
         pos += nb
     Hkv, D, di = shape.num_kv_heads, shape.head_dim, shape.idx_dim
     k = normal_bf16((num_pages, Hkv, B, D), seed, TENSOR_IDS["k"], device)
-    v = normal_bf16((num_pages, Hkv, D, B), seed, TENSOR_IDS["v"], device)
+    v = normal_bf16((num_pages, Hkv, B, D), seed, TENSOR_IDS["v"], device)
     if shape.idx_k_heads > 1:
         idx_k = normal_bf16((num_pages, shape.idx_k_heads, B, di), seed, TENSOR_IDS["idx_k"],
                             device)
@@ -205,7 +205,7 @@ def build_paged_cache(shape: Shape, lengths: Sequence[int], seed: int,
         if tail:
             page = int(table[s, nblocks[s] - 1])
             k[page, :, tail:, :] = POISON
-            v[page, :, :, tail:] = POISON
+            v[page, :, tail:, :] = POISON
             idx_k[page, ..., tail:, :] = POISON
     return PagedCache(k=k, v=v, idx_k=idx_k,
                       block_table=torch.from_numpy(table).to(k.device),

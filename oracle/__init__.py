@@ -271,7 +271,7 @@ def cache_append(shape, k: np.ndarray, v: np.ndarray, idx_k: np.ndarray, block_t
                  k_new, v_new, idx_new, start_pos) -> None:
     """Oracle cache append, in place on host arrays of bfloat16 bits (int16).
 
-    k [P][Hkv][B][D], v [P][Hkv][D][B], idx_k [P][B][d_i] (or [P][Hkv][B][d_i]
+    k [P][Hkv][B][D], v [P][Hkv][B][D], idx_k [P][B][d_i] (or [P][Hkv][B][d_i]
     with per-group index keys); k_new, v_new [batch][n_new][Hkv][D] and
     idx_new [batch][n_new][d_i] (or [batch][n_new][Hkv][d_i]) (tensors or
     arrays); start_pos [batch]: position of each sequence's first new token.

@@ -44,7 +44,7 @@
  *
  * Paged cache layout (page = one block of B tokens):
  *   k      [num_pages][Hkv][B][D]      keys, token-major
- *   v      [num_pages][Hkv][D][B]      values, transposed within the page
+ *   v      [num_pages][Hkv][B][D]      values, token-major
  *   idx_k  [num_pages][Hk][B][d_i]     index keys, Hk = 1 (the single shared
  *                                      head) or Hkv (one head per group)
  *   block_table [batch][max_blocks]    logical block -> physical page
@@ -92,7 +92,7 @@ static double value_at(const oracle_params *p, const oracle_cache *c, int32_t se
                        int32_t g, int64_t t, int32_t d) {
   const int32_t B = p->block_size, D = p->head_dim, H = p->num_kv_heads;
   int64_t pg = page_of(c, seq, t, B);
-  return bf(c->v[((pg * H + g) * D + d) * B + t % B]);
+  return bf(c->v[((pg * H + g) * B + t % B) * D + d]);
 }
 
 static int32_t idx_k_heads(const oracle_params *p) {
@@ -237,6 +237,25 @@ static int check(const oracle_params *p, const oracle_cache *c) {
   return 0;
 }
 
+/*
+ * Step 2 of decode for every query head of every sequence: head j of
+ * sequence s attends to the tokens t <= seq_lens[s]-1 of the blocks listed in
+ * sel[s][j / G] (the selection of its group).
+ */
+static void attend_decode_heads(const oracle_params *p, const oracle_cache *c,
+                                const uint16_t *q, const int32_t *seq_lens, int32_t batch,
+                                const int32_t *sel, double *out) {
+  const int32_t H = p->num_kv_heads, Hq = p->num_q_heads, G = Hq / H;
+  const int32_t D = p->head_dim, k = p->top_k;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int32_t s = 0; s < batch; s++)
+    for (int32_t j = 0; j < Hq; j++) {
+      int32_t g = j / G;
+      attend(p, c, s, g, q + ((int64_t)s * Hq + j) * D, sel + ((int64_t)s * H + g) * k,
+             (int64_t)seq_lens[s] - 1, out + ((int64_t)s * Hq + j) * D);
+    }
+}
+
 int msa_oracle_max_threads(void) { return omp_get_max_threads(); }
 
 /* Exported for the tests: the TopK rule on a given score vector. */
@@ -268,8 +287,8 @@ int msa_oracle_decode(const oracle_params *p, const oracle_cache *c,
                       const int32_t *seq_lens, int32_t batch, double *out,
                       int32_t *sel, double *pooled) {
   if (check(p, c) || !q || !idx_q || !seq_lens || !out || !sel || batch < 1) return -1;
-  const int32_t B = p->block_size, H = p->num_kv_heads, Hq = p->num_q_heads;
-  const int32_t G = Hq / H, D = p->head_dim, k = p->top_k, MB = c->max_blocks;
+  const int32_t B = p->block_size, H = p->num_kv_heads;
+  const int32_t k = p->top_k, MB = c->max_blocks;
   for (int32_t s = 0; s < batch; s++)
     if (seq_lens[s] < 1 || (int64_t)seq_lens[s] > (int64_t)MB * B) return -1;
 
@@ -295,13 +314,7 @@ int msa_oracle_decode(const oracle_params *p, const oracle_cache *c,
                     p->sink_blocks, p->local_blocks, sel + ((int64_t)s * H + g) * k);
 
   /* Step 2 per query head. */
-#pragma omp parallel for collapse(2) schedule(dynamic, 1)
-  for (int32_t s = 0; s < batch; s++)
-    for (int32_t j = 0; j < Hq; j++) {
-      int32_t g = j / G;
-      attend(p, c, s, g, q + ((int64_t)s * Hq + j) * D, sel + ((int64_t)s * H + g) * k,
-             (int64_t)seq_lens[s] - 1, out + ((int64_t)s * Hq + j) * D);
-    }
+  attend_decode_heads(p, c, q, seq_lens, batch, sel, out);
 
   if (pooled) memcpy(pooled, score, sizeof(double) * (size_t)batch * H * MB);
   free(score);
@@ -313,15 +326,7 @@ int msa_oracle_attend_decode(const oracle_params *p, const oracle_cache *c,
                              const uint16_t *q, const int32_t *seq_lens,
                              int32_t batch, const int32_t *sel, double *out) {
   if (check(p, c) || !q || !seq_lens || !sel || !out || batch < 1) return -1;
-  const int32_t H = p->num_kv_heads, Hq = p->num_q_heads, G = Hq / H;
-  const int32_t D = p->head_dim, k = p->top_k;
-#pragma omp parallel for collapse(2) schedule(dynamic, 1)
-  for (int32_t s = 0; s < batch; s++)
-    for (int32_t j = 0; j < Hq; j++) {
-      int32_t g = j / G;
-      attend(p, c, s, g, q + ((int64_t)s * Hq + j) * D, sel + ((int64_t)s * H + g) * k,
-             (int64_t)seq_lens[s] - 1, out + ((int64_t)s * Hq + j) * D);
-    }
+  attend_decode_heads(p, c, q, seq_lens, batch, sel, out);
   return 0;
 }
 
@@ -478,7 +483,7 @@ int msa_oracle_append(const oracle_params *p, uint16_t *k, uint16_t *v, uint16_t
       for (int32_t g = 0; g < H; ++g) {
         for (int32_t d = 0; d < D; ++d) {
           k[((pg * H + g) * B + slot) * D + d] = k_new[(src * H + g) * D + d];
-          v[((pg * H + g) * D + d) * B + slot] = v_new[(src * H + g) * D + d];
+          v[((pg * H + g) * B + slot) * D + d] = v_new[(src * H + g) * D + d];
         }
       }
       for (int32_t h = 0; h < Hk; ++h)

@@ -17,7 +17,7 @@ def token_rows(cache, shape, seq: int, positions):
     pages = cache.block_table[seq].to(pos.device).long()[pos // B]
     slots = pos % B
     k = cache.k[pages, :, slots, :]
-    v = cache.v[pages, :, :, slots]
+    v = cache.v[pages, :, slots, :]
     if cache.idx_k.dim() == 4:  # per-group index keys: [n][Hkv][d_i]
         idx = cache.idx_k[pages, :, slots, :]
     else:
@@ -44,7 +44,7 @@ def holed_copy(cache, shape, starts, n_new):
         pages = cache.block_table[s].to(pos.device).long()[pos // B]
         slots = pos % B
         c.k[pages, :, slots, :] = POISON
-        c.v[pages, :, :, slots] = POISON
+        c.v[pages, :, slots, :] = POISON
         if c.idx_k.dim() == 4:
             c.idx_k[pages, :, slots, :] = POISON
         else:

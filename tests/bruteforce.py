@@ -24,10 +24,10 @@ def logical(case, s: int, length: int):
     nb = (length + B - 1) // B
     pages = cache.block_table[s, :nb].cpu().numpy().astype(np.int64)
     k = f64(cache.k)[pages]                      # [nb][Hkv][B][D]
-    v = f64(cache.v)[pages]                      # [nb][Hkv][D][B]
+    v = f64(cache.v)[pages]                      # [nb][Hkv][B][D]
     ik = f64(cache.idx_k)[pages]                 # [nb][B][d_i] or [nb][Hkv][B][d_i]
     K = k.transpose(1, 0, 2, 3).reshape(sh.num_kv_heads, nb * B, sh.head_dim)[:, :length]
-    V = v.transpose(1, 0, 3, 2).reshape(sh.num_kv_heads, nb * B, sh.head_dim)[:, :length]
+    V = v.transpose(1, 0, 2, 3).reshape(sh.num_kv_heads, nb * B, sh.head_dim)[:, :length]
     if ik.ndim == 4:
         IK = ik.transpose(1, 0, 2, 3).reshape(ik.shape[1], nb * B, sh.idx_dim)[:, :length]
     else:
@@ -116,3 +116,63 @@ def prefill(case):
         sels.append(sel_t)
         pools.append(pool_t)
     return {"out": out, "sel": np.stack(sels), "pooled": pools}
+
+
+def attend_decode(case, sel):
+    """Sparse branch alone for a given selection sel [batch][Hkv][k] (any valid
+    blocks, -1 padded): head j of sequence s over the tokens <= L_s - 1 of
+    sel[s][j // G]."""
+    sh = case.shape
+    B, G = sh.block_size, sh.group_size
+    sel = np.asarray(sel)
+    outs = []
+    for s, L in enumerate(case.lengths):
+        K, V, _ = logical(case, s, L)
+        q = f64(case.q[s])
+        outs.append(np.stack([
+            softmax_attend(q[j], K[j // G][tokens_of(sel[s, j // G], B, L - 1)],
+                           V[j // G][tokens_of(sel[s, j // G], B, L - 1)], sh.softmax_scale)
+            for j in range(sh.num_q_heads)]))
+    return np.stack(outs)
+
+
+def attend_prefill(case, sel, tiles=None):
+    """Prefill sparse branch alone for a given selection sel [num_tiles][Hkv][k]:
+    every query of the listed tiles (all if None) over the tokens of its
+    tile's kept blocks up to its own position.  Rows of other tiles are NaN."""
+    sh = case.shape
+    B, G = sh.block_size, sh.group_size
+    P, C = case.prior_len, case.chunk_len
+    K, V, _ = logical(case, 0, P + C)
+    q = f64(case.q)
+    sel = np.asarray(sel)
+    out = np.full((C, sh.num_q_heads, sh.head_dim), np.nan)
+    for tau in (range(case.num_tiles) if tiles is None else tiles):
+        own = P // B + tau
+        for i in range(max(0, own * B - P), min(C, (own + 1) * B - P)):
+            for j in range(sh.num_q_heads):
+                t = tokens_of(sel[tau, j // G], B, P + i)
+                out[i, j] = softmax_attend(q[i, j], K[j // G][t], V[j // G][t], sh.softmax_scale)
+    return out
+
+
+def block_scores(case, group, blocks, seq=0, tile=None):
+    """Pooled index scores of the listed blocks: decode sequence ``seq``
+    (its index queries), or prefill tile ``tile`` (the queries inside the
+    tile's own block)."""
+    sh = case.shape
+    B = sh.block_size
+    blocks = [int(b) for b in blocks]
+    nb = max(blocks) + 1 if blocks else 0
+    if tile is None:
+        _, _, IK = logical(case, seq, nb * B)
+        rows = f64(case.idx_q[seq])[group]                   # [n_i][d_i]
+    else:
+        P, C = case.prior_len, case.chunk_len
+        _, _, IK = logical(case, 0, nb * B)
+        own = P // B + tile
+        q0, q1 = max(0, own * B - P), min(C, (own + 1) * B - P)
+        rows = f64(case.idx_q)[q0:q1, group].reshape(-1, sh.idx_dim)
+    ikg = IK if IK.ndim == 2 else IK[group]
+    tok = rows @ ikg.T                                      # [rows][nb*B]
+    return np.array([tok[:, b * B:(b + 1) * B].max() for b in blocks])

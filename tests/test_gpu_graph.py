@@ -37,7 +37,7 @@ def test_multi_layer_decode_graph_replays(append):
     pages = c.block_table.long()[rows, pos // 64]
     slots = pos % 64
     kn = c.k[pages, :, slots, :].contiguous()
-    vn = c.v[pages, :, :, slots].contiguous()
+    vn = c.v[pages, :, slots, :].contiguous()
     outs = torch.empty(n_layers, batch, shape.num_q_heads, shape.head_dim, device="cuda")
     sels = torch.empty(n_layers, batch, shape.num_kv_heads, shape.top_k, dtype=torch.int32,
                        device="cuda")

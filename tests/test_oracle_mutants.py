@@ -15,6 +15,7 @@ from tests.append_util import holed_copy, new_token_batch
 from tests.test_oracle_forced import FORCED
 from tests.test_oracle_groupkeys import GK
 from tests import bruteforce
+from tests import test_oracle_given_sel as given_sel
 from tests.test_oracle_pins import TINY, TINY1, _by_sort
 from tests.test_oracle_pins import test_handworked_golden as _golden
 
@@ -27,8 +28,8 @@ MUTANTS = [
      "for (int64_t row = 0; row < nrows; row += ni)", False),
     ("own block scored", "if (b < own)\n", "if (b <= own)\n", False),
     ("ties keep the higher index", "score[b] > score[best]", "score[b] >= score[best]", False),
-    ("values read untransposed", "return bf(c->v[((pg * H + g) * D + d) * B + t % B]);",
-     "return bf(c->v[((pg * H + g) * B + t % B) * D + d]);", False),
+    ("values read dimension-major", "return bf(c->v[((pg * H + g) * B + t % B) * D + d]);",
+     "return bf(c->v[((pg * H + g) * D + d) * B + t % B]);", False),
     ("softmax scale dropped", "z[i] = p->softmax_scale * dot;", "z[i] = dot;", False),
     ("heads mapped to groups round-robin", "int32_t g = j / G;", "int32_t g = j % H;", True),
     ("one block too few", "int32_t kk = k - 1 - n;", "int32_t kk = k - 2 - n;", False),
@@ -42,8 +43,8 @@ MUTANTS = [
     ("softmax not normalised", "out[d] = acc / den;", "out[d] = acc;", False),
     ("index key dims swapped with query", "dot += qry[row * di + d] * key[r * di + d];",
      "dot += qry[row * di + d] * key[d * B + r];", False),
-    ("append writes V untransposed", "v[((pg * H + g) * D + d) * B + slot] = v_new",
-     "v[((pg * H + g) * B + slot) * D + d] = v_new", False),
+    ("append writes V dimension-major", "v[((pg * H + g) * B + slot) * D + d] = v_new",
+     "v[((pg * H + g) * D + d) * B + slot] = v_new", False),
     ("append slot off by one", "const int64_t slot = t % B;", "const int64_t slot = (t + 1) % B;",
      False),
     ("local window one block short", "if (b < n_sink || b >= own - n_local) {",
@@ -55,6 +56,27 @@ MUTANTS = [
     ("append ignores the block table",
      "const int64_t pg = block_table[(int64_t)s * max_blocks + t / B];",
      "const int64_t pg = t / B;", False),
+    # the entry points that take the caller's selection or query range
+    ("given selection read from sequence 0's row",
+     "sel + ((int64_t)s * H + g) * k,\n             (int64_t)seq_lens[s] - 1",
+     "sel + (int64_t)g * k,\n             (int64_t)seq_lens[s] - 1", False),
+    ("prefill query sees one token fewer", "(int64_t)prior_len + qi[r], out",
+     "(int64_t)prior_len + qi[r] - 1, out", False),
+    ("listed tiles take the selection of their list position", "qi[n] = i; qt[n] = list[u];",
+     "qi[n] = i; qt[n] = u;", False),
+    ("block scores of sequence 0's pages",
+     "out[i] = block_score(p, c, seq, idx_q, q0, q1, g, blocks[i]);",
+     "out[i] = block_score(p, c, 0, idx_q, q0, q1, g, blocks[i]);", False),
+]
+
+# Mistakes planted in the Python wrapper's slicing (oracle/__init__.py):
+# (name, text, replacement)
+PY_MUTANTS = [
+    ("tile rows start one query late", "    q0 = max(0, own * B - case.prior_len)\n",
+     "    q0 = max(0, own * B - case.prior_len) + 1\n"),
+    ("decode block scores take sequence 0's index queries",
+     "        iq = P.idx_q.reshape(case.batch, -1)[seq]\n",
+     "        iq = P.idx_q.reshape(case.batch, -1)[0]\n"),
 ]
 
 
@@ -94,6 +116,13 @@ def _pins_pass() -> bool:
             own = (L - 1) // GK.block_size
             for g in range(GK.num_kv_heads):
                 np.testing.assert_array_equal(o["pooled"][s, g, :own], r["pooled"][s][g])
+        for shape, lengths, seed, kw in given_sel.DECODE_CASES[:2]:
+            given_sel.test_attend_decode_given_selection(shape, lengths, seed, kw)
+            given_sel.test_block_scores_decode(shape, lengths, seed, kw)
+        for shape, P, C, seed in given_sel.PREFILL_CASES[:2]:
+            given_sel.test_attend_prefill_given_selection(shape, P, C, seed)
+            given_sel.test_block_scores_prefill(shape, P, C, seed)
+        given_sel.test_tile_rows_partial_tiles()
     except AssertionError:
         return False
     return True
@@ -141,3 +170,20 @@ def test_pins_catch_planted_mistake(tmp_path, name, old, new, every):
         assert not _pins_pass(), "pins did not catch: " + name
     finally:
         oracle.use_library(None)
+
+
+@pytest.mark.parametrize("name,old,new", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_pins_catch_planted_wrapper_mistake(monkeypatch, name, old, new):
+    """The same for the wrapper's own slicing: a mutated copy of
+    oracle/__init__.py is loaded as a separate module and its functions are
+    swapped into the oracle module for the duration of the test."""
+    import types
+    path = oracle.__file__
+    text = open(path).read()
+    assert text.count(old) == 1, name
+    mod = types.ModuleType("oracle_mutant")
+    mod.__file__ = path
+    exec(compile(text.replace(old, new), path, "exec"), mod.__dict__)
+    for fn in ("tile_rows", "block_scores", "prefill", "attend_prefill", "attend_decode", "decode"):
+        monkeypatch.setattr(oracle, fn, getattr(mod, fn))
+    assert not _pins_pass(), "pins did not catch: " + name

@@ -214,7 +214,7 @@ def test_constant_values_give_that_value():
     case = make_decode_case(TINY, [50, 23], 71, shuffle_pages=True)
     u = torch.randn(TINY.num_kv_heads, TINY.head_dim, dtype=torch.float64)
     u_bf = u.to(torch.bfloat16)
-    case.cache.v[:] = u_bf[None, :, :, None]
+    case.cache.v[:] = u_bf[None, :, None, :]
     o = oracle.decode(case)
     G = TINY.group_size
     for j in range(TINY.num_q_heads):
@@ -275,7 +275,7 @@ def test_handworked_golden():
     ik[:L] = torch.tensor(g["idx_k"]).float()
     cache = PagedCache(
         k=k.view(nb, B, sh.num_kv_heads, sh.head_dim).permute(0, 2, 1, 3).contiguous().to(torch.bfloat16),
-        v=v.view(nb, B, sh.num_kv_heads, sh.head_dim).permute(0, 2, 3, 1).contiguous().to(torch.bfloat16),
+        v=v.view(nb, B, sh.num_kv_heads, sh.head_dim).permute(0, 2, 1, 3).contiguous().to(torch.bfloat16),
         idx_k=ik.view(nb, B, sh.idx_dim).contiguous().to(torch.bfloat16),
         block_table=torch.arange(nb, dtype=torch.int32)[None], num_pages=nb, max_blocks=nb,
         lengths=[L])
