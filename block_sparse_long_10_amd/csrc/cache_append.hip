@@ -4,19 +4,16 @@
 // head) and section 2 keeps the real, uncompressed K/V; the page layout is
 // the one the other kernels read:
 //   k     [page][Hkv][B][D]   token-major
-//   v     [page][Hkv][D][B]   transposed within the page
+//   v     [page][Hkv][B][D]   token-major
 //   idx_k [page][Hk][B][d_i]  (Hk = 1, the shared head, or Hkv per group)
 //
 // One 256-thread workgroup per (sequence, touched block, group) writes the
-// new tokens that fall into one page: K rows and index-key rows are 16-byte
-// copies; V is staged token-major in LDS and written out along the page's
-// token axis, so consecutive lanes store consecutive tokens of one dimension.
+// new tokens that fall into one page: K, V and index-key rows are 16-byte
+// copies, consecutive lanes on consecutive chunks of a row.
 #include "msa_device.h"
 #include "msa_launch.h"
 
 namespace msa {
-
-constexpr int kVStride = 130;  // bf16 per LDS row (128 dims + 2: conflict-free column reads)
 
 template <int B>
 __global__ __launch_bounds__(256) void cache_append_kernel(
@@ -25,7 +22,6 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
     int32_t idx_k_heads,
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const uint16_t* __restrict__ idx_new, const int32_t* __restrict__ start_pos, int32_t n_new) {
-  __shared__ uint32_t vt[B * kVStride / 2];
   const int j = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x;
   const int start = start_pos[s];
@@ -36,12 +32,15 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
   const size_t page = (size_t)block_table[(size_t)s * max_blocks + b];
   const size_t tok0 = (size_t)s * n_new + i0;  // first new token of this workgroup
 
-  // K rows of group g: 16 chunks of 16 bytes per token
+  // K and V rows of group g: 16 chunks of 16 bytes per token each
   for (int x = tid; x < n * 16; x += 256) {
     const int i = x >> 4, c = x & 15;
-    const u32x4 val =
-        *reinterpret_cast<const u32x4*>(k_new + ((tok0 + i) * num_kv_heads + g) * 128 + c * 8);
-    *reinterpret_cast<u32x4*>(kc + ((page * num_kv_heads + g) * B + slot0 + i) * 128 + c * 8) = val;
+    const size_t src = ((tok0 + i) * num_kv_heads + g) * 128 + c * 8;
+    const size_t dst = ((page * num_kv_heads + g) * B + slot0 + i) * 128 + c * 8;
+    const u32x4 kval = *reinterpret_cast<const u32x4*>(k_new + src);
+    const u32x4 vval = *reinterpret_cast<const u32x4*>(v_new + src);
+    *reinterpret_cast<u32x4*>(kc + dst) = kval;
+    *reinterpret_cast<u32x4*>(vc + dst) = vval;
   }
   // index-key rows: the shared head is written once, by group 0; per-group
   // heads by their group
@@ -53,18 +52,6 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
           *reinterpret_cast<const u32x4*>(idx_new + ((tok0 + i) * idx_k_heads + h) * 64 + c * 8);
       *reinterpret_cast<u32x4*>(ic + ((page * idx_k_heads + h) * B + slot0 + i) * 64 + c * 8) = val;
     }
-  }
-  // V of group g: token-major rows into LDS, then dimension-major out
-  for (int x = tid; x < n * 64; x += 256) {
-    const int i = x >> 6, w = x & 63;  // dims 2w, 2w+1
-    vt[i * (kVStride / 2) + w] =
-        *reinterpret_cast<const uint32_t*>(v_new + ((tok0 + i) * num_kv_heads + g) * 128 + 2 * w);
-  }
-  __syncthreads();
-  const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(vt);
-  for (int x = tid; x < n * 128; x += 256) {
-    const int d = x / n, i = x - d * n;
-    vc[((page * num_kv_heads + g) * 128 + d) * B + slot0 + i] = vt16[i * kVStride + d];
   }
 }
 

@@ -50,13 +50,26 @@ __host__ __device__ constexpr size_t attend_wo_bytes(int group) {
   return (size_t)4 * group * kWoStride * sizeof(float);
 }
 
+// LDS bytes for staging V: 32 token rows of 256 bytes per wave.
+constexpr size_t kAttendVStageBytes = 4 * 32 * 256;
+
+// Swizzle of the staged V rows: 16-byte chunk c of row r is stored at chunk
+// c ^ 2*vswz(r), so that the transpose reads of one instruction (rows
+// r0 .. r0+3 and r0+8 .. r0+11, 32 bytes each) fall on distinct banks.
+__device__ __forceinline__ int vswz(int r) { return (r & 3) | ((r >> 1) & 4); }
+
 // Attention of the G heads of group g of sequence s over kept block blk
 // (blk < 0: an empty slot) by a 256-thread workgroup: 4 waves x 32 tokens,
 // S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 (heads padded to
-// 16), the per-wave partials combined in LDS.  The result is stored as the
-// partial of `slot`: o at ro[(slot*G + h)*128 ..] and (max, sum) at
-// rml[(slot*G + h)*16] (16-byte records), both with agent-scope stores.
-// Probabilities enter the PV contraction as hi + lo bf16 parts
+// 16), the per-wave partials combined in LDS.  K rows come straight from the
+// token-major page as the A operand; the wave's 32 V rows are staged in LDS
+// (vstage, kAttendVStageBytes) by direct loads, and V^T, the A operand of the
+// PV product, is read from them with LDS transpose reads.  vstage may alias
+// w_o.  V rows past the sequence's last token are zeroed in LDS: their
+// probability is zero, and unwritten cache slots may hold any bits.  The
+// result is stored as the partial of `slot`: o at ro[(slot*G + h)*128 ..] and
+// (max, sum) at rml[(slot*G + h)*16] (16-byte records), both with agent-scope
+// stores.  Probabilities enter the PV contraction as hi + lo bf16 parts
 // (P - hi - lo < 2^-16 P).
 template <int B>
 __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ kc,
@@ -65,7 +78,7 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ kc,
                                              int num_kv_heads, int g, int group, float scale_log2,
                                              int slot, __amdgpu_buffer_rsrc_t ro,
                                              __amdgpu_buffer_rsrc_t rml, AttendShared& sh,
-                                             float* __restrict__ w_o) {
+                                             float* __restrict__ w_o, uint8_t* __restrict__ vstage) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   if (blk < 0) {  // empty slot: weight zero in the merge, output zeros
     for (int h = tid; h < group; h += 256)
@@ -99,9 +112,38 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ kc,
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) kf[mt][ks] = load_bf16x8(kp + (size_t)tok * 128 + q4 * 8 + ks * 32);
     }
-    const uint16_t* vp = vc + ((size_t)page * num_kv_heads + g) * (size_t)(128 * B) + t0 + 8 * q4;
+    // V rows t0 .. t0+31 into the wave's 8 KiB of LDS: load i fills rows
+    // 4i .. 4i+3, lane l row 4i + l/16 at chunk position l%16
+    uint8_t* vs = vstage + wave * 8192;
+    {
+      const uint8_t* vsrc = reinterpret_cast<const uint8_t*>(vc) +
+                            (((size_t)page * num_kv_heads + g) * B + t0) * 256;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) vf[mt] = load_bf16x8(vp + (size_t)(16 * mt + r16) * B);
+      for (int i = 0; i < 8; ++i) {
+        const int row = 4 * i + (lane >> 4);
+        const int c = (lane & 15) ^ (2 * vswz(row));
+        load_lds16(vsrc + row * 256 + c * 16, vs + i * 1024);
+      }
+    }
+    wait_vmem();  // K, Q and the staged V rows are in place (one wave: no barrier)
+    if (t0 + 32 > n_valid) {  // rows past the last token: zero (uniform)
+      for (int x = lane + 16 * (n_valid - t0); x < 32 * 16; x += kWave)
+        *reinterpret_cast<u32x4*>(vs + x * 16) = u32x4{0u, 0u, 0u, 0u};
+    }
+    // (no LDS read may move above the stores)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // V^T operand of dims 16 mt .. 16 mt + 15, tokens 8 q4 .. 8 q4 + 7: lane
+    // u = r16 of its 16-lane group addresses row 8 q4 + u/4 (+4), dims
+    // 16 mt + 4 (u%4) .. +3, at swizzled chunk positions
+    {
+      const int row = 8 * q4 + (r16 >> 2);
+      const uint32_t a0 = (uint32_t)(row * 256 + 32 * vswz(row) + 8 * (r16 & 3));
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const uint32_t a = a0 ^ (uint32_t)(32 * mt);
+        vf[mt] = join_tr(lds_read_tr16(vs + a), lds_read_tr16(vs + a + 4 * 256));
+      }
+    }
 
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[ks] = r16 < group ? qf[ks] : zero_bf16x8();
@@ -151,6 +193,7 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ kc,
     sh.w_m[wave][lane] = m_w;
     sh.w_l[wave][lane] = l_w;
   }
+  __syncthreads();  // every wave's V reads are done before w_o (aliasing vstage) is written
   if (r16 < group) {
     float* row = w_o + (wave * group + r16) * kWoStride;
 #pragma unroll

@@ -30,14 +30,13 @@ __device__ __forceinline__ void append_current_token(const DecodeAppend& ap, int
   const int own = (L - 1) / B, slot = (L - 1) % B;
   const size_t page = (size_t)ap.cache.block_table[(size_t)s * ap.cache.max_blocks + own];
   const size_t kv0 = (size_t)s * num_kv_heads * 128;
-  for (int x = lane; x < num_kv_heads * 16; x += kWave) {  // K rows, 16-byte chunks
+  for (int x = lane; x < num_kv_heads * 16; x += kWave) {  // K and V rows, 16-byte chunks
     const int g = x >> 4, c = x & 15;
-    *reinterpret_cast<u32x4*>(ap.cache.k + ((page * num_kv_heads + g) * B + slot) * 128 + c * 8) =
+    const size_t dst = ((page * num_kv_heads + g) * B + slot) * 128 + c * 8;
+    *reinterpret_cast<u32x4*>(ap.cache.k + dst) =
         *reinterpret_cast<const u32x4*>(ap.k_new + kv0 + g * 128 + c * 8);
-  }
-  for (int x = lane; x < num_kv_heads * 128; x += kWave) {  // V columns of the page
-    const int g = x >> 7, d = x & 127;
-    ap.cache.v[((page * num_kv_heads + g) * 128 + d) * B + slot] = ap.v_new[kv0 + x];
+    *reinterpret_cast<u32x4*>(ap.cache.v + dst) =
+        *reinterpret_cast<const u32x4*>(ap.v_new + kv0 + g * 128 + c * 8);
   }
   for (int x = lane; x < idx_k_heads * 8; x += kWave) {  // index-key rows, 16-byte chunks
     const int h = x >> 3, c = x & 7;

@@ -35,7 +35,6 @@ __global__ __launch_bounds__(256, 4) void index_score_prefill_kernel(
     const uint16_t* __restrict__ idx_q, ChunkMap map, int32_t num_kv_heads,
     int32_t num_idx_heads, int32_t idx_k_heads, int32_t max_blocks, int32_t blocks_per_split,
     float* __restrict__ pooled) {
-  constexpr int NT = B / 32;                       // 32-token N tiles per block
   constexpr int BLOCK_BYTES = B * 128;             // B tokens x 64 bf16
   constexpr int WLOADS = BLOCK_BYTES / 1024 / 4;   // 1 KB loads per wave per block
   // the two key buffers are separate objects, each addressed at compile time:

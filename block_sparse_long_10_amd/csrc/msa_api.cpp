@@ -3,13 +3,15 @@
 //
 // Validation is pure host code and runs before any HIP call, so a rejected
 // call touches no device state.  Nothing here allocates, copies or
-// synchronises.
+// synchronises.  No C++ exception can leave an entry point: the error text
+// lives in a fixed thread-local buffer (no allocation), and every entry point
+// also catches whatever a callee might throw.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
-#include <string>
+#include <cstring>
 
 #include "msa.h"
 #include "msa_launch.h"
@@ -17,10 +19,10 @@
 
 namespace {
 
-thread_local std::string g_last_error;
+thread_local char g_last_error[512];
 
-msa_status fail(msa_status st, const std::string& msg) {
-  g_last_error = msg;
+msa_status fail(msa_status st, const char* msg) {
+  std::snprintf(g_last_error, sizeof g_last_error, "%s", msg);
   return st;
 }
 
@@ -101,7 +103,8 @@ msa::Cache cache_of(const msa_paged_kv* kv) {
 
 msa_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return MSA_OK;
-  return fail(MSA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  std::snprintf(g_last_error, sizeof g_last_error, "%s: %s", what, hipGetErrorString(e));
+  return MSA_ERR_HIP;
 }
 
 // decode workspace layout
@@ -223,52 +226,64 @@ msa_status check_prefill_sizes(const msa_params* p, const msa_paged_kv* kv, int3
 
 extern "C" {
 
-const char* msa_last_error(void) { return g_last_error.c_str(); }
+const char* msa_last_error(void) { return g_last_error; }
 
 const char* msa_version(void) { return "msa-mi355x 0.1.0 (gfx950)"; }
 
 size_t msa_decode_workspace_bytes(const msa_params* params, int32_t batch,
                                   int32_t max_blocks_per_seq) {
-  if (check_params(params) != MSA_OK || batch < 1 || max_blocks_per_seq < 1) return 0;
-  return decode_layout(params, batch, max_blocks_per_seq).total;
+  try {
+    if (check_params(params) != MSA_OK || batch < 1 || max_blocks_per_seq < 1) return 0;
+    return decode_layout(params, batch, max_blocks_per_seq).total;
+  } catch (...) {
+    return 0;
+  }
 }
 
 msa_status msa_index_score_decode(const msa_params* params, const msa_paged_kv* kv,
                                   const void* idx_q, const int32_t* seq_lens, int32_t batch,
                                   int32_t max_seq_len, float* pooled, void* stream) {
-  msa_status st = check_params(params);
-  if (st != MSA_OK) return st;
-  if ((st = check_kv(kv)) != MSA_OK) return st;
-  if (idx_q == nullptr || seq_lens == nullptr || pooled == nullptr)
-    return fail(MSA_ERR_INVALID_ARGUMENT, "idx_q, seq_lens and pooled must not be NULL");
-  if (batch < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "batch must be >= 1");
-  if (max_seq_len < 1 || (int64_t)max_seq_len > (int64_t)kv->max_blocks_per_seq * params->block_size)
-    return fail(MSA_ERR_INVALID_ARGUMENT, "max_seq_len must be in [1, max_blocks_per_seq*block_size]");
-  return hip_status(msa::launch_index_score_decode(dims_of(params), cache_of(kv),
-                                                   static_cast<const uint16_t*>(idx_q), seq_lens,
-                                                   batch, max_seq_len, pooled, nullptr,
-                                                   static_cast<hipStream_t>(stream)),
-                    "index score launch");
+  try {
+    msa_status st = check_params(params);
+    if (st != MSA_OK) return st;
+    if ((st = check_kv(kv)) != MSA_OK) return st;
+    if (idx_q == nullptr || seq_lens == nullptr || pooled == nullptr)
+      return fail(MSA_ERR_INVALID_ARGUMENT, "idx_q, seq_lens and pooled must not be NULL");
+    if (batch < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "batch must be >= 1");
+    if (max_seq_len < 1 || (int64_t)max_seq_len > (int64_t)kv->max_blocks_per_seq * params->block_size)
+      return fail(MSA_ERR_INVALID_ARGUMENT, "max_seq_len must be in [1, max_blocks_per_seq*block_size]");
+    return hip_status(msa::launch_index_score_decode(dims_of(params), cache_of(kv),
+                                                     static_cast<const uint16_t*>(idx_q), seq_lens,
+                                                     batch, max_seq_len, pooled, nullptr,
+                                                     static_cast<hipStream_t>(stream)),
+                      "index score launch");
+  } catch (...) {
+    return fail(MSA_ERR_HIP, "unexpected internal error");
+  }
 }
 
 msa_status msa_cache_append(const msa_params* params, const msa_paged_kv_mut* kv,
                             const void* k_new, const void* v_new, const void* idx_k_new,
                             const int32_t* start_pos, int32_t batch, int32_t n_new, void* stream) {
-  msa_status st = check_params(params);
-  if (st != MSA_OK) return st;
-  if ((st = check_kv_mut(kv)) != MSA_OK) return st;
-  if (k_new == nullptr || v_new == nullptr || idx_k_new == nullptr || start_pos == nullptr)
-    return fail(MSA_ERR_INVALID_ARGUMENT, "k_new, v_new, idx_k_new and start_pos must not be NULL");
-  if (batch < 1 || n_new < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "batch and n_new must be >= 1");
-  if (batch > 65535) return fail(MSA_ERR_UNSUPPORTED, "batch must be <= 65535");
-  if ((int64_t)n_new > (int64_t)kv->max_blocks_per_seq * params->block_size)
-    return fail(MSA_ERR_INVALID_ARGUMENT, "n_new exceeds max_blocks_per_seq * block_size");
-  return hip_status(msa::launch_cache_append(dims_of(params), cache_w_of(kv),
-                                             static_cast<const uint16_t*>(k_new),
-                                             static_cast<const uint16_t*>(v_new),
-                                             static_cast<const uint16_t*>(idx_k_new), start_pos,
-                                             batch, n_new, static_cast<hipStream_t>(stream)),
-                    "cache append launch");
+  try {
+    msa_status st = check_params(params);
+    if (st != MSA_OK) return st;
+    if ((st = check_kv_mut(kv)) != MSA_OK) return st;
+    if (k_new == nullptr || v_new == nullptr || idx_k_new == nullptr || start_pos == nullptr)
+      return fail(MSA_ERR_INVALID_ARGUMENT, "k_new, v_new, idx_k_new and start_pos must not be NULL");
+    if (batch < 1 || n_new < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "batch and n_new must be >= 1");
+    if (batch > 65535) return fail(MSA_ERR_UNSUPPORTED, "batch must be <= 65535");
+    if ((int64_t)n_new > (int64_t)kv->max_blocks_per_seq * params->block_size)
+      return fail(MSA_ERR_INVALID_ARGUMENT, "n_new exceeds max_blocks_per_seq * block_size");
+    return hip_status(msa::launch_cache_append(dims_of(params), cache_w_of(kv),
+                                               static_cast<const uint16_t*>(k_new),
+                                               static_cast<const uint16_t*>(v_new),
+                                               static_cast<const uint16_t*>(idx_k_new), start_pos,
+                                               batch, n_new, static_cast<hipStream_t>(stream)),
+                      "cache append launch");
+  } catch (...) {
+    return fail(MSA_ERR_HIP, "unexpected internal error");
+  }
 }
 
 static msa_status decode_impl(const msa_params* params, const msa_paged_kv* kv, const void* q,
@@ -281,8 +296,12 @@ msa_status msa_decode(const msa_params* params, const msa_paged_kv* kv, const vo
                       const void* idx_q, const int32_t* seq_lens, int32_t batch,
                       int32_t max_seq_len, float* out, int32_t* sel, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  return decode_impl(params, kv, q, idx_q, seq_lens, batch, max_seq_len, out, sel, workspace,
-                     workspace_bytes, stream, nullptr);
+  try {
+    return decode_impl(params, kv, q, idx_q, seq_lens, batch, max_seq_len, out, sel, workspace,
+                       workspace_bytes, stream, nullptr);
+  } catch (...) {
+    return fail(MSA_ERR_HIP, "unexpected internal error");
+  }
 }
 
 msa_status msa_decode_append(const msa_params* params, const msa_paged_kv_mut* kv,
@@ -290,16 +309,20 @@ msa_status msa_decode_append(const msa_params* params, const msa_paged_kv_mut* k
                              const void* q, const void* idx_q, const int32_t* seq_lens,
                              int32_t batch, int32_t max_seq_len, float* out, int32_t* sel,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  msa_status st = check_kv_mut(kv);
-  if (st != MSA_OK) return st;
-  if (k_new == nullptr || v_new == nullptr || idx_k_new == nullptr)
-    return fail(MSA_ERR_INVALID_ARGUMENT, "k_new, v_new and idx_k_new must not be NULL");
-  const msa_paged_kv view = read_view(kv);
-  const msa::DecodeAppend ap{cache_w_of(kv), static_cast<const uint16_t*>(k_new),
-                             static_cast<const uint16_t*>(v_new),
-                             static_cast<const uint16_t*>(idx_k_new)};
-  return decode_impl(params, &view, q, idx_q, seq_lens, batch, max_seq_len, out, sel, workspace,
-                     workspace_bytes, stream, &ap);
+  try {
+    msa_status st = check_kv_mut(kv);
+    if (st != MSA_OK) return st;
+    if (k_new == nullptr || v_new == nullptr || idx_k_new == nullptr)
+      return fail(MSA_ERR_INVALID_ARGUMENT, "k_new, v_new and idx_k_new must not be NULL");
+    const msa_paged_kv view = read_view(kv);
+    const msa::DecodeAppend ap{cache_w_of(kv), static_cast<const uint16_t*>(k_new),
+                               static_cast<const uint16_t*>(v_new),
+                               static_cast<const uint16_t*>(idx_k_new)};
+    return decode_impl(params, &view, q, idx_q, seq_lens, batch, max_seq_len, out, sel, workspace,
+                       workspace_bytes, stream, &ap);
+  } catch (...) {
+    return fail(MSA_ERR_HIP, "unexpected internal error");
+  }
 }
 
 static msa_status decode_impl(const msa_params* params, const msa_paged_kv* kv, const void* q,
@@ -340,105 +363,129 @@ static msa_status decode_impl(const msa_params* params, const msa_paged_kv* kv, 
 
 size_t msa_prefill_workspace_bytes(const msa_params* params, int32_t prior_len, int32_t chunk_len,
                                    int32_t max_blocks_per_seq) {
-  if (check_params(params) != MSA_OK || prior_len < 0 || chunk_len < 1 || max_blocks_per_seq < 1)
+  try {
+    if (check_params(params) != MSA_OK || prior_len < 0 || chunk_len < 1 || max_blocks_per_seq < 1)
+      return 0;
+    return prefill_layout(params, prior_len, chunk_len, max_blocks_per_seq).total;
+  } catch (...) {
     return 0;
-  return prefill_layout(params, prior_len, chunk_len, max_blocks_per_seq).total;
+  }
 }
 
 msa_status msa_index_score_prefill(const msa_params* params, const msa_paged_kv* kv,
                                    const void* idx_q, int32_t prior_len, int32_t chunk_len,
                                    float* pooled, void* stream) {
-  msa_status st = check_params(params);
-  if (st != MSA_OK) return st;
-  if ((st = check_kv(kv)) != MSA_OK) return st;
-  if (idx_q == nullptr || pooled == nullptr)
-    return fail(MSA_ERR_INVALID_ARGUMENT, "idx_q and pooled must not be NULL");
-  if ((st = check_prefill_sizes(params, kv, prior_len, chunk_len)) != MSA_OK) return st;
-  const int32_t B = params->block_size;
-  const int32_t tiles = num_tiles_of(prior_len, chunk_len, B);
-  return hip_status(msa::launch_index_score_prefill(
-                        dims_of(params), cache_of(kv), static_cast<const uint16_t*>(idx_q),
-                        single_map(prior_len, chunk_len, kv->max_blocks_per_seq), tiles,
-                        prior_len / B + tiles - 1, pooled, static_cast<hipStream_t>(stream)),
-                    "prefill index score launch");
+  try {
+    msa_status st = check_params(params);
+    if (st != MSA_OK) return st;
+    if ((st = check_kv(kv)) != MSA_OK) return st;
+    if (idx_q == nullptr || pooled == nullptr)
+      return fail(MSA_ERR_INVALID_ARGUMENT, "idx_q and pooled must not be NULL");
+    if ((st = check_prefill_sizes(params, kv, prior_len, chunk_len)) != MSA_OK) return st;
+    const int32_t B = params->block_size;
+    const int32_t tiles = num_tiles_of(prior_len, chunk_len, B);
+    return hip_status(msa::launch_index_score_prefill(
+                          dims_of(params), cache_of(kv), static_cast<const uint16_t*>(idx_q),
+                          single_map(prior_len, chunk_len, kv->max_blocks_per_seq), tiles,
+                          prior_len / B + tiles - 1, pooled, static_cast<hipStream_t>(stream)),
+                      "prefill index score launch");
+  } catch (...) {
+    return fail(MSA_ERR_HIP, "unexpected internal error");
+  }
 }
 
 msa_status msa_block_topk_prefill(const msa_params* params, int32_t prior_len, int32_t chunk_len,
                                   int32_t max_blocks_per_seq, const float* pooled, int32_t* sel,
                                   void* stream) {
-  msa_status st = check_params(params);
-  if (st != MSA_OK) return st;
-  if (pooled == nullptr || sel == nullptr)
-    return fail(MSA_ERR_INVALID_ARGUMENT, "pooled and sel must not be NULL");
-  if (prior_len < 0 || chunk_len < 1 || max_blocks_per_seq < 1 ||
-      (int64_t)prior_len + chunk_len > (int64_t)max_blocks_per_seq * params->block_size)
-    return fail(MSA_ERR_INVALID_ARGUMENT, "inconsistent prior_len, chunk_len, max_blocks_per_seq");
-  return hip_status(msa::launch_block_topk_prefill(
-                        dims_of(params), single_map(prior_len, chunk_len, max_blocks_per_seq),
-                        num_tiles_of(prior_len, chunk_len, params->block_size),
-                        max_blocks_per_seq, pooled, sel, static_cast<hipStream_t>(stream)),
-                    "prefill topk launch");
+  try {
+    msa_status st = check_params(params);
+    if (st != MSA_OK) return st;
+    if (pooled == nullptr || sel == nullptr)
+      return fail(MSA_ERR_INVALID_ARGUMENT, "pooled and sel must not be NULL");
+    if (prior_len < 0 || chunk_len < 1 || max_blocks_per_seq < 1 ||
+        (int64_t)prior_len + chunk_len > (int64_t)max_blocks_per_seq * params->block_size)
+      return fail(MSA_ERR_INVALID_ARGUMENT, "inconsistent prior_len, chunk_len, max_blocks_per_seq");
+    return hip_status(msa::launch_block_topk_prefill(
+                          dims_of(params), single_map(prior_len, chunk_len, max_blocks_per_seq),
+                          num_tiles_of(prior_len, chunk_len, params->block_size),
+                          max_blocks_per_seq, pooled, sel, static_cast<hipStream_t>(stream)),
+                      "prefill topk launch");
+  } catch (...) {
+    return fail(MSA_ERR_HIP, "unexpected internal error");
+  }
 }
 
 msa_status msa_sparse_attn_prefill(const msa_params* params, const msa_paged_kv* kv, const void* q,
                                    int32_t prior_len, int32_t chunk_len, const int32_t* sel,
                                    float* out, void* stream) {
-  msa_status st = check_params(params);
-  if (st != MSA_OK) return st;
-  if ((st = check_kv(kv)) != MSA_OK) return st;
-  if (q == nullptr || sel == nullptr || out == nullptr)
-    return fail(MSA_ERR_INVALID_ARGUMENT, "q, sel and out must not be NULL");
-  if ((st = check_prefill_sizes(params, kv, prior_len, chunk_len)) != MSA_OK) return st;
-  return hip_status(msa::launch_sparse_attn_prefill(
-                        dims_of(params), cache_of(kv), static_cast<const uint16_t*>(q),
-                        single_map(prior_len, chunk_len, kv->max_blocks_per_seq),
-                        num_tiles_of(prior_len, chunk_len, params->block_size), sel, out,
-                        static_cast<hipStream_t>(stream)),
-                    "prefill sparse attention launch");
+  try {
+    msa_status st = check_params(params);
+    if (st != MSA_OK) return st;
+    if ((st = check_kv(kv)) != MSA_OK) return st;
+    if (q == nullptr || sel == nullptr || out == nullptr)
+      return fail(MSA_ERR_INVALID_ARGUMENT, "q, sel and out must not be NULL");
+    if ((st = check_prefill_sizes(params, kv, prior_len, chunk_len)) != MSA_OK) return st;
+    return hip_status(msa::launch_sparse_attn_prefill(
+                          dims_of(params), cache_of(kv), static_cast<const uint16_t*>(q),
+                          single_map(prior_len, chunk_len, kv->max_blocks_per_seq),
+                          num_tiles_of(prior_len, chunk_len, params->block_size), sel, out,
+                          static_cast<hipStream_t>(stream)),
+                      "prefill sparse attention launch");
+  } catch (...) {
+    return fail(MSA_ERR_HIP, "unexpected internal error");
+  }
 }
 
 msa_status msa_prefill_chunk(const msa_params* params, const msa_paged_kv* kv, const void* q,
                              const void* idx_q, int32_t prior_len, int32_t chunk_len, float* out,
                              int32_t* sel, void* workspace, size_t workspace_bytes, void* stream) {
-  msa_status st = check_params(params);
-  if (st != MSA_OK) return st;
-  if ((st = check_kv(kv)) != MSA_OK) return st;
-  if (q == nullptr || idx_q == nullptr || out == nullptr)
-    return fail(MSA_ERR_INVALID_ARGUMENT, "q, idx_q and out must not be NULL");
-  if ((st = check_prefill_sizes(params, kv, prior_len, chunk_len)) != MSA_OK) return st;
-  const PrefillWs w = prefill_layout(params, prior_len, chunk_len, kv->max_blocks_per_seq);
-  if (workspace == nullptr || workspace_bytes < w.total)
-    return fail(MSA_ERR_WORKSPACE, "workspace missing or smaller than msa_prefill_workspace_bytes()");
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  float* pooled = reinterpret_cast<float*>(ws + w.pooled);
-  int32_t* sel_buf = sel != nullptr ? sel : reinterpret_cast<int32_t*>(ws + w.sel);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const msa::Dims d = dims_of(params);
-  const msa::Cache c = cache_of(kv);
-  const msa::ChunkMap m = single_map(prior_len, chunk_len, kv->max_blocks_per_seq);
-  const int32_t tiles = num_tiles_of(prior_len, chunk_len, params->block_size);
-  const int32_t max_own = prior_len / params->block_size + tiles - 1;
-  st = hip_status(msa::launch_index_score_prefill(d, c, static_cast<const uint16_t*>(idx_q), m,
-                                                  tiles, max_own, pooled, s),
-                  "prefill index score launch");
-  if (st != MSA_OK) return st;
-  st = hip_status(msa::launch_block_topk_prefill(d, m, tiles, kv->max_blocks_per_seq, pooled,
-                                                 sel_buf, s),
-                  "prefill topk launch");
-  if (st != MSA_OK) return st;
-  return hip_status(msa::launch_sparse_attn_prefill(d, c, static_cast<const uint16_t*>(q), m,
-                                                    tiles, sel_buf, out, s),
-                    "prefill sparse attention launch");
+  try {
+    msa_status st = check_params(params);
+    if (st != MSA_OK) return st;
+    if ((st = check_kv(kv)) != MSA_OK) return st;
+    if (q == nullptr || idx_q == nullptr || out == nullptr)
+      return fail(MSA_ERR_INVALID_ARGUMENT, "q, idx_q and out must not be NULL");
+    if ((st = check_prefill_sizes(params, kv, prior_len, chunk_len)) != MSA_OK) return st;
+    const PrefillWs w = prefill_layout(params, prior_len, chunk_len, kv->max_blocks_per_seq);
+    if (workspace == nullptr || workspace_bytes < w.total)
+      return fail(MSA_ERR_WORKSPACE, "workspace missing or smaller than msa_prefill_workspace_bytes()");
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    float* pooled = reinterpret_cast<float*>(ws + w.pooled);
+    int32_t* sel_buf = sel != nullptr ? sel : reinterpret_cast<int32_t*>(ws + w.sel);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const msa::Dims d = dims_of(params);
+    const msa::Cache c = cache_of(kv);
+    const msa::ChunkMap m = single_map(prior_len, chunk_len, kv->max_blocks_per_seq);
+    const int32_t tiles = num_tiles_of(prior_len, chunk_len, params->block_size);
+    const int32_t max_own = prior_len / params->block_size + tiles - 1;
+    st = hip_status(msa::launch_index_score_prefill(d, c, static_cast<const uint16_t*>(idx_q), m,
+                                                    tiles, max_own, pooled, s),
+                    "prefill index score launch");
+    if (st != MSA_OK) return st;
+    st = hip_status(msa::launch_block_topk_prefill(d, m, tiles, kv->max_blocks_per_seq, pooled,
+                                                   sel_buf, s),
+                    "prefill topk launch");
+    if (st != MSA_OK) return st;
+    return hip_status(msa::launch_sparse_attn_prefill(d, c, static_cast<const uint16_t*>(q), m,
+                                                      tiles, sel_buf, out, s),
+                      "prefill sparse attention launch");
+  } catch (...) {
+    return fail(MSA_ERR_HIP, "unexpected internal error");
+  }
 }
 
 size_t msa_prefill_varlen_workspace_bytes(const msa_params* params, const int32_t* prior_lens_host,
                                           const int32_t* chunk_lens_host, int32_t batch,
                                           int32_t max_blocks_per_seq) {
-  if (check_params(params) != MSA_OK || max_blocks_per_seq < 1 ||
-      check_varlen(params, max_blocks_per_seq, prior_lens_host, chunk_lens_host, batch) != MSA_OK)
+  try {
+    if (check_params(params) != MSA_OK || max_blocks_per_seq < 1 ||
+        check_varlen(params, max_blocks_per_seq, prior_lens_host, chunk_lens_host, batch) != MSA_OK)
+      return 0;
+    const VarlenSizes v = varlen_sizes(prior_lens_host, chunk_lens_host, batch, params->block_size);
+    return varlen_layout(params, v.tiles, batch, max_blocks_per_seq).total;
+  } catch (...) {
     return 0;
-  const VarlenSizes v = varlen_sizes(prior_lens_host, chunk_lens_host, batch, params->block_size);
-  return varlen_layout(params, v.tiles, batch, max_blocks_per_seq).total;
+  }
 }
 
 msa_status msa_prefill_varlen(const msa_params* params, const msa_paged_kv* kv, const void* q,
@@ -447,49 +494,53 @@ msa_status msa_prefill_varlen(const msa_params* params, const msa_paged_kv* kv, 
                               const int32_t* chunk_lens_host, int32_t batch, float* out,
                               int32_t* sel, void* workspace, size_t workspace_bytes,
                               void* stream) {
-  msa_status st = check_params(params);
-  if (st != MSA_OK) return st;
-  if ((st = check_kv(kv)) != MSA_OK) return st;
-  if (q == nullptr || idx_q == nullptr || out == nullptr || prior_lens == nullptr ||
-      chunk_lens == nullptr)
-    return fail(MSA_ERR_INVALID_ARGUMENT,
-                "q, idx_q, out, prior_lens and chunk_lens must not be NULL");
-  if (batch > 65535) return fail(MSA_ERR_UNSUPPORTED, "batch must be <= 65535");
-  if ((st = check_varlen(params, kv->max_blocks_per_seq, prior_lens_host, chunk_lens_host,
-                         batch)) != MSA_OK)
-    return st;
-  const VarlenSizes v = varlen_sizes(prior_lens_host, chunk_lens_host, batch, params->block_size);
-  const VarlenWs w = varlen_layout(params, v.tiles, batch, kv->max_blocks_per_seq);
-  if (workspace == nullptr || workspace_bytes < w.total)
-    return fail(MSA_ERR_WORKSPACE,
-                "workspace missing or smaller than msa_prefill_varlen_workspace_bytes()");
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  float* pooled = reinterpret_cast<float*>(ws + w.pooled);
-  int32_t* sel_buf = sel != nullptr ? sel : reinterpret_cast<int32_t*>(ws + w.sel);
-  int32_t* tile_seq = reinterpret_cast<int32_t*>(ws + w.tile_seq);
-  int32_t* tile_start = reinterpret_cast<int32_t*>(ws + w.tile_start);
-  int32_t* q_start = reinterpret_cast<int32_t*>(ws + w.q_start);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const msa::Dims d = dims_of(params);
-  const msa::Cache c = cache_of(kv);
-  const int32_t tiles = (int32_t)v.tiles;
-  st = hip_status(msa::launch_chunk_map(prior_lens, chunk_lens, batch, params->block_size, tiles,
-                                        tile_seq, tile_start, q_start, s),
-                  "prefill chunk map launch");
-  if (st != MSA_OK) return st;
-  const msa::ChunkMap m{tile_seq, tile_start, q_start, prior_lens, chunk_lens, 0, 0,
-                        kv->max_blocks_per_seq};
-  st = hip_status(msa::launch_index_score_prefill(d, c, static_cast<const uint16_t*>(idx_q), m,
-                                                  tiles, v.max_own, pooled, s),
-                  "prefill index score launch");
-  if (st != MSA_OK) return st;
-  st = hip_status(msa::launch_block_topk_prefill(d, m, tiles, kv->max_blocks_per_seq, pooled,
-                                                 sel_buf, s),
-                  "prefill topk launch");
-  if (st != MSA_OK) return st;
-  return hip_status(msa::launch_sparse_attn_prefill(d, c, static_cast<const uint16_t*>(q), m,
-                                                    tiles, sel_buf, out, s),
-                    "prefill sparse attention launch");
+  try {
+    msa_status st = check_params(params);
+    if (st != MSA_OK) return st;
+    if ((st = check_kv(kv)) != MSA_OK) return st;
+    if (q == nullptr || idx_q == nullptr || out == nullptr || prior_lens == nullptr ||
+        chunk_lens == nullptr)
+      return fail(MSA_ERR_INVALID_ARGUMENT,
+                  "q, idx_q, out, prior_lens and chunk_lens must not be NULL");
+    if (batch > 65535) return fail(MSA_ERR_UNSUPPORTED, "batch must be <= 65535");
+    if ((st = check_varlen(params, kv->max_blocks_per_seq, prior_lens_host, chunk_lens_host,
+                           batch)) != MSA_OK)
+      return st;
+    const VarlenSizes v = varlen_sizes(prior_lens_host, chunk_lens_host, batch, params->block_size);
+    const VarlenWs w = varlen_layout(params, v.tiles, batch, kv->max_blocks_per_seq);
+    if (workspace == nullptr || workspace_bytes < w.total)
+      return fail(MSA_ERR_WORKSPACE,
+                  "workspace missing or smaller than msa_prefill_varlen_workspace_bytes()");
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    float* pooled = reinterpret_cast<float*>(ws + w.pooled);
+    int32_t* sel_buf = sel != nullptr ? sel : reinterpret_cast<int32_t*>(ws + w.sel);
+    int32_t* tile_seq = reinterpret_cast<int32_t*>(ws + w.tile_seq);
+    int32_t* tile_start = reinterpret_cast<int32_t*>(ws + w.tile_start);
+    int32_t* q_start = reinterpret_cast<int32_t*>(ws + w.q_start);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const msa::Dims d = dims_of(params);
+    const msa::Cache c = cache_of(kv);
+    const int32_t tiles = (int32_t)v.tiles;
+    st = hip_status(msa::launch_chunk_map(prior_lens, chunk_lens, batch, params->block_size, tiles,
+                                          tile_seq, tile_start, q_start, s),
+                    "prefill chunk map launch");
+    if (st != MSA_OK) return st;
+    const msa::ChunkMap m{tile_seq, tile_start, q_start, prior_lens, chunk_lens, 0, 0,
+                          kv->max_blocks_per_seq};
+    st = hip_status(msa::launch_index_score_prefill(d, c, static_cast<const uint16_t*>(idx_q), m,
+                                                    tiles, v.max_own, pooled, s),
+                    "prefill index score launch");
+    if (st != MSA_OK) return st;
+    st = hip_status(msa::launch_block_topk_prefill(d, m, tiles, kv->max_blocks_per_seq, pooled,
+                                                   sel_buf, s),
+                    "prefill topk launch");
+    if (st != MSA_OK) return st;
+    return hip_status(msa::launch_sparse_attn_prefill(d, c, static_cast<const uint16_t*>(q), m,
+                                                      tiles, sel_buf, out, s),
+                      "prefill sparse attention launch");
+  } catch (...) {
+    return fail(MSA_ERR_HIP, "unexpected internal error");
+  }
 }
 
 }  // extern "C"
@@ -497,24 +548,32 @@ msa_status msa_prefill_varlen(const msa_params* params, const msa_paged_kv* kv, 
 // ------------------------------------------------------------ measurement
 extern "C" msa_status msa_probe_read_stream(const void* src, size_t bytes, int32_t workgroups,
                                             uint32_t* sink, void* stream) {
-  if (src == nullptr || sink == nullptr)
-    return fail(MSA_ERR_INVALID_ARGUMENT, "src and sink must not be NULL");
-  if (bytes < 16 || bytes % 16 != 0)
-    return fail(MSA_ERR_INVALID_ARGUMENT, "bytes must be a positive multiple of 16");
-  if (workgroups < 1 || workgroups > (1 << 20))
-    return fail(MSA_ERR_INVALID_ARGUMENT, "workgroups must be in [1, 2^20]");
-  return hip_status(msa::launch_read_stream(src, bytes, workgroups, sink,
-                                            static_cast<hipStream_t>(stream)),
-                    "read stream launch");
+  try {
+    if (src == nullptr || sink == nullptr)
+      return fail(MSA_ERR_INVALID_ARGUMENT, "src and sink must not be NULL");
+    if (bytes < 16 || bytes % 16 != 0)
+      return fail(MSA_ERR_INVALID_ARGUMENT, "bytes must be a positive multiple of 16");
+    if (workgroups < 1 || workgroups > (1 << 20))
+      return fail(MSA_ERR_INVALID_ARGUMENT, "workgroups must be in [1, 2^20]");
+    return hip_status(msa::launch_read_stream(src, bytes, workgroups, sink,
+                                              static_cast<hipStream_t>(stream)),
+                      "read stream launch");
+  } catch (...) {
+    return fail(MSA_ERR_HIP, "unexpected internal error");
+  }
 }
 
 extern "C" msa_status msa_probe_mfma_bf16(int32_t iters, int32_t workgroups, float* sink,
                                           void* stream) {
-  if (sink == nullptr) return fail(MSA_ERR_INVALID_ARGUMENT, "sink must not be NULL");
-  if (iters < 1 || iters > (1 << 24))
-    return fail(MSA_ERR_INVALID_ARGUMENT, "iters must be in [1, 2^24]");
-  if (workgroups < 1 || workgroups > 65536)
-    return fail(MSA_ERR_INVALID_ARGUMENT, "workgroups must be in [1, 65536]");
-  return hip_status(msa::launch_mfma_loop(iters, workgroups, sink, static_cast<hipStream_t>(stream)),
-                    "mfma loop launch");
+  try {
+    if (sink == nullptr) return fail(MSA_ERR_INVALID_ARGUMENT, "sink must not be NULL");
+    if (iters < 1 || iters > (1 << 24))
+      return fail(MSA_ERR_INVALID_ARGUMENT, "iters must be in [1, 2^24]");
+    if (workgroups < 1 || workgroups > 65536)
+      return fail(MSA_ERR_INVALID_ARGUMENT, "workgroups must be in [1, 65536]");
+    return hip_status(msa::launch_mfma_loop(iters, workgroups, sink, static_cast<hipStream_t>(stream)),
+                      "mfma loop launch");
+  } catch (...) {
+    return fail(MSA_ERR_HIP, "unexpected internal error");
+  }
 }

@@ -43,6 +43,26 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_base) {
 // Wait for every outstanding vector-memory operation of this wave.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane u supplies the address of 4 consecutive 16-bit elements; lane i
+// of the group receives element i%4 of the chunks addressed by lanes
+// i/4, 4 + i/4, 8 + i/4 and 12 + i/4, in that order.  So if lane u = 4j + c
+// addresses row r0 + j, columns c0 + 4c .. c0 + 4c + 3 of a row-major tile,
+// lane i receives column c0 + i of rows r0 .. r0 + 3: the column a matrix-core
+// operand needs when its K dimension runs along the rows.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* lds_byte_addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(__attribute__((address_space(3))) void*)(lds_byte_addr));
+}
+// Two transpose reads (rows r0..r0+3, then r0+4..r0+7) as one 8-element operand.
+__device__ __forceinline__ bf16x8 join_tr(i16x4 a, i16x4 b) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
   return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 }
@@ -99,6 +119,17 @@ __device__ __forceinline__ float wave_min(float v) {
   v = row16_min(v);
   v = fminf(v, xor_lane(v, 16));
   return fminf(v, xor_lane(v, 32));
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v = min(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v = max(v, __shfl_xor(v, m, kWave));
+  return v;
 }
 
 __device__ __forceinline__ float max4(f32x4 v) { return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])); }

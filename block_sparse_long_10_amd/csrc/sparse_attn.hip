@@ -5,10 +5,11 @@
 //
 // Both kernels compute S^T = K Q^T (keys on the MFMA M side, query rows on the
 // N side) so that a query row's softmax statistics live in one lane pair, and
-// O^T = V^T P^T with V^T read straight from the page layout [D][B] (8
-// consecutive tokens of one dimension = one 16-byte operand).  Probabilities
-// enter the bf16 PV contraction as hi + lo bf16 parts (P - hi - lo < 2^-16 P),
-// so the only rounding left is fp32 accumulation.
+// O^T = V^T P^T.  K and V pages are token-major ([B][D] per page and head); V
+// is staged in LDS and V^T, whose MFMA operand holds 8 consecutive tokens of
+// one dimension, is formed by LDS transpose reads (ds_read_b64_tr_b16).
+// Probabilities enter the bf16 PV contraction as hi + lo bf16 parts
+// (P - hi - lo < 2^-16 P), so the only rounding left is fp32 accumulation.
 //
 // Decode: one launch after the index scores (two for large batches).  One
 // workgroup per (sequence, group, kept-block slot) derives the group's
@@ -20,7 +21,7 @@
 //
 // Prefill: one workgroup per (tile, group, 256 query rows); rows are
 // (query, head) pairs of the group.  Kept blocks are staged whole through LDS
-// (K token-major, V^T dimension-major, XOR-swizzled 16-byte chunks) and
+// (K and V token-major, XOR-swizzled 16-byte chunks) and
 // consumed 32 keys at a time with v_mfma_f32_32x32x16_bf16 and an online
 // softmax; the causal mask applies inside the tile's diagonal block only.
 #include <algorithm>
@@ -68,9 +69,9 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
   __shared__ int sel_s[kMaxTopK], tmp_s[kMaxTopK];
   __shared__ AttendShared ash;
   __shared__ int is_last;
-  // dynamic LDS: the per-wave outputs of the block attention (sized by the
-  // group), then the merge's scratch (the merge runs after a barrier that
-  // follows the last read of the outputs)
+  // dynamic LDS: the staged V rows of the block attention, then the per-wave
+  // outputs (sized by the group), then the merge's scratch (each phase starts
+  // after a barrier that follows the last read of the previous one)
   extern __shared__ __attribute__((aligned(16))) float dyn_lds[];
   MergeShared& msh = *reinterpret_cast<MergeShared*>(dyn_lds);
 
@@ -101,7 +102,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
   const __amdgpu_buffer_rsrc_t rml = buffer_of(part_ml + sg * top_k * group * 4, ml_bytes);
   const int32_t page = blk >= 0 ? block_table[(size_t)s * max_blocks + blk] : 0;
   attend_block<B>(kc, vc, page, blk, L, q + ((size_t)s * Hq + (size_t)g * group) * 128,
-                  num_kv_heads, g, group, scale_log2, slot, ro, rml, ash, dyn_lds);
+                  num_kv_heads, g, group, scale_log2, slot, ro, rml, ash, dyn_lds,
+                  reinterpret_cast<uint8_t*>(dyn_lds));
 
   // hand-off: stores complete, then count this slot in; the last slot
   // workgroup reads the partials with agent-scope loads issued after its
@@ -129,9 +131,8 @@ hipError_t launch_decode_attn(const Dims& d, const Cache& c, const uint16_t* q,
   const dim3 grid_sg(d.num_kv_heads, batch);
   const dim3 grid_attn(d.top_k, d.num_kv_heads, batch);
   const bool fused = (size_t)d.top_k * d.num_kv_heads * batch <= kFusedTopkMaxWorkgroups;
-  // the dynamic LDS (block outputs, then merge scratch) is sized by the group:
-  // at group 8 it is half the size of group 16's, so more workgroups fit a CU
-  const size_t dyn = std::max(attend_wo_bytes(G), sizeof(MergeShared));
+  // the dynamic LDS (staged V, block outputs, then merge scratch)
+  const size_t dyn = std::max(std::max(attend_wo_bytes(G), sizeof(MergeShared)), kAttendVStageBytes);
 #define MSA_ATTN_ARGS c.k, c.v, c.block_table, c.max_blocks, q, seq_lens, pooled, sel, \
     d.num_kv_heads, G, d.top_k, d.sink_blocks, d.local_blocks, sl2, part_o, part_ml, counters, out
   if (d.block_size == 64) {
@@ -206,10 +207,6 @@ __device__ __forceinline__ float truncated_rest(float a) {
   return a - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) & 0xFFFF0000u);
 }
 
-// A wave-uniform float moved to a scalar register.
-__device__ __forceinline__ float uniform_f32(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
-}
 
 template <int B>
 __global__ __launch_bounds__(512) void prefill_attn_kernel(
@@ -218,12 +215,9 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
     const int32_t* __restrict__ sel, ChunkMap map, int32_t num_kv_heads, int32_t group,
     int32_t top_k, int32_t num_units, int32_t zr, float scale_log2, float* __restrict__ out) {
   constexpr int KBYTES = B * 256;          // K block: B rows of 256 bytes
-  constexpr int VROW = 2 * B;              // V^T row: B keys
-  constexpr int VCH = B / 8;               // 16-byte chunks per V^T row
-  constexpr int VBYTES = 128 * VROW;
+  constexpr int VBYTES = B * 256;          // V block: B rows of 256 bytes
   constexpr int KI = KBYTES / 1024 / kPrefillWaves;  // 1 KB wave loads per block, K
-  constexpr int VI = VBYTES / 1024 / kPrefillWaves;  // and V^T
-  constexpr int VRPI = 1024 / VROW;                  // V^T rows per wave load
+  constexpr int VI = VBYTES / 1024 / kPrefillWaves;  // and V
   // the two ring slots are separate objects, each addressed at compile time:
   // reads of one slot then provably miss the direct loads into the other,
   // and need not wait for them
@@ -276,8 +270,13 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   }
   // the wave's query positions, for the causal diagonal block (wave-uniform:
   // held in scalar registers)
-  const float pos_min = uniform_f32(wave_min((float)pos));
-  const float pos_max = uniform_f32(wave_max((float)pos));
+  const int pos_min = __builtin_amdgcn_readfirstlane(wave_min_i(pos));
+  const int pos_max = __builtin_amdgcn_readfirstlane(wave_max_i(pos));
+  // tokens of the diagonal block past the sequence's end (the last tile's):
+  // their V rows are zeroed in LDS after staging, since unwritten cache slots
+  // may hold any bits and a zero probability times NaN is NaN
+  const int seq_end = prior_len + loc.chunk;
+  const int diag_valid = min(B, seq_end - own * B);
 
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(kc);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vc);
@@ -300,9 +299,9 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
       const int ins = wave * VI + i;
-      const int dd = ins * VRPI + ln / VCH;
-      const int c = (ln % VCH) ^ (dd & (VCH - 1));
-      load_lds16(vg + (uint32_t)(dd * VROW + c * 16), vdst + ins * 1024);
+      const int key = ins * 4 + (ln >> 4);
+      const int c = (ln & 15) ^ (4 * (key & 3));
+      load_lds16(vg + (uint32_t)(key * 256 + c * 16), vdst + ins * 1024);
     }
   };
 
@@ -369,12 +368,18 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   };
 
   // LDS byte addresses of this lane's operand rows.  K: chunk ks of key
-  // 32 s + kmap(m) sits at s*8192 + (k_lane ^ 32 ks); V^T: keys 32 s + 16 s2 +
-  // 8 half.. of dimension 32 mt + m sit at 32 mt VROW + (v_lane ^ 16 (4 s +
-  // 2 s2)).  (The swizzles XOR only address bits 4..7, and rows are 256 or 128
-  // bytes, so the XOR and the row/step/slot offsets commute.)
+  // 32 s + kmap(m) sits at s*8192 + (k_lane ^ 32 ks).  V (16-byte chunk c of
+  // key row r stored at chunk c ^ 4(r%4)): the V^T operand of dimensions
+  // 32 mt .. 32 mt + 31 and keys 32 s + 16 s2 + 8 half .. +7 is two transpose
+  // reads, in which lane u = lane%16 of 16-lane group h4 = lane/16 addresses key
+  // row 32 s + 16 s2 + 8 (h4/2) + u/4 (+4 for the second read), dimensions
+  // 32 mt + 16 (h4%2) + 4 (u%4) .. +3: at (v_lane + (32 s + 16 s2) 256) ^ 64 mt.
+  // (The swizzles XOR only address bits 4..7 and rows are 256 bytes, so the
+  // XOR and the row/step offsets commute.)
   const uint32_t k_lane = (uint32_t)(kmap(m) * 256 + ((half ^ kswz(kmap(m))) << 4));
-  const uint32_t v_lane = (uint32_t)(m * VROW + (((m & (VCH - 1)) ^ half) << 4));
+  const int u16 = lane & 15, h4 = lane >> 4;
+  const uint32_t v_lane = (uint32_t)((8 * (h4 >> 1) + (u16 >> 2)) * 256 + 64 * (u16 >> 2) +
+                                     32 * (h4 & 1) + 8 * (u16 & 3));
 
   // attention of the wave's rows over kept block j, staged in ks_ and vs_
   auto attend = [&](int j, const uint8_t* ks_, const uint8_t* vs_) {
@@ -393,11 +398,12 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
       asm volatile("" : "+v"(a));
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        const uint32_t a2 = a ^ (uint32_t)((s * 4 + 2 * s2) << 4);
+        const uint32_t a2 = a + (uint32_t)((32 * s + 16 * s2) * 256);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          vf[s2][mt] = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(vs_ + a2 + mt * 32 * VROW));
+        for (int mt = 0; mt < 4; ++mt) {
+          const uint32_t am = a2 ^ (uint32_t)(64 * mt);
+          vf[s2][mt] = join_tr(lds_read_tr16(vs_ + am), lds_read_tr16(vs_ + am + 4 * 256));
+        }
       }
     };
     // S^T = K Q^T of 32 keys x the wave's 32 rows
@@ -415,12 +421,12 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
     load_k(0, kf);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if (diag && (float)(key0 + 32 * s) > pos_max) break;  // wave sees none of these keys
+      if (diag && key0 + 32 * s > pos_max) break;  // wave sees none of these keys
       f32x16 acc = scores(kf);
       if (s + 1 < NS) load_k(s + 1, kf);
       bf16x8 vf[2][4];
       load_v(s, vf);
-      if (diag && (float)(key0 + 32 * s + 31) > pos_min) {
+      if (diag && key0 + 32 * s + 31 > pos_min) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int kk = 32 * s + 16 * (v >> 3) + 8 * half + (v & 7);
@@ -434,6 +440,16 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
     }
   };
 
+  // V rows of the staged diagonal block past the sequence's end are zeroed
+  // (only the last tile's diagonal block has any; uniform).
+  auto zero_tail = [&](int j, uint8_t* vs_) {
+    if (diag_valid < B && __builtin_amdgcn_readfirstlane(blocks[j]) == own) {
+      for (int x = tid + 16 * diag_valid; x < B * 16; x += 512)
+        *reinterpret_cast<u32x4*>(vs_ + x * 16) = u32x4{0u, 0u, 0u, 0u};
+      __syncthreads();
+    }
+  };
+
   // Two blocks per trip, one per slot: block j + 1 streams into the other
   // slot while block j is computed; the barrier before each block also
   // closes every wave's reads of the slot the next load overwrites.
@@ -441,11 +457,13 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   for (int j = 0; j < nsel; j += 2) {
     wait_vmem();
     __syncthreads();
+    zero_tail(j, vslot0);
     if (j + 1 < nsel) issue(j + 1, kslot1, vslot1);
     attend(j, kslot0, vslot0);
     if (j + 1 >= nsel) break;
     wait_vmem();
     __syncthreads();
+    zero_tail(j + 1, vslot1);
     if (j + 2 < nsel) issue(j + 2, kslot0, vslot0);
     attend(j + 1, kslot1, vslot1);
   }

@@ -234,3 +234,48 @@ def test_read_stream_probe_rejects_bad_arguments(args, msg):
 def test_mfma_probe_rejects_bad_arguments(args, msg):
     assert msa.lib().msa_probe_mfma_bf16(*args, None) == INVALID
     assert msg in msa.msa_last_error()
+
+
+_NO_DEVICE_SCRIPT = r"""
+import ctypes, sys
+import block_sparse_long_10_amd as msa
+from block_sparse_long_10_amd import Params, PagedKV
+L = msa.lib()
+F = 0x10000
+p = Params(num_q_heads=64, num_kv_heads=8, head_dim=128, num_idx_heads=4, idx_dim=64,
+           block_size=128, top_k=16, softmax_scale=128 ** -0.5)
+kv = PagedKV(F, F, F, F, 100, 50)
+calls = {
+    "decode": lambda: L.msa_decode(ctypes.byref(p), ctypes.byref(kv), F, F, F, 2, 1000, F, None, F,
+                                   L.msa_decode_workspace_bytes(ctypes.byref(p), 2, 50), None),
+    "prefill": lambda: L.msa_prefill_chunk(ctypes.byref(p), ctypes.byref(kv), F, F, 1000, 100, F,
+                                           None, F,
+                                           L.msa_prefill_workspace_bytes(ctypes.byref(p), 1000,
+                                                                         100, 50), None),
+    "index": lambda: L.msa_index_score_decode(ctypes.byref(p), ctypes.byref(kv), F, F, 2, 1000,
+                                              F, None),
+}
+for name, call in calls.items():
+    st = call()
+    err = msa.msa_last_error()
+    print(name, st, err)
+    if st != -4 or not err:
+        sys.exit(1)
+"""
+
+
+def test_launching_call_without_a_device_returns_hip_error():
+    """With no GPU visible, a call that passes host validation reaches its
+    first launch, which fails: the call returns MSA_ERR_HIP with a message and
+    nothing crashes.  Run in a child process with every device hidden; skipped
+    where a GPU is visible to this process (then the fake pointers could
+    reach a real launch)."""
+    import subprocess
+    import sys
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible; the no-device path is checked on hosts without one")
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="", ROCR_VISIBLE_DEVICES="")
+    r = subprocess.run([sys.executable, "-c", _NO_DEVICE_SCRIPT], cwd=ROOT, env=env,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.count(" -4 ") == 3, r.stdout

@@ -1,17 +1,19 @@
 """MSA calls captured in one HIP graph (through torch's graph capture of the
 C ABI calls on the capture stream) and replayed: several decode layers, and a
-chunked plus a batched prefill.  Every replay, with eager work and
-synchronisations between the replays, must give the eager outputs bit for
-bit.  Marked gpu."""
+chunked plus a batched prefill.  The eager decode layers are checked against
+the oracle layer by layer; every replay, with eager work and synchronisations
+between the replays, must give the eager outputs bit for bit.  Marked gpu."""
 import sys
 
+import numpy as np
 import pytest
 import torch
 
 import block_sparse_long_10_amd as msa
-from msa_inputs import (TENSOR_IDS, Shape, make_decode_case, make_prefill_case,
-                        make_varlen_prefill_case, normal_bf16)
-from tests.gpu_util import params_of
+import oracle
+from msa_inputs import (TENSOR_IDS, DecodeCase, PagedCache, Shape, make_decode_case,
+                        make_prefill_case, make_varlen_prefill_case, normal_bf16)
+from tests.gpu_util import check_out, check_selection, params_of
 
 pytestmark = pytest.mark.gpu
 
@@ -59,6 +61,22 @@ def test_multi_layer_decode_graph_replays(append):
     torch.cuda.synchronize()
     ref_out, ref_sel = outs.clone(), sels.clone()
     assert torch.isfinite(ref_out).all()
+    # every layer of the eager run against the oracle on that layer's index
+    # keys and queries (the replays below must then equal it bit for bit)
+    for l, (ik, q, iq) in enumerate(layers):
+        one = DecodeCase(shape, PagedCache(k=c.k, v=c.v, idx_k=ik, block_table=c.block_table,
+                                           num_pages=c.num_pages, max_blocks=c.max_blocks,
+                                           lengths=list(lengths)),
+                         q, iq, case.seq_lens, list(lengths))
+        P = oracle.prepare(one)
+        ref = oracle.decode(one, prepared=P)
+        gsel = ref_sel[l].cpu().numpy()
+        for sq, L in enumerate(lengths):
+            own = (L - 1) // shape.block_size
+            for gi in range(shape.num_kv_heads):
+                check_selection(gsel[sq, gi], ref["pooled"][sq, gi], own, shape.top_k)
+        check_out(ref_out[l].cpu().numpy().astype(np.float64),
+                  oracle.attend_decode(one, gsel, prepared=P), "layer %d" % l)
 
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()

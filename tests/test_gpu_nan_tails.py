@@ -1,0 +1,125 @@
+"""GPU parity when the cache slots past a sequence's last token hold NaN or
+Inf bit patterns (bf16 0x7FC0, 0x7F80, 0xFF80), as an unwritten page slot
+may: those slots are outside the attention (their probability is zero) and
+outside the index scores (only blocks before the own block are scored), so
+outputs must stay finite and match the oracle, which never reads them.
+Covers decode, decode with the fused append, and prefill whose chunk ends
+inside a block.  Marked gpu."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_10_amd as msa
+import oracle
+from msa_inputs import Shape, make_decode_case, make_prefill_case
+from tests.gpu_util import (check_out, check_pooled, check_selection, kv_of, params_of,
+                            run_decode, run_prefill)
+
+pytestmark = pytest.mark.gpu
+
+NAN, INF, NINF = 0x7FC0, 0x7F80, -128  # bf16 bit patterns as int16 (0xFF80 = -128)
+
+
+def _announce(what):
+    print("\n[gpu nan tails] " + what, flush=True)
+    sys.stdout.flush()
+
+
+def poison_tails(case, lengths):
+    """Fill the slots past each sequence's last token (in its last page) with
+    NaN keys and values and +-Inf index keys."""
+    c, B = case.cache, case.shape.block_size
+    bt = c.block_table.cpu().numpy()
+    for s, L in enumerate(lengths):
+        tail = L % B
+        if tail == 0:
+            continue
+        page = int(bt[s, (L - 1) // B])
+        c.k.view(torch.int16)[page, :, tail:, :] = NAN
+        c.v.view(torch.int16)[page, :, tail:, :] = NAN
+        iv = c.idx_k.view(torch.int16)
+        iv[page, ..., tail:, :] = INF
+        iv[page, ..., tail + 1:, :] = NINF
+
+
+SHAPES = [
+    Shape(num_q_heads=16, num_kv_heads=2, num_idx_heads=4, block_size=128, top_k=4),
+    Shape(num_q_heads=24, num_kv_heads=3, num_idx_heads=2, block_size=64, top_k=6),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_decode_with_nan_tails(shape):
+    lengths = [3001, 130, 777, 64 * 7 + 5, 1]
+    _announce("decode %s" % (shape,))
+    case = make_decode_case(shape, lengths, 91, device="cuda", shuffle_pages=True,
+                            poison_frac=0.1)
+    poison_tails(case, lengths)
+    g = run_decode(case)
+    P = oracle.prepare(case)
+    ref = oracle.decode(case, prepared=P)
+    for s, L in enumerate(lengths):
+        own = (L - 1) // shape.block_size
+        for gi in range(shape.num_kv_heads):
+            check_pooled(g["pooled"][s, gi, :own], ref["pooled"][s, gi, :own])
+            check_selection(g["sel"][s, gi], ref["pooled"][s, gi], own, shape.top_k)
+    check_out(g["out"], oracle.attend_decode(case, g["sel"], prepared=P))
+
+
+def test_decode_append_with_nan_tails():
+    """The current token's own slot starts as NaN too; the fused append writes
+    it before the sparse branch reads it."""
+    shape = SHAPES[0]
+    lengths = [3001, 130, 777]
+    _announce("decode append")
+    case = make_decode_case(shape, lengths, 92, device="cuda", shuffle_pages=True)
+    c, B = case.cache, shape.block_size
+    pos = torch.tensor([L - 1 for L in lengths], dtype=torch.long, device="cuda")
+    rows = torch.arange(len(lengths), device="cuda")
+    pages = c.block_table.long()[rows, pos // B]
+    slots = pos % B
+    kn = c.k[pages, :, slots, :].contiguous()
+    vn = c.v[pages, :, slots, :].contiguous()
+    xn = c.idx_k[pages, slots, :].contiguous()
+    P = oracle.prepare(case)  # before the cache is punched
+    ref = oracle.decode(case, prepared=P)
+    poison_tails(case, [L - 1 for L in lengths])  # own slot and everything after it
+    p = params_of(shape)
+    kvm = msa.make_kv_mut(c.k, c.v, c.idx_k, c.block_table)
+    out = torch.full((len(lengths), shape.num_q_heads, shape.head_dim), float("nan"), device="cuda")
+    sel = torch.full((len(lengths), shape.num_kv_heads, shape.top_k), -7, dtype=torch.int32,
+                     device="cuda")
+    ws = torch.empty(msa.msa_decode_workspace_bytes(p, len(lengths), c.max_blocks),
+                     dtype=torch.uint8, device="cuda")
+    msa.msa_decode_append(p, kvm, kn, vn, xn, case.q, case.idx_q, case.seq_lens, len(lengths),
+                          max(lengths), out, sel, ws)
+    torch.cuda.synchronize()
+    gsel = sel.cpu().numpy()
+    for s, L in enumerate(lengths):
+        own = (L - 1) // B
+        for gi in range(shape.num_kv_heads):
+            check_selection(gsel[s, gi], ref["pooled"][s, gi], own, shape.top_k)
+    check_out(out.cpu().numpy().astype(np.float64), oracle.attend_decode(case, gsel, prepared=P))
+
+
+@pytest.mark.parametrize("shape,prior,chunk", [
+    (SHAPES[0], 1000, 300),   # chunk ends inside a block
+    (SHAPES[1], 130, 77),
+    (SHAPES[0], 256, 1),
+])
+def test_prefill_with_nan_tails(shape, prior, chunk):
+    _announce("prefill %s P=%d C=%d" % (shape, prior, chunk))
+    case = make_prefill_case(shape, prior, chunk, 93, device="cuda", shuffle_pages=True,
+                             poison_frac=0.1)
+    poison_tails(case, [prior + chunk])
+    g = run_prefill(case)
+    P = oracle.prepare(case)
+    ref = oracle.prefill(case, prepared=P)
+    for t in range(case.num_tiles):
+        own = prior // shape.block_size + t
+        for gi in range(shape.num_kv_heads):
+            check_pooled(g["pooled"][t, gi, :own], ref["pooled"][t, gi, :own])
+            check_selection(g["sel"][t, gi], ref["pooled"][t, gi], own, shape.top_k)
+    check_out(g["out"], oracle.attend_prefill(case, g["sel"], prepared=P))

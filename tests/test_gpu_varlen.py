@@ -80,9 +80,12 @@ def test_varlen_prefill_small(shape):
                   "sequence %d" % s)
 
 
+@pytest.mark.timeout(600)
 def test_varlen_prefill_paged_b32_equals_single_calls():
     """The 32 sequences of the paged decode workload (log-uniform lengths in
-    [4096, 524288], shuffled pages) each prefilling its last 512 tokens."""
+    [4096, 524288], shuffled pages) each prefilling its last 512 tokens: four
+    sequences against the oracle, and all 32 bit for bit against one
+    msa_prefill_chunk call per sequence."""
     lengths = log_uniform_lengths(32, 4096, 524288, 5)
     chunk = 512
     priors = [L - chunk for L in lengths]
@@ -92,6 +95,30 @@ def test_varlen_prefill_paged_b32_equals_single_calls():
     out, sel = run_varlen(case)
     p = params_of(GQA64)
     toff, qs = _tile_offsets(case), case.q_start
+    # four sequences against the oracle: the shortest, the longest and two
+    # seeded others (pooled scores via the selection rule, and every output row)
+    order = sorted(range(case.batch), key=lambda s: lengths[s])
+    rng = np.random.default_rng(77)
+    picked = sorted({order[0], order[-1]} |
+                    set(rng.choice(order[1:-1], size=2, replace=False).tolist()))
+    sel_h, out_h = sel.cpu().numpy(), out.cpu().numpy().astype(np.float64)
+    B = GQA64.block_size
+    for s in picked:
+        one = case.sequence(s)
+        P = oracle.prepare(one, kv_pages=[])
+        ref = oracle.prefill(one, prepared=P)
+        nt = one.num_tiles
+        my_sel = sel_h[toff[s]:toff[s] + nt]
+        bt = one.cache.block_table.cpu().numpy()
+        for t in range(nt):
+            own = one.prior_len // B + t
+            for gi in range(GQA64.num_kv_heads):
+                check_selection(my_sel[t, gi], ref["pooled"][t, gi], own, GQA64.top_k)
+        P.fill_pages(one, {int(bt[0, b]) for b in my_sel.reshape(-1) if b >= 0})
+        worst = check_out(out_h[qs[s]:qs[s] + chunk],
+                          oracle.attend_prefill(one, my_sel, prepared=P), "sequence %d" % s)
+        print("sequence %d (L=%d) against the oracle: worst row err %.3g" % (s, lengths[s], worst),
+              flush=True)
     for s in range(case.batch):
         one = case.sequence(s)
         kv = msa.make_kv(one.cache.k, one.cache.v, one.cache.idx_k, one.cache.block_table)
