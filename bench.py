@@ -123,7 +123,7 @@ def run_decode_bench(args, torch, msa, mi, gu):
     batch, maxL, mb = base.batch, max(base.lengths), base.cache.max_blocks
     out = torch.empty(batch, sh.num_q_heads, sh.head_dim, device="cuda")
     sel = torch.empty(batch, sh.num_kv_heads, sh.top_k, dtype=torch.int32, device="cuda")
-    ws = torch.empty(msa.msa_decode_workspace_bytes(p, batch, mb), dtype=torch.uint8,
+    ws = torch.zeros(msa.msa_decode_workspace_bytes(p, batch, mb), dtype=torch.uint8,
                      device="cuda")
     pooled = torch.empty(batch, sh.num_kv_heads, mb, device="cuda")
 
@@ -206,7 +206,7 @@ def run_other_decode_bench(args, torch, msa, mi, gu):
         batch, maxL, mb = base.batch, max(base.lengths), base.cache.max_blocks
         out = torch.empty(batch, sh.num_q_heads, sh.head_dim, device="cuda")
         sel = torch.empty(batch, sh.num_kv_heads, sh.top_k, dtype=torch.int32, device="cuda")
-        ws = torch.empty(msa.msa_decode_workspace_bytes(p, batch, mb), dtype=torch.uint8,
+        ws = torch.zeros(msa.msa_decode_workspace_bytes(p, batch, mb), dtype=torch.uint8,
                          device="cuda")
 
         calls = [0]
@@ -263,7 +263,7 @@ def run_layers_bench(args, torch, msa, mi, dec):
         layers.append((msa.make_kv(c.k, c.v, ik, c.block_table), q, iq))
     batch, maxL, mb = base.batch, max(base.lengths), c.max_blocks
     outs = torch.empty(n, batch, sh.num_q_heads, sh.head_dim, device="cuda")
-    ws = torch.empty(msa.msa_decode_workspace_bytes(p, batch, mb), dtype=torch.uint8,
+    ws = torch.zeros(msa.msa_decode_workspace_bytes(p, batch, mb), dtype=torch.uint8,
                      device="cuda")
 
     def token():
@@ -441,7 +441,7 @@ def run_group_keys_bench(args, torch, msa, mi, gu):
     p = gu.params_of(sh)
     batch, maxL, mb = base.batch, max(base.lengths), c.max_blocks
     out = torch.empty(batch, sh.num_q_heads, sh.head_dim, device="cuda")
-    ws = torch.empty(msa.msa_decode_workspace_bytes(p, batch, mb), dtype=torch.uint8,
+    ws = torch.zeros(msa.msa_decode_workspace_bytes(p, batch, mb), dtype=torch.uint8,
                      device="cuda")
     pooled = torch.empty(batch, sh.num_kv_heads, mb, device="cuda")
 

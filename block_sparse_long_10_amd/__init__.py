@@ -148,7 +148,7 @@ def make_params(num_q_heads: int, num_kv_heads: int, head_dim: int = 128, num_id
 
 def make_kv(k: torch.Tensor, v: torch.Tensor, idx_k: torch.Tensor,
             block_table: torch.Tensor) -> PagedKV:
-    """Paged cache descriptor: k [P][Hkv][B][D], v [P][Hkv][D][B], idx_k [P][B][d_i] or
+    """Paged cache descriptor: k [P][Hkv][B][D], v [P][Hkv][B][D], idx_k [P][B][d_i] or
     [P][Hkv][B][d_i] (bf16), block_table int32 [batch][max_blocks]."""
     kv = PagedKV(_dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
                  _dev(idx_k, torch.bfloat16, "idx_k"), _dev(block_table, torch.int32, "block_table"),

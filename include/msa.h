@@ -57,7 +57,7 @@
  * Paged KV cache (one page holds one KV block of block_size tokens)
  * -----------------------------------------------------------------
  *   k      bf16 [num_pages][Hkv][B][D]   keys, token-major within a page
- *   v      bf16 [num_pages][Hkv][D][B]   values, transposed within a page
+ *   v      bf16 [num_pages][Hkv][B][D]   values, token-major within a page
  *   idx_k  bf16 [num_pages][B][d_i]      the single shared index-key head
  *          ([num_pages][Hkv][B][d_i] with per-group index keys)
  *   block_table int32 [batch][max_blocks_per_seq]: logical block b of
@@ -102,7 +102,7 @@ typedef struct {
 
 typedef struct {
   const void *k;              /* bf16 [num_pages][Hkv][B][D]  */
-  const void *v;              /* bf16 [num_pages][Hkv][D][B]  */
+  const void *v;              /* bf16 [num_pages][Hkv][B][D]  */
   const void *idx_k;          /* bf16 [num_pages][B][d_i]     */
   const int32_t *block_table; /* int32 [batch][max_blocks_per_seq] */
   int32_t num_pages;
@@ -113,7 +113,7 @@ typedef struct {
  * and meaning as in msa_paged_kv. */
 typedef struct {
   void *k;                    /* bf16 [num_pages][Hkv][B][D]  */
-  void *v;                    /* bf16 [num_pages][Hkv][D][B]  */
+  void *v;                    /* bf16 [num_pages][Hkv][B][D]  */
   void *idx_k;                /* bf16 [num_pages][B][d_i]     */
   const int32_t *block_table; /* int32 [batch][max_blocks_per_seq] */
   int32_t num_pages;
@@ -127,10 +127,9 @@ typedef struct {
  * section 2: the real, uncompressed K/V stay in the cache).
  * Sequence s receives n_new >= 1 consecutive tokens at positions
  * start_pos[s] .. start_pos[s]+n_new-1 (token t goes to page
- * block_table[s][t/B], slot t%B; the V slot is column t%B of the page's
- * transposed [D][B] rows).
+ * block_table[s][t/B], slot t%B, row t%B of the page's K and V).
  *   k_new     bf16 [batch][n_new][Hkv][D]
- *   v_new     bf16 [batch][n_new][Hkv][D]   (token-major; transposed here)
+ *   v_new     bf16 [batch][n_new][Hkv][D]
  *   idx_k_new bf16 [batch][n_new][d_i]
  *   start_pos int32 [batch]  (device)
  * Only the slots of the new tokens are written.  Pages written for one
@@ -154,7 +153,8 @@ msa_status msa_cache_append(const msa_params *params, const msa_paged_kv_mut *kv
  *   sel      int32 [batch][Hkv][top_k] or NULL: kept blocks, ascending,
  *            padded with -1
  *   workspace  device memory of at least msa_decode_workspace_bytes(); its
- *              contents on entry do not matter.
+ *              contents on entry do not matter.  Calls that overlap in time
+ *              must not share a workspace.
  */
 size_t msa_decode_workspace_bytes(const msa_params *params, int32_t batch,
                                   int32_t max_blocks_per_seq);

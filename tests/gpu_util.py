@@ -37,14 +37,16 @@ def kv_of(case):
     return msa.make_kv(c.k, c.v, c.idx_k, c.block_table)
 
 
-def run_decode(case, with_pooled=True):
+def run_decode(case, with_pooled=True, ws=None):
     sh = case.shape
     p, kv = params_of(sh), kv_of(case)
     dev = case.q.device
     batch, maxL, mb = case.batch, max(case.lengths), case.cache.max_blocks
     out = torch.full((batch, sh.num_q_heads, sh.head_dim), float("nan"), device=dev)
     sel = torch.full((batch, sh.num_kv_heads, sh.top_k), -7, dtype=torch.int32, device=dev)
-    ws = torch.empty(msa.msa_decode_workspace_bytes(p, batch, mb), dtype=torch.uint8, device=dev)
+    if ws is None:  # zero-filled: the selection reads the chunk maxima
+        ws = torch.zeros(msa.msa_decode_workspace_bytes(p, batch, mb), dtype=torch.uint8,
+                         device=dev)
     msa.msa_decode(p, kv, case.q, case.idx_q, case.seq_lens, batch, maxL, out, sel, ws)
     res = {}
     if with_pooled:

@@ -77,7 +77,7 @@ def _decode_append_matches(case, check_oracle):
     batch, maxL, mb = case.batch, max(case.lengths), case.cache.max_blocks
     out = torch.full((batch, sh.num_q_heads, sh.head_dim), float("nan"), device=DEV)
     sel = torch.full((batch, sh.num_kv_heads, sh.top_k), -7, dtype=torch.int32, device=DEV)
-    ws = torch.empty(msa.msa_decode_workspace_bytes(p, batch, mb), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(msa.msa_decode_workspace_bytes(p, batch, mb), dtype=torch.uint8, device=DEV)
     msa.msa_decode_append(p, kv, kn, vn, xn, case.q, case.idx_q, case.seq_lens, batch, maxL, out,
                           sel, ws)
     torch.cuda.synchronize()

@@ -6,9 +6,10 @@ import numpy as np
 import pytest
 import torch
 
+import block_sparse_long_10_amd as msa
 import oracle
 from msa_inputs import Shape, GQA64, make_decode_case, make_workload
-from tests.gpu_util import (check_out, check_pooled, check_selection, run_decode)
+from tests.gpu_util import (check_out, check_pooled, check_selection, params_of, run_decode)
 
 pytestmark = pytest.mark.gpu
 
@@ -178,3 +179,28 @@ def test_decode_deterministic():
     b = run_decode(case, with_pooled=False)
     np.testing.assert_array_equal(a["sel"], b["sel"])
     assert np.array_equal(a["out"], b["out"])
+
+
+@pytest.mark.parametrize("fill", ["zeros", "ones", "random"])
+def test_decode_workspace_contents_do_not_change_results(fill):
+    """The workspace's contents on entry do not matter: zero bytes, 0xFF bytes
+    and random bytes give the same selection and bit-identical outputs, on two
+    calls in a row.  Covers the fused TopK (batch 2) and the separate TopK
+    launch (batch 9: more than 1024 slot workgroups)."""
+    _announce("workspace contents: %s" % fill)
+    for lengths, seed in [([70000, 131072], 108), ([9000 + 4000 * i for i in range(9)], 109)]:
+        case = make_decode_case(GQA64, lengths, seed, device=DEV, shuffle_pages=True)
+        ref = run_decode(case, with_pooled=False)
+        p = params_of(GQA64)
+        ws = torch.empty(msa.msa_decode_workspace_bytes(p, case.batch, case.cache.max_blocks),
+                         dtype=torch.uint8, device=DEV)
+        if fill == "zeros":
+            ws.zero_()
+        elif fill == "ones":
+            ws.fill_(255)
+        else:
+            ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device=DEV))
+        for rep in range(2):
+            got = run_decode(case, with_pooled=False, ws=ws)
+            np.testing.assert_array_equal(got["sel"], ref["sel"])
+            assert np.array_equal(got["out"], ref["out"]), (fill, rep)

@@ -43,7 +43,7 @@ def test_multi_layer_decode_graph_replays(append):
     outs = torch.empty(n_layers, batch, shape.num_q_heads, shape.head_dim, device="cuda")
     sels = torch.empty(n_layers, batch, shape.num_kv_heads, shape.top_k, dtype=torch.int32,
                        device="cuda")
-    ws = torch.empty(msa.msa_decode_workspace_bytes(p, batch, mb), dtype=torch.uint8,
+    ws = torch.zeros(msa.msa_decode_workspace_bytes(p, batch, mb), dtype=torch.uint8,
                      device="cuda")
 
     def token():

@@ -91,7 +91,7 @@ def test_decode_append_with_nan_tails():
     out = torch.full((len(lengths), shape.num_q_heads, shape.head_dim), float("nan"), device="cuda")
     sel = torch.full((len(lengths), shape.num_kv_heads, shape.top_k), -7, dtype=torch.int32,
                      device="cuda")
-    ws = torch.empty(msa.msa_decode_workspace_bytes(p, len(lengths), c.max_blocks),
+    ws = torch.zeros(msa.msa_decode_workspace_bytes(p, len(lengths), c.max_blocks),
                      dtype=torch.uint8, device="cuda")
     msa.msa_decode_append(p, kvm, kn, vn, xn, case.q, case.idx_q, case.seq_lens, len(lengths),
                           max(lengths), out, sel, ws)
