@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "MSAError", "Params", "PagedKV", "make_params", "make_kv", "library_path",
-    "msa_decode_workspace_bytes", "msa_decode", "msa_index_score_decode",
+    "msa_decode_workspace_bytes", "msa_decode", "msa_decode_noalloc", "msa_index_score_decode",
     "msa_prefill_workspace_bytes", "msa_prefill_chunk", "msa_index_score_prefill",
     "msa_block_topk_prefill", "msa_sparse_attn_prefill", "msa_last_error", "msa_version",
     "PagedKVMut", "make_kv_mut", "msa_cache_append", "msa_decode_append",
@@ -81,6 +81,7 @@ def lib():
         sigs = {
             "msa_decode_workspace_bytes": (sz, [P, i32, i32]),
             "msa_decode": (ctypes.c_int, [P, K, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]),
+            "msa_decode_noalloc": (ctypes.c_int, [P, K, vp, vp, vp, i32, i32, vp, vp, vp]),
             "msa_index_score_decode": (ctypes.c_int, [P, K, vp, vp, i32, i32, vp, vp]),
             "msa_prefill_workspace_bytes": (sz, [P, i32, i32, i32]),
             "msa_prefill_chunk": (ctypes.c_int, [P, K, vp, vp, i32, i32, vp, vp, vp, sz, vp]),
@@ -204,6 +205,16 @@ def msa_decode(params: Params, kv: PagedKV, q, idx_q, seq_lens, batch: int, max_
                             _dev(seq_lens, torch.int32, "seq_lens"), batch, max_seq_len,
                             _dev(out, torch.float32, "out"), _dev(sel, torch.int32, "sel"),
                             _dev(workspace, None, "workspace"), ws_bytes, _stream(stream)))
+
+
+def msa_decode_noalloc(params: Params, kv: PagedKV, q, idx_q, seq_lens, batch: int,
+                       max_seq_len: int, out, sel=None, stream=None) -> None:
+    _check(lib().msa_decode_noalloc(ctypes.byref(params), ctypes.byref(kv),
+                                    _dev(q, torch.bfloat16, "q"),
+                                    _dev(idx_q, torch.bfloat16, "idx_q"),
+                                    _dev(seq_lens, torch.int32, "seq_lens"), batch, max_seq_len,
+                                    _dev(out, torch.float32, "out"),
+                                    _dev(sel, torch.int32, "sel"), _stream(stream)))
 
 
 def msa_index_score_decode(params: Params, kv: PagedKV, idx_q, seq_lens, batch: int,

@@ -16,6 +16,7 @@
 #include "msa.h"
 #include "msa_launch.h"
 #include "msa_probes.h"
+#include "msa_api_internal.h"
 
 namespace {
 
@@ -224,6 +225,10 @@ msa_status check_prefill_sizes(const msa_params* p, const msa_paged_kv* kv, int3
 
 }  // namespace
 
+namespace msa {
+msa_status set_error(msa_status st, const char* msg) { return fail(st, msg); }
+}  // namespace msa
+
 extern "C" {
 
 const char* msa_last_error(void) { return g_last_error; }
@@ -286,11 +291,7 @@ msa_status msa_cache_append(const msa_params* params, const msa_paged_kv_mut* kv
   }
 }
 
-static msa_status decode_impl(const msa_params* params, const msa_paged_kv* kv, const void* q,
-                              const void* idx_q, const int32_t* seq_lens, int32_t batch,
-                              int32_t max_seq_len, float* out, int32_t* sel, void* workspace,
-                              size_t workspace_bytes, void* stream,
-                              const msa::DecodeAppend* append);
+using msa::decode_impl;
 
 msa_status msa_decode(const msa_params* params, const msa_paged_kv* kv, const void* q,
                       const void* idx_q, const int32_t* seq_lens, int32_t batch,
@@ -325,11 +326,14 @@ msa_status msa_decode_append(const msa_params* params, const msa_paged_kv_mut* k
   }
 }
 
-static msa_status decode_impl(const msa_params* params, const msa_paged_kv* kv, const void* q,
-                              const void* idx_q, const int32_t* seq_lens, int32_t batch,
-                              int32_t max_seq_len, float* out, int32_t* sel, void* workspace,
-                              size_t workspace_bytes, void* stream,
-                              const msa::DecodeAppend* append) {
+}  // extern "C"
+
+// (shared with the allocation-free entry point, msa_decode_noalloc)
+msa_status msa::decode_impl(const msa_params* params, const msa_paged_kv* kv, const void* q,
+                            const void* idx_q, const int32_t* seq_lens, int32_t batch,
+                            int32_t max_seq_len, float* out, int32_t* sel, void* workspace,
+                            size_t workspace_bytes, void* stream,
+                            const msa::DecodeAppend* append) {
   msa_status st = check_params(params);
   if (st != MSA_OK) return st;
   if ((st = check_kv(kv)) != MSA_OK) return st;
@@ -360,6 +364,8 @@ static msa_status decode_impl(const msa_params* params, const msa_paged_kv* kv, 
                               sel != nullptr ? sel : reinterpret_cast<int32_t*>(ws + w.sel), out, s),
       "sparse attention launch");
 }
+
+extern "C" {
 
 size_t msa_prefill_workspace_bytes(const msa_params* params, int32_t prior_len, int32_t chunk_len,
                                    int32_t max_blocks_per_seq) {

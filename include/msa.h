@@ -181,6 +181,22 @@ msa_status msa_decode_append(const msa_params *params, const msa_paged_kv_mut *k
                              int32_t *sel, void *workspace,
                              size_t workspace_bytes, void *stream);
 
+/* msa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments and results as msa_decode, without the workspace: the kernels'
+ * scratch is a static 32 MiB array of the library, one per GPU, held until
+ * the process ends (its device address is looked up on the first call on
+ * each device).  A call whose msa_decode_workspace_bytes() would exceed
+ * 32 MiB returns MSA_ERR_WORKSPACE (at 64/8 heads and top_k 16 the 1M-token
+ * single-sequence decode needs 0.8 MiB, 32 sequences of up to 512K tokens
+ * 20.5 MiB).  Calls on one GPU share the array: calls that overlap in time
+ * on one GPU race. */
+msa_status msa_decode_noalloc(const msa_params *params, const msa_paged_kv *kv,
+                              const void *q, const void *idx_q,
+                              const int32_t *seq_lens, int32_t batch,
+                              int32_t max_seq_len, float *out, int32_t *sel,
+                              void *stream);
+
 /* Step 1 of decode alone (index scores + block max pool):
  *   pooled f32 [batch][Hkv][max_blocks_per_seq]; entries b < c are written,
  *   the others are left untouched. */
