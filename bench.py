@@ -223,6 +223,8 @@ def run_other_decode_bench(args, torch, msa, mi, gu):
         res[name] = {"batch": batch, "context_tokens": int(sum(base.lengths)),
                      "us_per_step": round(ms * 1e3, 3), "algorithmic_bytes": total,
                      "gbps": round(total / (ms * 1e-3) / 1e9, 1), "rotated_buffer_sets": rot}
+        if args.cpu_budget > 0:
+            res[name]["cpu_baseline"] = cpu_baseline(base, max(2.0, args.cpu_budget / 4), name)
         del sets, kvs, base, out, sel, ws
         torch.cuda.empty_cache()
     return res
@@ -325,6 +327,20 @@ def prefill_algorithmic_flops(sh, P, C):
     return pairs * rows * sh.idx_dim * 2, attn_pairs * sh.num_q_heads * sh.head_dim * 4
 
 
+def prefill_padded_attn_flops(sh, P, C):
+    """Attention flops counted per whole block: every query over its kept
+    blocks and its whole diagonal block (the block-granular work, against the
+    exact-causal count above)."""
+    B = sh.block_size
+    nt = (P + C + B - 1) // B - P // B
+    pairs = 0
+    for t in range(nt):
+        own = P // B + t
+        q0, q1 = max(0, own * B - P), min(C, (own + 1) * B - P)
+        pairs += (q1 - q0) * (min(sh.top_k - 1, own) + 1) * B
+    return pairs * sh.num_q_heads * sh.head_dim * 4
+
+
 def run_prefill_bench(args, torch, msa, mi, gu):
     log("[bench] generating %s" % PREFILL_WORKLOAD)
     case = mi.make_workload(PREFILL_WORKLOAD, "cuda")
@@ -369,8 +385,10 @@ def run_prefill_bench(args, torch, msa, mi, gu):
     ms_append = timed(lambda: msa.msa_cache_append(p, kvm, k_new, v_new, x_new, start, 1, C), n, w)
     append_bytes = 2 * C * (2 * sh.num_kv_heads * sh.head_dim * 2 + sh.idx_dim * 2)
     index_flops, attn_flops = prefill_algorithmic_flops(sh, P, C)
+    attn_flops_padded = prefill_padded_attn_flops(sh, P, C)
     return {"case": case, "ms_chunk": ms_chunk, "ms_index": ms_index, "ms_topk": ms_topk,
             "ms_attn": ms_attn, "index_flops": index_flops, "attn_flops": attn_flops,
+            "attn_flops_padded": attn_flops_padded,
             "ms_append": ms_append, "append_bytes": append_bytes}
 
 
@@ -562,13 +580,28 @@ def practical_peaks(torch):
             "note": "torch device copy (read + write bytes) and torch.matmul 8192^3 bf16"}
 
 
-def cpu_baseline(case, budget_s):
+def cpu_model():
+    """The host CPU's model name and logical core count."""
+    name = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return "%s (%d logical cores on the host)" % (name, os.cpu_count() or 0)
+
+
+def cpu_baseline(case, budget_s, workload=None):
     """The oracle on the host cores: whole decode steps of the same workload
     (index scores of every block, TopK, attention), repeated for about
     budget_s seconds; K/V pages are copied to the host for the kept blocks."""
     import oracle
     oracle.build()
-    log("[bench] cpu baseline: oracle decode on the host")
+    workload = workload or DECODE_WORKLOAD
+    log("[bench] cpu baseline: oracle decode of %s on the host" % workload)
     P = oracle.prepare(case, kv_pages=[])
     first = oracle.decode(case, prepared=P)
     bt = case.cache.block_table.cpu().numpy()
@@ -586,29 +619,26 @@ def cpu_baseline(case, budget_s):
     times.sort()
     med = times[len(times) // 2]
     return {"value": med * 1e6, "unit": "us/step", "cores": oracle.max_threads(),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": "%d full decode steps of %s (median), fp64 C oracle with OpenMP"
-                      % (len(times), DECODE_WORKLOAD)}
+                      % (len(times), workload)}
 
 
 def cpu_prefill_baseline(case, budget_s):
     """The oracle's prefill on the host cores, on a bounded sample of the same
     chunk: whole tiles (index scores of every eligible block, TopK, attention
     of the tile's queries), the first and the last tile, then more tiles while
-    the budget lasts; K/V are copied for the kept pages only.  Reported as
-    chunk tokens per second extrapolated from the sampled tiles to all of
-    them (an extrapolation)."""
+    the budget lasts, each computed once; the whole K/V cache is copied to the
+    host first.  Reported as chunk tokens per second extrapolated from the
+    sampled tiles to all of them (an extrapolation)."""
     import oracle
     oracle.build()
     log("[bench] cpu baseline: oracle prefill tiles on the host")
     nt = case.num_tiles
     order = [0, nt - 1] + list(range(1, nt - 1))
-    P = oracle.prepare(case, kv_pages=[])
-    bt = case.cache.block_table.cpu().numpy()
+    P = oracle.prepare(case)
     done, spent = [], 0.0
     for t in order:
-        first = oracle.prefill(case, tiles=[t], prepared=P, want_pooled=False)
-        P.fill_pages(case, {int(bt[0, b]) for b in first["sel"][t].ravel() if b >= 0})
         t0 = time.time()
         oracle.prefill(case, tiles=[t], prepared=P, want_pooled=False)
         spent += time.time() - t0
@@ -616,10 +646,12 @@ def cpu_prefill_baseline(case, budget_s):
         if len(done) >= 2 and spent >= budget_s:
             break
     per_tile = spent / len(done)
+    del P
     return {"value": case.chunk_len / (per_tile * nt), "unit": "tokens/s",
-            "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": "%d of %d tiles of %s (%.1f s per tile), extrapolated to the whole "
-                      "chunk: an extrapolation" % (len(done), nt, PREFILL_WORKLOAD, per_tile)}
+            "cores": oracle.max_threads(), "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": "%d of %d tiles of %s (%.1f s per tile, each computed once), "
+                      "extrapolated to the whole chunk: an extrapolation"
+                      % (len(done), nt, PREFILL_WORKLOAD, per_tile)}
 
 
 COPY_PROBE_BYTES = 128 << 20
@@ -952,6 +984,9 @@ def main():
             "attn_mfma_frac": round(pre["attn_flops"] / (pre["ms_attn"] * 1e-3) / 1e12
                                     / BF16_PEAK_TFLOPS, 4),
             "index_flops": pre["index_flops"], "attn_flops": pre["attn_flops"],
+            "attn_flops_padded": pre["attn_flops_padded"],
+            "attn_mfma_frac_padded": round(pre["attn_flops_padded"] / (pre["ms_attn"] * 1e-3)
+                                           / 1e12 / BF16_PEAK_TFLOPS, 4),
             "peak_tflops": BF16_PEAK_TFLOPS,
             "practical_peak_tflops": roofs["mfma_bf16_tflops"],
             "index_frac_of_practical": round(pre["index_flops"] / (pre["ms_index"] * 1e-3) / 1e12

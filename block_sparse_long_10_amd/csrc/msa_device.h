@@ -18,6 +18,17 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+// LDS (address space 3) pointers, for addresses formed from byte offsets
+typedef __attribute__((address_space(3))) const uint8_t* lds_u8;
+typedef __attribute__((address_space(3))) const u32x4* lds_u32x4;
+
+// v_mfma_f32_32x32x16_f16: the same lane layout as the bf16 form below.
+__device__ __forceinline__ f32x16 mfma32_f16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 // v_mfma_f32_32x32x16_bf16: lane l holds A[l%32][8*(l/32)+j], B[8*(l/32)+j][l%32]
 // and D[8*(v/4)+4*(l/32)+v%4][l%32] (v = 0..15).
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -55,6 +66,9 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 __device__ __forceinline__ i16x4 lds_read_tr16(const void* lds_byte_addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_i16x4*)(__attribute__((address_space(3))) void*)(lds_byte_addr));
+}
+__device__ __forceinline__ i16x4 lds_read_tr16_l(lds_u8 p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
 }
 // Two transpose reads (rows r0..r0+3, then r0+4..r0+7) as one 8-element operand.
 __device__ __forceinline__ bf16x8 join_tr(i16x4 a, i16x4 b) {

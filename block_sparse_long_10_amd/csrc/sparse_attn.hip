@@ -8,8 +8,9 @@
 // O^T = V^T P^T.  K and V pages are token-major ([B][D] per page and head); V
 // is staged in LDS and V^T, whose MFMA operand holds 8 consecutive tokens of
 // one dimension, is formed by LDS transpose reads (ds_read_b64_tr_b16).
-// Probabilities enter the bf16 PV contraction as hi + lo bf16 parts
-// (P - hi - lo < 2^-16 P), so the only rounding left is fp32 accumulation.
+// In decode, probabilities enter the bf16 PV contraction as hi + lo bf16
+// parts (P - hi - lo < 2^-16 P), so the only rounding left is fp32
+// accumulation; prefill uses half precision (below).
 //
 // Decode: one launch after the index scores (two for large batches).  One
 // workgroup per (sequence, group, kept-block slot) derives the group's
@@ -24,7 +25,21 @@
 // (K and V token-major, XOR-swizzled 16-byte chunks) and
 // consumed 32 keys at a time with v_mfma_f32_32x32x16_bf16 and an online
 // softmax; the causal mask applies inside the tile's diagonal block only.
+// The PV product runs in IEEE half when the staged V block allows it: V is
+// converted in LDS (exact for magnitudes in [2^-14, 65504]; the block is
+// taken when its largest magnitude lies in [2^-8, 2^15]) and P is rounded to
+// nearest-even half (11 significant bits), the row sums adding the rounded
+// values; on the 1M prefill attention shape the worst row error of half P is
+// 4.8e-4 in the oracle, against 3.6e-3 for bf16 P.  One MFMA per product
+// instead of the hi + lo pair.  Outside the diagonal block the 32-key steps
+// are software-pipelined: the scores of step s + 1 go to the matrix cores
+// before the probabilities of step s are formed.  A workgroup that meets a
+// block outside the half range stops, marks its first output row (a NaN in
+// its first element) and a second launch of the same kernel, with the bf16
+// hi + lo form throughout, redoes exactly the marked workgroups (the others
+// exit after one load).
 #include <algorithm>
+#include <type_traits>
 
 #include "block_topk.h"
 #include "chunk_map.h"
@@ -208,7 +223,7 @@ __device__ __forceinline__ float truncated_rest(float a) {
 }
 
 
-template <int B>
+template <int B, bool HALF>
 __global__ __launch_bounds__(512) void prefill_attn_kernel(
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ block_table, const uint16_t* __restrict__ q,
@@ -225,7 +240,14 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t kslot1[KBYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t vslot0[VBYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t vslot1[VBYTES];
-  __shared__ int32_t pages[64], blocks[64];
+  // (the small arrays first in LDS, at addresses an instruction offset reaches)
+  __shared__ __attribute__((aligned(2048))) struct {
+    int32_t pages[64], blocks[64];
+    uint32_t vmax_w[kPrefillWaves];
+  } sm;
+  int32_t* const pages = sm.pages;
+  int32_t* const blocks = sm.blocks;
+  uint32_t* const vmax_w = sm.vmax_w;
 
   // workgroup -> (unit, row group); unit = tile * Hkv + g
   const int wg = blockIdx.x;
@@ -233,7 +255,8 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   const int z = (wg >> 3) % zr;
   if (unit >= num_units) return;
   const int tile = unit / num_kv_heads, g = unit % num_kv_heads;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // (uniform: scalar)
   const TileLoc loc = locate_tile(map, tile);
   const int prior_len = loc.prior;
   const int own = prior_len / B + loc.tile;
@@ -244,6 +267,13 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   const int row0 = z * kPrefillRows;
   if (row0 >= nrows) return;
   const int Hq = num_kv_heads * group;
+  // the first element of the workgroup's first output row: the mark of a
+  // workgroup the half-precision launch left to the bf16 one
+  float* const mark =
+      out + ((size_t)(loc.q0 + q0 + row0 % nq) * Hq + (size_t)g * group + row0 / nq) * 128;
+  if constexpr (!HALF) {
+    if (!__builtin_isnan(*mark)) return;  // (uniform) done by the half-precision launch
+  }
 
   const int32_t* srow = sel + (size_t)unit * top_k;
   int blk_t = -1;
@@ -366,6 +396,30 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
         o[mt] = mfma32(vf[s2][mt], plo[s2], o[mt]);
       }
   };
+  // The same in half precision: P rounded to nearest-even half, one product;
+  // the row sum adds the rounded values (v_dot2 with ones), so that numerator
+  // and denominator weigh each key alike.
+  auto probabilities_h = [&](const f32x16& acc, f16x8* ph) {
+    const half2 ones = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      half2 h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = __builtin_amdgcn_exp2f(fmaf(acc[8 * s2 + 2 * e], scale_log2, -m_run));
+        const float b = __builtin_amdgcn_exp2f(fmaf(acc[8 * s2 + 2 * e + 1], scale_log2, -m_run));
+        h[e] = half2{(_Float16)a, (_Float16)b};
+        l_run = __builtin_amdgcn_fdot2(h[e], ones, l_run, false);
+      }
+      ph[s2] = f16x8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+    }
+  };
+  auto accumulate_pv_h = [&](const f16x8 (&vf)[2][4], const f16x8* ph) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) o[mt] = mfma32_f16(vf[s2][mt], ph[s2], o[mt]);
+  };
 
   // LDS byte addresses of this lane's operand rows.  K: chunk ks of key
   // 32 s + kmap(m) sits at s*8192 + (k_lane ^ 32 ks).  V (16-byte chunk c of
@@ -382,7 +436,10 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
                                      32 * (h4 & 1) + 8 * (u16 & 3));
 
   // attention of the wave's rows over kept block j, staged in ks_ and vs_
-  auto attend = [&](int j, const uint8_t* ks_, const uint8_t* vs_) {
+  // (V in half precision when VHALF; two copies of the step loop, so that each
+  // keeps its own registers)
+  auto attend = [&](int j, const uint8_t* ks_, const uint8_t* vs_, auto vhalf_tag) {
+    constexpr bool VHALF = decltype(vhalf_tag)::value;
     // (per-step addresses start from opaque copies of the lane offsets, so
     // that the compiler does not hold every step's addresses across the loop)
     auto load_k = [&](int s, bf16x8* kf) {
@@ -427,17 +484,183 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
       bf16x8 vf[2][4];
       load_v(s, vf);
       if (diag && key0 + 32 * s + 31 > pos_min) {
+        // value v holds key key0 + 32 s + 16 (v / 8) + 8 half + v % 8
+        int lim = pos - key0 - 32 * s - 8 * half;
+        asm volatile("" : "+v"(lim));  // (nothing of this hoisted out of the block loop)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int kk = 32 * s + 16 * (v >> 3) + 8 * half + (v & 7);
-          if (key0 + kk > pos) acc[v] = -INFINITY;
-        }
+        for (int v = 0; v < 16; ++v)
+          if (16 * (v >> 3) + (v & 7) > lim) acc[v] = -INFINITY;
       }
       raise_max(tile_max(acc));
-      bf16x8 phi[2], plo[2];
-      probabilities(acc, phi, plo);
-      accumulate_pv(vf, phi, plo);
+      if constexpr (VHALF) {
+        f16x8 vh[2][4], ph[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) vh[s2][mt] = __builtin_bit_cast(f16x8, vf[s2][mt]);
+        probabilities_h(acc, ph);
+        accumulate_pv_h(vh, ph);
+      } else {
+        bf16x8 phi[2], plo[2];
+        probabilities(acc, phi, plo);
+        accumulate_pv(vf, phi, plo);
+      }
     }
+  };
+
+  // Attention of the wave's rows over a staged non-diagonal block in half
+  // precision, software-pipelined: the scores of step s + 1 are issued before
+  // the probabilities of step s are formed, so that the matrix cores work on
+  // them while the vector unit computes exponentials.  Lane addresses are
+  // formed once per block (LDS byte addresses, opaque to the compiler, with
+  // every step's displacement an instruction offset).
+  auto attend_pipe = [&](const uint8_t* ks_, const uint8_t* vs_) {
+    // (from opaque copies of the lane offsets, so that nothing is hoisted
+    // out of the block loop to stay live across it)
+    uint32_t kl = k_lane, vl = v_lane;
+    asm volatile("" : "+v"(kl), "+v"(vl));
+    auto load_k = [&](int s, bf16x8* kf) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        kf[ks] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(ks_ + (kl ^ (uint32_t)(ks << 5)) + s * 8192));
+    };
+    // V^T operands of keys 32 s + 16 s2 .. +15 (all four dimension tiles)
+    auto load_v = [&](int s, int s2, f16x8* vf) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const uint8_t* a = vs_ + (vl ^ (uint32_t)(64 * mt)) + (32 * s + 16 * s2) * 256;
+        vf[mt] = __builtin_bit_cast(f16x8, join_tr(lds_read_tr16(a), lds_read_tr16(a + 1024)));
+      }
+    };
+    auto scores = [&](const bf16x8* kf) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) acc = mfma32(kf[ks], qf[ks], acc);
+      return acc;
+    };
+    // half-precision P of keys 32 s + 16 s2 .. +15 (values 8 s2 .. 8 s2 + 7
+    // of the score tile), added to the row sum as rounded
+    auto probs = [&](const f32x16& acc, int s2) {
+      const half2 ones = {(_Float16)1.f, (_Float16)1.f};
+      half2 h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = __builtin_amdgcn_exp2f(fmaf(acc[8 * s2 + 2 * e], scale_log2, -m_run));
+        const float b = __builtin_amdgcn_exp2f(fmaf(acc[8 * s2 + 2 * e + 1], scale_log2, -m_run));
+        h[e] = half2{(_Float16)a, (_Float16)b};
+        l_run = __builtin_amdgcn_fdot2(h[e], ones, l_run, false);
+      }
+      return f16x8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+    };
+    auto pv = [&](const f16x8* vf, f16x8 ph) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) o[mt] = mfma32_f16(vf[mt], ph, o[mt]);
+    };
+    bf16x8 kf[8];
+    load_k(0, kf);
+    f32x16 acc = scores(kf);
+    load_k(1, kf);
+    raise_max(tile_max(acc));
+    // Each step below is one scheduling region (the rescale branch closes
+    // it), laid out in three phases fenced from each other, each spreading
+    // one kind of work between the matrix products of another:
+    //   1. scores of step s + 1 (8 products) | P of keys 0..15 of step s,
+    //      V^T operands of those keys
+    //   2. PV of keys 0..15 (4 products) | P of keys 16..31, their V^T
+    //      operands
+    //   3. PV of keys 16..31 (4 products) | K operands of step s + 2, row
+    //      maxima of step s + 1
+    // (K operands are loaded only once the scores of step s are dead, which
+    // keeps the register peak under the 256 of two waves per SIMD.)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      f16x8 vf0[4], vf1[4];
+      f32x16 accn;
+      // phase 1
+      load_v(s, 0, vf0);
+      if (s + 1 < NS) accn = scores(kf);
+      const f16x8 ph0 = probs(acc, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // matrix product
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // vector ALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // phase 2
+      load_v(s, 1, vf1);
+      pv(vf0, ph0);
+      const f16x8 ph1 = probs(acc, 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // phase 3
+      if (s + 2 < NS) load_k(s + 2, kf);
+      pv(vf1, ph1);
+      if (s + 1 < NS) {
+        const float mx = tile_max(accn);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        acc = accn;
+        raise_max(mx);
+      }
+    }
+  };
+
+  // Half-precision V for block j staged in vs_, converted by the wave that
+  // loaded each piece (a wave's direct loads have landed once its own vector
+  // memory count is zero, so no barrier is needed first): rows past the
+  // sequence's end (the last tile's diagonal block) are zeroed, then the
+  // block's largest |v| (bf16 magnitude bits, ordered as integers) decides for
+  // the whole workgroup after the one barrier, which also publishes the
+  // converted block.  When it lies in [2^-8, 2^15] every value converts to
+  // half exactly or (below 2^-14) to within 2^-25; otherwise the workgroup
+  // leaves the tile to the bf16 launch, which stages its own copy.
+  auto convert_own = [&](int j, uint8_t* vs_) {
+    int ln = lane;  // (opaque: nothing lane-indexed is held across the block loop)
+    asm volatile("" : "+v"(ln));
+    if (diag_valid < B && __builtin_amdgcn_readfirstlane(blocks[j]) == own) {  // rare
+#pragma unroll
+      for (int i = 0; i < VI; ++i) {
+        const int ins = wave * VI + i;
+        if (ins * 4 + (ln >> 4) >= diag_valid)
+          *reinterpret_cast<u32x4*>(vs_ + ins * 1024 + ln * 16) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    u32x4 r[VI];
+#pragma unroll
+    for (int i = 0; i < VI; ++i)
+      r[i] = *reinterpret_cast<const u32x4*>(vs_ + (wave * VI + i) * 1024 + ln * 16);
+    u16x2 mx2 = {0, 0};  // largest magnitude bits of each half-word
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      u32x4 h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(u16x2, r[i][e] & 0x7FFF7FFFu));
+        const half2 v = {(_Float16)__builtin_bit_cast(float, r[i][e] << 16),
+                         (_Float16)__builtin_bit_cast(float, r[i][e] & 0xFFFF0000u)};
+        h[e] = __builtin_bit_cast(uint32_t, v);
+      }
+      *reinterpret_cast<u32x4*>(vs_ + (wave * VI + i) * 1024 + ln * 16) = h;
+    }
+    const uint32_t mx = wave_umax(umax_(mx2[0], mx2[1]));
+    if (lane == 0) vmax_w[wave] = mx;
+    __syncthreads();
+    uint32_t bm = vmax_w[0];
+#pragma unroll
+    for (int w = 1; w < kPrefillWaves; ++w) bm = umax_(bm, vmax_w[w]);
+    return bm >= 0x3B80u && bm <= 0x4700u;  // |v| in [2^-8, 2^15]
   };
 
   // V rows of the staged diagonal block past the sequence's end are zeroed
@@ -453,19 +676,47 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   // Two blocks per trip, one per slot: block j + 1 streams into the other
   // slot while block j is computed; the barrier before each block also
   // closes every wave's reads of the slot the next load overwrites.
+  // the half-precision launch stops at a block outside the half range: the
+  // direct loads in flight land first, then the mark (uniform)
+  auto give_up = [&]() {
+    wait_vmem();
+    if (tid == 0) *mark = __builtin_nanf("");
+  };
   if (nsel > 0) issue(0, kslot0, vslot0);
-  for (int j = 0; j < nsel; j += 2) {
-    wait_vmem();
-    __syncthreads();
-    zero_tail(j, vslot0);
-    if (j + 1 < nsel) issue(j + 1, kslot1, vslot1);
-    attend(j, kslot0, vslot0);
-    if (j + 1 >= nsel) break;
-    wait_vmem();
-    __syncthreads();
-    zero_tail(j + 1, vslot1);
-    if (j + 2 < nsel) issue(j + 2, kslot0, vslot0);
-    attend(j + 1, kslot1, vslot1);
+  if constexpr (HALF) {
+    // the diagonal block (causal mask, steps past the wave's last query
+    // skipped) takes the plain step loop
+    auto attend_h = [&](int j, const uint8_t* ks_, const uint8_t* vs_) {
+      if (__builtin_amdgcn_readfirstlane(blocks[j]) == own)
+        attend(j, ks_, vs_, std::true_type{});
+      else
+        attend_pipe(ks_, vs_);
+    };
+    for (int j = 0; j < nsel; j += 2) {
+      wait_vmem();
+      if (!convert_own(j, vslot0)) return give_up();
+      if (j + 1 < nsel) issue(j + 1, kslot1, vslot1);
+      attend_h(j, kslot0, vslot0);
+      if (j + 1 >= nsel) break;
+      wait_vmem();
+      if (!convert_own(j + 1, vslot1)) return give_up();
+      if (j + 2 < nsel) issue(j + 2, kslot0, vslot0);
+      attend_h(j + 1, kslot1, vslot1);
+    }
+  } else {
+    for (int j = 0; j < nsel; j += 2) {
+      wait_vmem();
+      __syncthreads();
+      zero_tail(j, vslot0);
+      if (j + 1 < nsel) issue(j + 1, kslot1, vslot1);
+      attend(j, kslot0, vslot0, std::false_type{});
+      if (j + 1 >= nsel) break;
+      wait_vmem();
+      __syncthreads();
+      zero_tail(j + 1, vslot1);
+      if (j + 2 < nsel) issue(j + 2, kslot0, vslot0);
+      attend(j + 1, kslot1, vslot1, std::false_type{});
+    }
   }
   const float l_row = half_swap_sum(l_run);
   if (!row_ok) return;
@@ -491,14 +742,18 @@ hipError_t launch_sparse_attn_prefill(const Dims& d, const Cache& c, const uint1
   const int zr = (B * G + kPrefillRows - 1) / kPrefillRows;
   const int nwg = (units + 7) / 8 * 8 * zr;
   const float sl2 = d.softmax_scale * kLog2e;
-  if (B == 64)
-    hipLaunchKernelGGL(prefill_attn_kernel<64>, dim3(nwg), dim3(512), 0, stream, c.k, c.v,
-                       c.block_table, q, sel, map, d.num_kv_heads, G, d.top_k, units, zr, sl2,
-                       out);
-  else
-    hipLaunchKernelGGL(prefill_attn_kernel<128>, dim3(nwg), dim3(512), 0, stream, c.k, c.v,
-                       c.block_table, q, sel, map, d.num_kv_heads, G, d.top_k, units, zr, sl2,
-                       out);
+  // half-precision PV first; then the bf16 form for the workgroups it marked
+#define MSA_PREFILL_ATTN(BB, H)                                                                 \
+  hipLaunchKernelGGL((prefill_attn_kernel<BB, H>), dim3(nwg), dim3(512), 0, stream, c.k, c.v,  \
+                     c.block_table, q, sel, map, d.num_kv_heads, G, d.top_k, units, zr, sl2, out)
+  if (B == 64) {
+    MSA_PREFILL_ATTN(64, true);
+    MSA_PREFILL_ATTN(64, false);
+  } else {
+    MSA_PREFILL_ATTN(128, true);
+    MSA_PREFILL_ATTN(128, false);
+  }
+#undef MSA_PREFILL_ATTN
   return hipGetLastError();
 }
 

@@ -11,6 +11,9 @@ max|o - o_exact| / max|o_exact| (the parity metric) for:
   trunc      P truncated to bf16, denominator exact
   rne_den    P rounded to bf16 in both the P.V sum and the denominator
   hi_lo      P as hi + lo, two bf16 terms (hi = rne(P), lo = rne(P - hi))
+  fp16       P rounded to nearest-even IEEE half (11 significant bits,
+             subnormal below 2^-14), denominator exact
+  fp16_den   P rounded to half in both the P.V sum and the denominator
 against the unmodified oracle (fp64 throughout).
 
 Inputs: the 1M prefill workload's per-tile attention shape, at a size the
@@ -54,6 +57,16 @@ static double diag_bf16(double x, int truncate) {
   double q = x / ulp;
   return (truncate ? floor(q) : nearbyint(q)) * ulp;
 }
+/* IEEE half rounding of a positive double in [0, 1] (11 significant bits;
+   below 2^-14 the spacing stays 2^-24) */
+static double diag_fp16(double x) {
+  if (!(x > 0.0)) return x;
+  int e;
+  frexp(x, &e);
+  if (e < -13) e = -13;            /* subnormal range: fixed spacing 2^-24 */
+  double ulp = ldexp(1.0, e - 11);
+  return nearbyint(x / ulp) * ulp;
+}
 """
 
 VARIANTS = {
@@ -64,18 +77,24 @@ VARIANTS = {
               "    double hi = diag_bf16(z[i], 0);\n"
               "    z[i] = hi + diag_bf16(z[i] - hi, 0);\n"
               "  }\n"),
+    "fp16": "  for (int64_t i = 0; i < n; i++) z[i] = diag_fp16(z[i]);\n",
+    "fp16_den": None,
 }
+
+# variants that round P before the denominator is summed
+_ROUND_IN_DEN = {"rne_den": "diag_bf16(exp(z[i] - zmax), 0)",
+                 "fp16_den": "diag_fp16(exp(z[i] - zmax))"}
 
 
 def variant_source(name: str) -> str:
     text = open(SRC).read()
     assert text.count(_ANCHOR) == 1
-    if name == "rne_den":
+    if name in _ROUND_IN_DEN:
         new = ("  double den = 0.0;\n"
                "  for (int64_t i = 0; i < n; i++) {\n"
-               "    z[i] = diag_bf16(exp(z[i] - zmax), 0);\n"
+               "    z[i] = %s;\n"
                "    den += z[i];\n"
-               "  }\n")
+               "  }\n" % _ROUND_IN_DEN[name])
     else:
         new = _ANCHOR + VARIANTS[name]
     text = text.replace(_ANCHOR, new)

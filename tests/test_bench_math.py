@@ -41,6 +41,17 @@ def test_prefill_flops_match_a_count_by_query(P, C, B, k):
     assert att == ap * sh.num_q_heads * sh.head_dim * 4
 
 
+@pytest.mark.parametrize("P,C,B,k", [(0, 1, 64, 4), (0, 300, 64, 8), (1000, 700, 128, 16),
+                                     (77, 1, 128, 16)])
+def test_padded_attention_flops_count_whole_blocks(P, C, B, k):
+    # query i in absolute block c: its kept blocks and its whole diagonal block
+    sh = Shape(num_q_heads=16, num_kv_heads=2, num_idx_heads=4, block_size=B, top_k=k)
+    pairs = sum((min(k - 1, (P + i) // B) + 1) * B for i in range(C))
+    padded = bench.prefill_padded_attn_flops(sh, P, C)
+    assert padded == pairs * sh.num_q_heads * sh.head_dim * 4
+    assert padded >= bench.prefill_algorithmic_flops(sh, P, C)[1]
+
+
 def test_prefill_flops_of_the_1m_chunk():
     # 8,622,964,736 query-key pairs x 32 index rows x 128 flop = 35.32 TFLOP;
     # sparse attention 0.5327 TFLOP exact-causal

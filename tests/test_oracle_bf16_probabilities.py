@@ -1,8 +1,8 @@
 """The bf16-probability diagnostic (oracle/diag_bf16_probabilities.py) on one
 tile of the 1M prefill workload's attention shape (CPU only): rounding the
 softmax probabilities to bfloat16 alone, by nearest-even or by truncation,
-breaks the 2e-3 per-row bound, while the two-term hi + lo form the kernels
-use stays far inside it.  The full run (8 tiles, 65,536 rows) is the
+breaks the 2e-3 per-row bound, while the two-term hi + lo form stays far
+inside it, and so does a single IEEE half (11 significant bits).  The full run (8 tiles, 65,536 rows) is the
 figure quoted with the kernels."""
 from oracle import diag_bf16_probabilities as diag
 
@@ -13,3 +13,5 @@ def test_bf16_probabilities_need_two_terms():
     assert r["trunc"]["worst_row_error"] > 2e-3
     assert r["rne_den"]["worst_row_error"] > 2e-3
     assert r["hi_lo"]["worst_row_error"] < 2e-5
+    assert r["fp16"]["worst_row_error"] < 1e-3
+    assert r["fp16_den"]["worst_row_error"] < 1e-3
