@@ -313,7 +313,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   // Block j's K and V^T into a ring slot: a wave-uniform page base plus
   // 32-bit lane offsets, recomputed per block from an opaque copy of the lane
   // index so that no per-lane address stays live across the block loop.
-  auto issue = [&](int j, uint8_t* kdst, uint8_t* vdst) {
+  auto issue = [&](int j, uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
     const size_t ph = (size_t)__builtin_amdgcn_readfirstlane(pages[j]) * num_kv_heads + g;
     const uint8_t* kg = kbase + ph * KBYTES;
     const uint8_t* vg = vbase + ph * VBYTES;
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   const int m = lane & 31;
 
   // Row maximum of a score tile in log2 units (both lane halves of a row).
-  auto tile_max = [&](const f32x16& acc) {
+  auto tile_max = [&](const f32x16& acc) __attribute__((always_inline)) {
     float mx = acc[0];
 #pragma unroll
     for (int v = 1; v < 16; ++v) mx = __builtin_fmaxf(mx, acc[v]);
@@ -352,7 +352,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   // Raise the running max only when a row's max exceeds it by more than the
   // slack; the output and the sum are rescaled then (exact: both always
   // refer to the same running max).
-  auto raise_max = [&](float mx) {
+  auto raise_max = [&](float mx) __attribute__((always_inline)) {
     if (__ballot(mx > m_run + kRescaleSlack) != 0) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   };
   // P = exp2(S scale - m) of a score tile, added to the row sum and split into
   // bfloat16 hi + lo, hi the truncation of P: P - hi - lo < 2^-16 P.
-  auto probabilities = [&](const f32x16& acc, bf16x8* phi, bf16x8* plo) {
+  auto probabilities = [&](const f32x16& acc, bf16x8* phi, bf16x8* plo) __attribute__((always_inline)) {
     float p[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
     }
   };
   // O^T += V^T P^T over 32 keys (two K steps of 16), hi and lo parts.
-  auto accumulate_pv = [&](const bf16x8 (&vf)[2][4], const bf16x8* phi, const bf16x8* plo) {
+  auto accumulate_pv = [&](const bf16x8 (&vf)[2][4], const bf16x8* phi, const bf16x8* plo) __attribute__((always_inline)) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -399,7 +399,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   // The same in half precision: P rounded to nearest-even half, one product;
   // the row sum adds the rounded values (v_dot2 with ones), so that numerator
   // and denominator weigh each key alike.
-  auto probabilities_h = [&](const f32x16& acc, f16x8* ph) {
+  auto probabilities_h = [&](const f32x16& acc, f16x8* ph) __attribute__((always_inline)) {
     const half2 ones = {(_Float16)1.f, (_Float16)1.f};
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
@@ -414,7 +414,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
       ph[s2] = f16x8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
     }
   };
-  auto accumulate_pv_h = [&](const f16x8 (&vf)[2][4], const f16x8* ph) {
+  auto accumulate_pv_h = [&](const f16x8 (&vf)[2][4], const f16x8* ph) __attribute__((always_inline)) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -438,11 +438,11 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   // attention of the wave's rows over kept block j, staged in ks_ and vs_
   // (V in half precision when VHALF; two copies of the step loop, so that each
   // keeps its own registers)
-  auto attend = [&](int j, const uint8_t* ks_, const uint8_t* vs_, auto vhalf_tag) {
+  auto attend = [&](int j, const uint8_t* ks_, const uint8_t* vs_, auto vhalf_tag) __attribute__((always_inline)) {
     constexpr bool VHALF = decltype(vhalf_tag)::value;
     // (per-step addresses start from opaque copies of the lane offsets, so
     // that the compiler does not hold every step's addresses across the loop)
-    auto load_k = [&](int s, bf16x8* kf) {
+    auto load_k = [&](int s, bf16x8* kf) __attribute__((always_inline)) {
       uint32_t a = k_lane;
       asm volatile("" : "+v"(a));
 #pragma unroll
@@ -450,7 +450,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
         kf[ks] = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4*>(ks_ + (a ^ (uint32_t)(ks << 5)) + s * 8192));
     };
-    auto load_v = [&](int s, bf16x8 (&vf)[2][4]) {
+    auto load_v = [&](int s, bf16x8 (&vf)[2][4]) __attribute__((always_inline)) {
       uint32_t a = v_lane;
       asm volatile("" : "+v"(a));
 #pragma unroll
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
       }
     };
     // S^T = K Q^T of 32 keys x the wave's 32 rows
-    auto scores = [&](const bf16x8* kf) {
+    auto scores = [&](const bf16x8* kf) __attribute__((always_inline)) {
       f32x16 acc = {};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) acc = mfma32(kf[ks], qf[ks], acc);
@@ -514,26 +514,26 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   // them while the vector unit computes exponentials.  Lane addresses are
   // formed once per block (LDS byte addresses, opaque to the compiler, with
   // every step's displacement an instruction offset).
-  auto attend_pipe = [&](const uint8_t* ks_, const uint8_t* vs_) {
+  auto attend_pipe = [&](const uint8_t* ks_, const uint8_t* vs_, auto&& after_prologue) __attribute__((always_inline)) {
     // (from opaque copies of the lane offsets, so that nothing is hoisted
     // out of the block loop to stay live across it)
     uint32_t kl = k_lane, vl = v_lane;
     asm volatile("" : "+v"(kl), "+v"(vl));
-    auto load_k = [&](int s, bf16x8* kf) {
+    auto load_k = [&](int s, bf16x8* kf) __attribute__((always_inline)) {
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
         kf[ks] = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4*>(ks_ + (kl ^ (uint32_t)(ks << 5)) + s * 8192));
     };
     // V^T operands of keys 32 s + 16 s2 .. +15 (all four dimension tiles)
-    auto load_v = [&](int s, int s2, f16x8* vf) {
+    auto load_v = [&](int s, int s2, f16x8* vf) __attribute__((always_inline)) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const uint8_t* a = vs_ + (vl ^ (uint32_t)(64 * mt)) + (32 * s + 16 * s2) * 256;
         vf[mt] = __builtin_bit_cast(f16x8, join_tr(lds_read_tr16(a), lds_read_tr16(a + 1024)));
       }
     };
-    auto scores = [&](const bf16x8* kf) {
+    auto scores = [&](const bf16x8* kf) __attribute__((always_inline)) {
       f32x16 acc = {};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) acc = mfma32(kf[ks], qf[ks], acc);
@@ -541,7 +541,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
     };
     // half-precision P of keys 32 s + 16 s2 .. +15 (values 8 s2 .. 8 s2 + 7
     // of the score tile), added to the row sum as rounded
-    auto probs = [&](const f32x16& acc, int s2) {
+    auto probs = [&](const f32x16& acc, int s2) __attribute__((always_inline)) {
       const half2 ones = {(_Float16)1.f, (_Float16)1.f};
       half2 h[4];
 #pragma unroll
@@ -553,7 +553,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
       }
       return f16x8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
     };
-    auto pv = [&](const f16x8* vf, f16x8 ph) {
+    auto pv = [&](const f16x8* vf, f16x8 ph) __attribute__((always_inline)) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) o[mt] = mfma32_f16(vf[mt], ph, o[mt]);
     };
@@ -561,6 +561,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
     load_k(0, kf);
     f32x16 acc = scores(kf);
     load_k(1, kf);
+    after_prologue();  // (the next block's loads, issued behind the first scores)
     raise_max(tile_max(acc));
     // Each step below is one scheduling region (the rescale branch closes
     // it), laid out in three phases fenced from each other, each spreading
@@ -626,7 +627,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   // converted block.  When it lies in [2^-8, 2^15] every value converts to
   // half exactly or (below 2^-14) to within 2^-25; otherwise the workgroup
   // leaves the tile to the bf16 launch, which stages its own copy.
-  auto convert_own = [&](int j, uint8_t* vs_) {
+  auto convert_own = [&](int j, uint8_t* vs_) __attribute__((always_inline)) {
     int ln = lane;  // (opaque: nothing lane-indexed is held across the block loop)
     asm volatile("" : "+v"(ln));
     if (diag_valid < B && __builtin_amdgcn_readfirstlane(blocks[j]) == own) {  // rare
@@ -665,7 +666,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
 
   // V rows of the staged diagonal block past the sequence's end are zeroed
   // (only the last tile's diagonal block has any; uniform).
-  auto zero_tail = [&](int j, uint8_t* vs_) {
+  auto zero_tail = [&](int j, uint8_t* vs_) __attribute__((always_inline)) {
     if (diag_valid < B && __builtin_amdgcn_readfirstlane(blocks[j]) == own) {
       for (int x = tid + 16 * diag_valid; x < B * 16; x += 512)
         *reinterpret_cast<u32x4*>(vs_ + x * 16) = u32x4{0u, 0u, 0u, 0u};
@@ -678,7 +679,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   // closes every wave's reads of the slot the next load overwrites.
   // the half-precision launch stops at a block outside the half range: the
   // direct loads in flight land first, then the mark (uniform)
-  auto give_up = [&]() {
+  auto give_up = [&]() __attribute__((always_inline)) {
     wait_vmem();
     if (tid == 0) *mark = __builtin_nanf("");
   };
@@ -686,22 +687,22 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   if constexpr (HALF) {
     // the diagonal block (causal mask, steps past the wave's last query
     // skipped) takes the plain step loop
-    auto attend_h = [&](int j, const uint8_t* ks_, const uint8_t* vs_) {
-      if (__builtin_amdgcn_readfirstlane(blocks[j]) == own)
+    auto attend_h = [&](int j, const uint8_t* ks_, const uint8_t* vs_, auto&& nxt) __attribute__((always_inline)) {
+      if (__builtin_amdgcn_readfirstlane(blocks[j]) == own) {
+        nxt();
         attend(j, ks_, vs_, std::true_type{});
-      else
-        attend_pipe(ks_, vs_);
+      } else {
+        attend_pipe(ks_, vs_, nxt);
+      }
     };
     for (int j = 0; j < nsel; j += 2) {
       wait_vmem();
       if (!convert_own(j, vslot0)) return give_up();
-      if (j + 1 < nsel) issue(j + 1, kslot1, vslot1);
-      attend_h(j, kslot0, vslot0);
+      attend_h(j, kslot0, vslot0, [&]() { if (j + 1 < nsel) issue(j + 1, kslot1, vslot1); });
       if (j + 1 >= nsel) break;
       wait_vmem();
       if (!convert_own(j + 1, vslot1)) return give_up();
-      if (j + 2 < nsel) issue(j + 2, kslot0, vslot0);
-      attend_h(j + 1, kslot1, vslot1);
+      attend_h(j + 1, kslot1, vslot1, [&]() { if (j + 2 < nsel) issue(j + 2, kslot0, vslot0); });
     }
   } else {
     for (int j = 0; j < nsel; j += 2) {
