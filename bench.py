@@ -706,12 +706,16 @@ def mfma_probe(args, torch, msa, mi, gu):
 
 
 def summarize_mfma(counter_csv, out_txt, command):
-    """MFMA work and busy fraction per kernel from a counter run of
-    --mfma-probe (SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES,
-    GRBM_GUI_ACTIVE): counted flops = MOPS x 512, checked on the issue loop
-    whose flops are known; busy = busy cycles / (active cycles x SIMDs).  The
-    per-dispatch GRBM_GUI_ACTIVE is the sum over the XCDs' GRBM instances, so
-    it is divided by the XCD count (Num_Xcc of the run's agent info)."""
+    """MFMA work, busy fraction and shader clock per kernel from a counter run
+    of --mfma-probe (SQ_INSTS_VALU_MFMA_MOPS_BF16 and _F16,
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_CYCLES, GRBM_GUI_ACTIVE, GRBM_COUNT): counted
+    flops = MOPS x 512, checked on the issue loop whose flops are known;
+    busy = busy cycles / (active cycles x SIMDs); core clock = GRBM_COUNT
+    per XCD / dispatch duration (the counter window is a little longer than
+    the kernel, so the clock of a short dispatch reads high; it is used, with
+    the peak scaled to it, only for dispatches of 5 ms and more).  The
+    per-dispatch GRBM counters are sums over the XCDs' GRBM instances, so they
+    are divided by the XCD count (Num_Xcc of the run's agent info)."""
     import csv
     import msa_inputs as mi
     n_xcc, n_simd = 8, 1024
@@ -722,9 +726,11 @@ def summarize_mfma(counter_csv, out_txt, command):
                 n_xcc, n_simd = int(r["Num_Xcc"]), int(r["Simd_Count"])
     w = mi.WORKLOADS[PREFILL_WORKLOAD]
     index_flops, attn_flops = prefill_algorithmic_flops(w.shape, w.prior_len, w.chunk_len)
+    B = w.shape.block_size
     known = {"mfma_loop_kernel": 32768.0 * 16 * MFMA_PROBE_ITERS * MFMA_PROBE_WORKGROUPS,
              "index_score_prefill_kernel": float(index_flops),
-             "prefill_attn_kernel": float(attn_flops)}
+             "prefill_attn_kernel<%d, true>" % B: float(attn_flops),
+             "prefill_attn_kernel<%d, false>" % B: float(attn_flops)}
     rows = {}
     for r in csv.DictReader(open(counter_csv)):
         name = next((k for k in known if k in r["Kernel_Name"]), None)
@@ -734,18 +740,32 @@ def summarize_mfma(counter_csv, out_txt, command):
             "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
         d[r["Counter_Name"]] = float(r["Counter_Value"])
     lines = ["rocprofv3 MFMA counters (one dispatch each)", "", "command:", "  " + command, "",
-             "counted TFLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; algorithmic TFLOP as the "
-             "bench counts them (exact causal);",
-             "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / %d XCDs x %d SIMDs)"
-             % (n_xcc, n_simd), "",
-             "%-30s %12s %12s %8s %10s %10s" % ("kernel", "counted TF", "algo TF", "ratio",
-                                                "busy %", "us")]
+             "counted TFLOP = (SQ_INSTS_VALU_MFMA_MOPS_BF16 + _F16) x 512; algorithmic TFLOP "
+             "as the bench counts them (exact causal);",
+             "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / %d XCDs x %d SIMDs);"
+             % (n_xcc, n_simd),
+             "clock = GRBM_COUNT / %d XCDs / duration (GHz; the counter window exceeds the "
+             "kernel, so short dispatches read high);" % n_xcc,
+             "frac = algorithmic TFLOP/s / 2.5 PFLOP/s dense bf16/fp16 peak (at 2.4 GHz); "
+             "frac@clk = the same against that peak scaled to the clock (dispatches >= 5 ms).",
+             "",
+             "%-32s %10s %9s %7s %7s %9s %7s %7s %8s" % (
+                 "kernel", "counted TF", "algo TF", "ratio", "busy %", "us", "clock", "frac",
+                 "frac@clk")]
     for (name, _), d in sorted(rows.items()):
-        counted = d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        counted = (d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+                   + d.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0)) * 512
         active = d.get("GRBM_GUI_ACTIVE", 0.0) / n_xcc
         busy = 100.0 * d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / max(1.0, active * n_simd)
-        lines.append("%-30s %12.4f %12.4f %8.3f %10.1f %10.1f" % (
-            name, counted / 1e12, known[name] / 1e12, counted / known[name], busy, d["us"]))
+        us = max(d["us"], 1e-3)
+        clk = d.get("GRBM_COUNT", 0.0) / n_xcc / us / 1e3       # GHz
+        tfs = known[name] / (us * 1e-6) / 1e12
+        frac = tfs / BF16_PEAK_TFLOPS
+        frac_clk = ("%8.3f" % (tfs / (BF16_PEAK_TFLOPS * clk / 2.4))
+                    if clk > 0 and us >= 5000 and counted > 0 else "%8s" % "-")
+        lines.append("%-32s %10.4f %9.4f %7.3f %7.1f %9.1f %7.3f %8.3f %s" % (
+            name, counted / 1e12, known[name] / 1e12, counted / known[name], busy, us, clk,
+            frac if counted > 0 else 0.0, frac_clk))
     with open(out_txt, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
