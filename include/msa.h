@@ -218,7 +218,15 @@ msa_status msa_index_score_decode(const msa_params *params,
  *   idx_q  bf16 [chunk_len][Hkv][n_i][d_i]
  *   out    f32 [chunk_len][Hq][D]
  *   sel    int32 [num_tiles][Hkv][top_k] or NULL (ascending, -1 padded)
- * block_table row 0 is used; it must cover prior_len+chunk_len tokens. */
+ * block_table row 0 is used; it must cover prior_len+chunk_len tokens.
+ * Precision: every output row is within 2e-3 (max |error| / max |value| of
+ * the row) of exact softmax attention over the kept blocks.  The sparse
+ * attention forms P.V in IEEE half (P rounded to nearest-even half, V
+ * converted exactly) when a workgroup's staged V lies in the half range
+ * (|v| <= 2^15 and not all of its values below 2^-8); otherwise a second
+ * launch recomputes that workgroup's rows with P as two bf16 terms.  That
+ * launch finds such workgroups by a NaN the first one leaves in `out`, so
+ * `out` must not be read before the call's work on `stream` is done. */
 size_t msa_prefill_workspace_bytes(const msa_params *params, int32_t prior_len,
                                    int32_t chunk_len,
                                    int32_t max_blocks_per_seq);
