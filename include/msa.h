@@ -222,8 +222,8 @@ msa_status msa_index_score_decode(const msa_params *params,
  * Precision: every output row is within 2e-3 (max |error| / max |value| of
  * the row) of exact softmax attention over the kept blocks.  The sparse
  * attention forms P.V in IEEE half (P rounded to nearest-even half, V
- * converted exactly) when a workgroup's staged V lies in the half range
- * (|v| <= 2^15 and not all of its values below 2^-8); otherwise a second
+ * converted exactly) when every kept block's largest |v| lies in
+ * [2^-8, 2^15] (and is finite); otherwise a second
  * launch recomputes that workgroup's rows with P as two bf16 terms.  That
  * launch finds such workgroups by a NaN the first one leaves in `out`, so
  * `out` must not be read before the call's work on `stream` is done. */
