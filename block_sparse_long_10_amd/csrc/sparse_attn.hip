@@ -675,10 +675,12 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(
   };
 
   // Two blocks per trip, one per slot: block j + 1 streams into the other
-  // slot while block j is computed; the barrier before each block also
-  // closes every wave's reads of the slot the next load overwrites.
-  // the half-precision launch stops at a block outside the half range: the
-  // direct loads in flight land first, then the mark (uniform)
+  // slot while block j is computed; the barrier before each block (in the
+  // half-precision form, the one inside convert_own) also closes every
+  // wave's reads of the slot the next load overwrites, whose loads are
+  // issued after it.
+  // The half-precision launch stops at a block outside the half range: the
+  // direct loads in flight land first, then the mark (uniform).
   auto give_up = [&]() __attribute__((always_inline)) {
     wait_vmem();
     if (tid == 0) *mark = __builtin_nanf("");
