@@ -3,9 +3,9 @@ rounding the softmax probabilities P to bfloat16 cost, on the 1M-context
 prefill workload's attention shape?
 
 The sparse branch ("MiniMax wird dünn", section 1, Schritt 2) is exact softmax
-attention over the kept blocks.  The GPU kernels feed P to a bf16 matrix
-product; this script measures, with copies of the oracle whose only change is
-a rounding of P inside the P.V sum, the worst per-row error
+attention over the kept blocks.  The GPU kernels feed P to a 16-bit matrix
+product (bf16 or IEEE half); this script measures, with copies of the oracle
+whose only change is a rounding of P inside the P.V sum, the worst per-row error
 max|o - o_exact| / max|o_exact| (the parity metric) for:
   rne        P rounded to nearest-even bf16, denominator exact
   trunc      P truncated to bf16, denominator exact
