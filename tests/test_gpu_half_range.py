@@ -48,3 +48,38 @@ def test_prefill_v_outside_half_range(shape, scale, every):
     pages = torch.arange(0, v.shape[0], every, device=v.device)
     v[pages] = v[pages] * scale
     _check(case, shape, prior)
+
+
+def test_varlen_prefill_v_outside_half_range():
+    """The batched call: sequences whose kept V includes scaled pages hand
+    their workgroups to the bf16 launch, the others stay in half; every
+    sequence is checked against the oracle."""
+    import numpy as np
+    from msa_inputs import make_varlen_prefill_case
+    from tests.test_gpu_varlen import _tile_offsets, run_varlen
+
+    shape = SHAPES[0]
+    priors, chunks = [0, 1000, 4096, 130, 5000], [300, 700, 512, 1, 200]
+    print("\n[gpu half range] varlen %s" % (shape,), flush=True)
+    sys.stdout.flush()
+    case = make_varlen_prefill_case(shape, priors, chunks, 95, device="cuda",
+                                    shuffle_pages=True)
+    v = case.cache.v
+    pages = torch.arange(0, v.shape[0], 5, device=v.device)
+    v[pages] = v[pages] * 2.0 ** 14
+    out, sel = run_varlen(case)
+    out, sel = out.cpu().numpy().astype(np.float64), sel.cpu().numpy()
+    B = shape.block_size
+    toff, qs = _tile_offsets(case), case.q_start
+    for s in range(case.batch):
+        one = case.sequence(s)
+        P = oracle.prepare(one)
+        ref = oracle.prefill(one, prepared=P)
+        nt = one.num_tiles
+        my_sel = sel[toff[s]:toff[s] + nt]
+        for t in range(nt):
+            own = one.prior_len // B + t
+            for g in range(shape.num_kv_heads):
+                check_selection(my_sel[t, g], ref["pooled"][t, g], own, shape.top_k)
+        check_out(out[qs[s]:qs[s] + one.chunk_len], oracle.attend_prefill(one, my_sel, prepared=P),
+                  "sequence %d" % s)
