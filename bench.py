@@ -546,6 +546,66 @@ def measured_peaks(torch, msa):
                     "of v_mfma_f32_32x32x16_bf16 per wave); best of a launch-shape sweep"}
 
 
+def measured_latency(torch, msa):
+    """What one dependent memory round trip and one kernel boundary cost, the
+    bound of the decode attention launch (a chain of short dependent steps).
+    One lane follows a random single-cycle table (msa_probe_latency_chain,
+    vector-memory loads), each call from a fresh random entry, so that no call
+    finds the lines of an earlier one in a cache:
+      - l2: a 256 KiB table whose whole cycle is walked first in the same
+        call (every line then sits in the L2 of the XCD the call runs on);
+      - infinity_cache: a 64 MiB table read once by the device beforehand
+        (it fits the 256 MB Infinity Cache, not the 4 MB L2 of an XCD);
+      - hbm: a 2 GiB table (an eighth of it fits the Infinity Cache).
+    The time per load is the difference between calls of 10000 and 2000
+    loads (100000 and 20000 for l2), the launch and the warm walk cancelling.  launch_us: the time per launch of
+    200 back-to-back one-load launches replayed as a captured HIP graph (no
+    host work between them)."""
+    import numpy as np
+    log("[bench] latency: dependent-load chains and launch cost")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    rng = np.random.default_rng(7)
+    res = {}
+    for name, nbytes in (("l2", 256 << 10), ("infinity_cache", 64 << 20), ("hbm", 2 << 30)):
+        n = nbytes // 4
+        perm = torch.randperm(n, device="cuda", generator=gen)
+        table = torch.empty(n, dtype=torch.int32, device="cuda")
+        table[perm] = torch.roll(perm, -1).to(torch.int32)  # one cycle through all n entries
+        del perm
+        if name == "infinity_cache":
+            torch.sum(table, dtype=torch.int64).item()
+        warm = n if name == "l2" else 0
+
+        def chase(k):
+            msa.msa_probe_latency_chain(table, warm + k, int(rng.integers(n)), sink)
+
+        ks = (20000, 100000) if name == "l2" else (2000, 10000)
+        ms = [_timed_ms(torch, lambda: chase(k), 3, 1) for k in ks]
+        res[name + "_ns_per_load"] = round((ms[1] - ms[0]) * 1e6 / (ks[1] - ks[0]), 1)
+        del table
+    tiny = torch.zeros(1, dtype=torch.int32, device="cuda")
+    launches = 200
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        msa.msa_probe_latency_chain(tiny, 1, 0, sink)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=st):
+            for _ in range(launches):
+                msa.msa_probe_latency_chain(tiny, 1, 0, sink)
+    torch.cuda.current_stream().wait_stream(st)
+    res["launch_us"] = round(_timed_ms(torch, g.replay, 5, 2) * 1e3 / launches, 2)
+    res["note"] = ("msa_probe_latency_chain: one lane, dependent vector loads through a random "
+                   "single-cycle table, a fresh start per call (256 KiB walked whole first in "
+                   "the call: L2; 64 MiB read beforehand: Infinity Cache; 2 GiB: mostly HBM); "
+                   "ns per load from the difference of two chain lengths; launch_us = time "
+                   "per launch of 200 one-load launches in a replayed HIP graph")
+    return res
+
+
 def practical_peaks(torch):
     """What library kernels reach on this machine, for context beside the
     datasheet peaks: a 2 GiB device-to-device copy (bytes read + written per
@@ -938,6 +998,7 @@ def main():
     # and the prefill index kernel is power-limited
     peaks = practical_peaks(torch)
     roofs = measured_peaks(torch, msa)
+    lat = measured_latency(torch, msa)
 
     case = dec["case"]
     sh = case.shape
@@ -986,6 +1047,7 @@ def main():
             "practical_peak_note": "read stream of the same size (128 MiB)",
         },
         "practical_peaks": roofs,
+        "latency_probe": lat,
     }
     if pre is not None:
         pc = pre["case"]

@@ -22,7 +22,7 @@ __all__ = [
     "msa_block_topk_prefill", "msa_sparse_attn_prefill", "msa_last_error", "msa_version",
     "PagedKVMut", "make_kv_mut", "msa_cache_append", "msa_decode_append",
     "msa_prefill_varlen_workspace_bytes", "msa_prefill_varlen", "msa_probe_read_stream",
-    "msa_probe_mfma_bf16",
+    "msa_probe_mfma_bf16", "msa_probe_latency_chain",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -98,6 +98,7 @@ def lib():
             "msa_version": (ctypes.c_char_p, []),
             "msa_probe_read_stream": (ctypes.c_int, [vp, sz, i32, vp, vp]),
             "msa_probe_mfma_bf16": (ctypes.c_int, [i32, i32, vp, vp]),
+            "msa_probe_latency_chain": (ctypes.c_int, [vp, i32, i32, i32, vp, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -308,3 +309,10 @@ def msa_probe_read_stream(src: torch.Tensor, workgroups: int, sink: torch.Tensor
 def msa_probe_mfma_bf16(iters: int, workgroups: int, sink: torch.Tensor, stream=None) -> None:
     """32768 * 16 * iters * workgroups flops of v_mfma_f32_32x32x16_bf16."""
     _check(lib().msa_probe_mfma_bf16(iters, workgroups, _dev(sink, None, "sink"), _stream(stream)))
+
+
+def msa_probe_latency_chain(next_: torch.Tensor, steps: int, start: int, sink: torch.Tensor,
+                            stream=None) -> None:
+    """steps dependent loads p = next_[p] from p = start (next_: int32 GPU table)."""
+    _check(lib().msa_probe_latency_chain(_dev(next_, torch.int32, "next"), next_.numel(), steps,
+                                         start, _dev(sink, torch.int32, "sink"), _stream(stream)))

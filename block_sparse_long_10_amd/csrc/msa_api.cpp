@@ -583,3 +583,20 @@ extern "C" msa_status msa_probe_mfma_bf16(int32_t iters, int32_t workgroups, flo
     return fail(MSA_ERR_HIP, "unexpected internal error");
   }
 }
+
+extern "C" msa_status msa_probe_latency_chain(const int32_t* next, int32_t n, int32_t steps,
+                                              int32_t start, int32_t* sink, void* stream) {
+  try {
+    if (next == nullptr || sink == nullptr)
+      return fail(MSA_ERR_INVALID_ARGUMENT, "next and sink must not be NULL");
+    if (n < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "n must be >= 1");
+    if (start < 0 || start >= n) return fail(MSA_ERR_INVALID_ARGUMENT, "start must be in [0, n)");
+    if (steps < 0 || steps > (1 << 24))
+      return fail(MSA_ERR_INVALID_ARGUMENT, "steps must be in [0, 2^24]");
+    return hip_status(msa::launch_latency_chain(next, n, steps, start, sink,
+                                                static_cast<hipStream_t>(stream)),
+                      "latency chain launch");
+  } catch (...) {
+    return fail(MSA_ERR_HIP, "unexpected internal error");
+  }
+}

@@ -90,6 +90,8 @@ hipError_t launch_chunk_map(const int32_t* prior_lens, const int32_t* chunk_lens
 hipError_t launch_read_stream(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink,
                               hipStream_t stream);
 hipError_t launch_mfma_loop(int32_t iters, int32_t workgroups, float* sink, hipStream_t stream);
+hipError_t launch_latency_chain(const int32_t* next, int32_t n, int32_t steps, int32_t start,
+                                int32_t* sink, hipStream_t stream);
 
 // Step 1, prefill: pooled[u][g][b] for b < own(u) = prior/B + t; max_own is
 // the largest own block of the call.

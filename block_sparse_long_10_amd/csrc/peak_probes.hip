@@ -1,6 +1,7 @@
 // Measurement kernels (include/msa_probes.h): a plain HBM read stream and a
 // bf16 MFMA issue loop, the practical peaks the attention path's kernels
-// are compared with.
+// are compared with, and a chain of dependent loads, the latency that bounds
+// the kernels made of short dependent steps.
 #include "msa_device.h"
 #include "msa_launch.h"
 
@@ -53,6 +54,25 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int32_t iters, float* __
   if (s == 1.0e30f) sink[0] = s;
 }
 
+// One lane follows `steps` links of a chain stored in next[0 .. n): p =
+// next[p], so each load waits for the one before it (an entry outside
+// [0, n) restarts the chain at 0, which keeps every load inside the table).
+// The index is kept in a vector register, so that the loads take the vector
+// memory path (the attention kernels' loads), not the scalar cache.  The
+// last index reached is written to sink[0].
+__global__ __launch_bounds__(64) void latency_chain_kernel(const int32_t* __restrict__ next,
+                                                           int32_t n, int32_t steps, int32_t start,
+                                                           int32_t* __restrict__ sink) {
+  if (threadIdx.x != 0) return;
+  int32_t p = start;
+  for (int32_t i = 0; i < steps; ++i) {
+    asm volatile("" : "+v"(p));
+    p = next[p];
+    if ((uint32_t)p >= (uint32_t)n) p = 0;
+  }
+  sink[0] = p;
+}
+
 hipError_t launch_read_stream(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink,
                               hipStream_t stream) {
   hipLaunchKernelGGL(read_stream_kernel, dim3(workgroups), dim3(64), 0, stream,
@@ -62,6 +82,13 @@ hipError_t launch_read_stream(const void* src, size_t bytes, int32_t workgroups,
 
 hipError_t launch_mfma_loop(int32_t iters, int32_t workgroups, float* sink, hipStream_t stream) {
   hipLaunchKernelGGL(mfma_loop_kernel, dim3(workgroups), dim3(256), 0, stream, iters, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_latency_chain(const int32_t* next, int32_t n, int32_t steps, int32_t start,
+                                int32_t* sink, hipStream_t stream) {
+  hipLaunchKernelGGL(latency_chain_kernel, dim3(1), dim3(64), 0, stream, next, n, steps, start,
+                     sink);
   return hipGetLastError();
 }
 

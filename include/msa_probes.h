@@ -10,7 +10,13 @@
  *                           only streams, as the decode index kernel does);
  *   msa_probe_mfma_bf16   - a loop of independent v_mfma_f32_32x32x16_bf16
  *                           chains (the bf16 matrix-core issue roof, as used
- *                           by the prefill index and attention kernels).
+ *                           by the prefill index and attention kernels);
+ *   msa_probe_latency_chain - one lane following a chain of dependent loads
+ *                           (the latency of one memory round trip, from the
+ *                           level of the memory hierarchy the table fits, and
+ *                           the cost of a launch: the bound of a kernel made
+ *                           of short dependent steps, such as the decode
+ *                           attention launch).
  * The caller times them (events on `stream`); the work per call is stated
  * below.  Same conventions as msa.h: device pointers owned by the caller,
  * host validation first (MSA_ERR_INVALID_ARGUMENT with msa_last_error()),
@@ -45,6 +51,16 @@ msa_status msa_probe_read_stream(const void *src, size_t bytes, int32_t workgrou
  * sink[0] (device, 4 bytes) is written only if a result equals an
  * improbable constant. */
 msa_status msa_probe_mfma_bf16(int32_t iters, int32_t workgroups, float *sink, void *stream);
+
+/* One workgroup; one lane loads p = next[p] `steps` times (0 .. 2^24) with
+ * vector-memory loads, starting at p = start (0 <= start < n), each load's
+ * address depending on the value before; an entry outside [0, n) restarts
+ * the chain at 0, so no load leaves next[0 .. n).  The last index reached is written to sink[0]
+ * (device, 4 bytes).  With a random single-cycle table, the call takes
+ * about steps round trips to wherever the table lives (L2, the Infinity
+ * Cache or HBM, by its size) plus one launch. */
+msa_status msa_probe_latency_chain(const int32_t *next, int32_t n, int32_t steps, int32_t start,
+                                   int32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

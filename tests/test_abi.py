@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
               "msa_index_score_prefill", "msa_block_topk_prefill", "msa_sparse_attn_prefill",
               "msa_cache_append", "msa_decode_append", "msa_prefill_varlen",
               "msa_prefill_varlen_workspace_bytes", "msa_probe_read_stream",
-              "msa_probe_mfma_bf16"]:
+              "msa_probe_mfma_bf16", "msa_probe_latency_chain"]:
         assert n in names
 
 
@@ -233,6 +233,20 @@ def test_read_stream_probe_rejects_bad_arguments(args, msg):
 ])
 def test_mfma_probe_rejects_bad_arguments(args, msg):
     assert msa.lib().msa_probe_mfma_bf16(*args, None) == INVALID
+    assert msg in msa.msa_last_error()
+
+
+@pytest.mark.parametrize("args,msg", [
+    ((None, 16, 4, 0, FAKE), "NULL"),
+    ((FAKE, 16, 4, 0, None), "NULL"),
+    ((FAKE, 0, 4, 0, FAKE), "n must be"),
+    ((FAKE, 16, 4, 16, FAKE), "start"),
+    ((FAKE, 16, 4, -1, FAKE), "start"),
+    ((FAKE, 16, -1, 0, FAKE), "steps"),
+    ((FAKE, 16, (1 << 24) + 1, 0, FAKE), "steps"),
+])
+def test_latency_probe_rejects_bad_arguments(args, msg):
+    assert msa.lib().msa_probe_latency_chain(*args, None) == INVALID
     assert msg in msa.msa_last_error()
 
 

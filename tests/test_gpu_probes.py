@@ -1,7 +1,8 @@
 """The measurement kernels of include/msa_probes.h on the GPU: the read
 stream visits every 16-byte word of its buffer (a single word whose fold
 equals the probe's constant, placed at chosen positions, must reach the
-sink), and the MFMA loop runs to completion.  Marked gpu."""
+sink), the MFMA loop runs to completion, and the latency chain ends where
+the same chain followed on the host ends.  Marked gpu."""
 import sys
 
 import pytest
@@ -47,3 +48,22 @@ def test_mfma_loop_runs():
     msa.msa_probe_mfma_bf16(64, 256, sink)
     torch.cuda.synchronize()
     assert float(sink[0].item()) == 0.0
+
+
+@pytest.mark.parametrize("n,steps,start", [(1, 5, 0), (1000, 0, 7), (1000, 137, 3), (4096, 5000, 0)])
+def test_latency_chain_follows_the_table(n, steps, start):
+    print("\n[gpu probes] latency chain n=%d steps=%d" % (n, steps), flush=True)
+    sys.stdout.flush()
+    g = torch.Generator().manual_seed(n + steps)
+    table = torch.randperm(n, generator=g).to(torch.int32)
+    table[n // 2] = n + 5  # outside the table: the chain restarts at 0
+    p = start
+    for _ in range(steps):
+        p = int(table[p])
+        if not 0 <= p < n:
+            p = 0
+    sink = torch.full((4,), -1, dtype=torch.int32, device="cuda")
+    msa.msa_probe_latency_chain(table.cuda(), steps, start, sink)
+    torch.cuda.synchronize()
+    assert int(sink[0].item()) == p
+
