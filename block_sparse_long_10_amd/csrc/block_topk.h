@@ -8,13 +8,18 @@
 //
 // Fast path (own <= 256*MAXV): the scores are loaded into registers, all
 // loads at once (-inf in the slots past the row).  Each thread takes the max
-// of its scores; an LDS histogram of the 256 thread maxima gives T, the
-// lowest key of the bin that completes k' = k-1 maxima; those k' distinct
-// scores reach T, so it bounds the k'-th best score from below.  The few
-// scores >= T are gathered to LDS (DPP prefix-sum offsets), sorted by
-// (score, index) with a wave-wide DPP bitonic sort, and the winners put in
-// block order by a second one; each sort network is only as wide as its
-// count.  If more than 64 scores reach T (heavy ties), or the row is longer
+// of its scores; an LDS histogram of the thread maxima (threads holding no
+// score left out, so that short rows keep fine bins) gives T, the lowest key
+// of the bin that completes k' = k-1 maxima; those k' distinct scores reach
+// T, so it bounds the k'-th best score from below.  The few scores >= T are
+// gathered to LDS (DPP prefix-sum offsets; every slot is written, the
+// others to a write-off slot, so there is no branch per slot).  With at most
+// four more than k' of them, the worst are dropped one at a time (wave
+// minimum of the key, then maximum of the index among equal keys);
+// otherwise they are sorted by (score, index) with a wave-wide DPP bitonic
+// sort.  A second sort puts the winners in block order; each sort network
+// is only as wide as its count.  If more than 64 scores reach T (heavy
+// ties), or the row is longer
 // than the registers hold, the general path runs instead, on keys re-read
 // from memory (so the fast path's registers are free for the caller's other
 // phases):
@@ -41,7 +46,13 @@ constexpr int kTopkCap = 256;
 constexpr int kMaxTopK = 64;
 
 struct TopkShared {
-  unsigned hist[kTopkBins];
+  // the fast path's histogram, then (once the bound is known) its candidate
+  // (score bits, index) pairs: slots below the count, and one write-off slot
+  // per lane above kWave
+  union {
+    unsigned hist[kTopkBins];
+    uint2 pair[kTopkBins / 2];
+  };
   uint32_t cand_k[kTopkCap];
   int cand_i[kTopkCap];
   int chosen[kMaxTopK];
@@ -69,21 +80,33 @@ template <int N>
 __device__ __forceinline__ uint32_t row_ror_u(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x120 + N, 0xF, 0xF, false);
 }
+// Wave maximum / minimum (every lane active): DPP rotations within each row
+// of 16 lanes, then the four row results meet in scalar registers (lane
+// reads instead of LDS permutes, which cost a round trip through the LDS
+// unit each).  The result is wave-uniform.
+__device__ __forceinline__ uint32_t rows_to_scalar_max(uint32_t v) {
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return umax_(umax_(a, b), umax_(c, d));
+}
+__device__ __forceinline__ uint32_t rows_to_scalar_min(uint32_t v) {
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return umin_(umin_(a, b), umin_(c, d));
+}
 __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
   v = umax_(v, row_ror_u<8>(v));
   v = umax_(v, row_ror_u<4>(v));
   v = umax_(v, row_ror_u<2>(v));
   v = umax_(v, row_ror_u<1>(v));
-  v = umax_(v, (uint32_t)__shfl_xor((int)v, 16, kWave));
-  return umax_(v, (uint32_t)__shfl_xor((int)v, 32, kWave));
+  return rows_to_scalar_max(v);
 }
 __device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
   v = umin_(v, row_ror_u<8>(v));
   v = umin_(v, row_ror_u<4>(v));
   v = umin_(v, row_ror_u<2>(v));
   v = umin_(v, row_ror_u<1>(v));
-  v = umin_(v, (uint32_t)__shfl_xor((int)v, 16, kWave));
-  return umin_(v, (uint32_t)__shfl_xor((int)v, 32, kWave));
+  return rows_to_scalar_min(v);
 }
 
 // Inverse of order_key for keys of finite floats (-0.0 comes back as +0.0).
@@ -307,17 +330,17 @@ __device__ __forceinline__ bool topk_fast(const RegKeys<MAXV>& src, int own, int
   for (int w = MAXV / 2; w >= 1; w /= 2)
 #pragma unroll
     for (int j = 0; j < w; ++j) mx[j] = fmaxf(mx[j], mx[j + w]);
+  // (threads with no score of the row hold -inf: they are left out of the
+  // range and the histogram, so that a short row keeps fine bins; at least
+  // keep < own threads hold a score)
   const uint32_t m = order_key(mx[0]);
-  const uint32_t wmax = wave_umax(m), wmin = wave_umin(m);
+  const bool has = m >= kKeyMinFinite;
+  const uint32_t wmax = wave_umax(m), wmin = wave_umin(has ? m : 0xFFFFFFFFu);
   if (lane == 0) {
     sh.red_a[wave] = wmax;
     sh.red_b[wave] = wmin;
   }
   for (int i = tid; i < kTopkBins; i += kTopkThreads) sh.hist[i] = 0u;
-  if (tid < kWave) {  // empty candidate slots rank below every real key
-    sh.cand_k[tid] = 0u;
-    sh.cand_i[tid] = 0x7FFFFFFF;
-  }
   __syncthreads();
   uint32_t hi = sh.red_a[0], lo = sh.red_b[0];
 #pragma unroll
@@ -331,7 +354,7 @@ __device__ __forceinline__ bool topk_fast(const RegKeys<MAXV>& src, int own, int
   const uint32_t span = hi - lo;
   const int bits = span == 0u ? 0 : 32 - __builtin_clz(span);
   const int shift = bits > 8 ? bits - 8 : 0;
-  atomicAdd(&sh.hist[(hi - m) >> shift], 1u);
+  if (has) atomicAdd(&sh.hist[(hi - m) >> shift], 1u);
   __syncthreads();
   if (wave == 0) {
     constexpr int kPer = kTopkBins / kWave;
@@ -369,25 +392,45 @@ __device__ __forceinline__ bool topk_fast(const RegKeys<MAXV>& src, int own, int
     total += c;
   }
   if (total > kWave) return false;  // uniform
+  // every thread writes every slot j, to its place in the candidate list or
+  // to its lane's write-off slot (no branch per slot); the histogram was last
+  // read before the barrier that published bstar
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
-    if (src.val[j] >= tf) {
-      sh.cand_k[base] = order_key(src.val[j]);
-      sh.cand_i[base] = j * kTopkThreads + tid;
-      ++base;
-    }
+    const bool c = src.val[j] >= tf;
+    sh.pair[c ? base : kWave + lane] =
+        uint2{__builtin_bit_cast(uint32_t, src.val[j]), (uint32_t)(j * kTopkThreads + tid)};
+    base += c ? 1 : 0;
   }
   __syncthreads();
   if (wave == 0) {
-    // the 64 slots in selection order (empty ones sort last), then the first
-    // `keep` indices ascending: sort ~index descending (others sort last)
-    // (sort networks only as wide as needed: the candidates, then the winners)
-    uint32_t key = sh.cand_k[lane], idx = (uint32_t)sh.cand_i[lane];
-    if (total <= 32) wave_sort_pairs<32>(key, idx);
-    else wave_sort_pairs<64>(key, idx);
-    uint32_t v = lane < keep ? ~idx : 0u;
-    if (keep <= 16) wave_sort_desc<16>(v);
-    else if (keep <= 32) wave_sort_desc<32>(v);
+    // total >= keep candidates (T bounds the keep-th best score).  A few
+    // too many: the worst are dropped one at a time (lowest key, then
+    // highest index); more: the candidates are sorted into selection order
+    // and the first keep taken.  The winners' indices are then put in
+    // ascending order (sort networks only as wide as needed).
+    const uint2 pr = sh.pair[lane];
+    bool live = lane < total;
+    uint32_t key = live ? order_key(__builtin_bit_cast(float, pr.x)) : 0u;
+    uint32_t idx = live ? pr.y : 0x7FFFFFFFu;
+    const int drop = total - keep;  // uniform
+    uint32_t v;
+    int width = total;
+    if (drop <= 4) {
+      for (int d = 0; d < drop; ++d) {
+        const uint32_t kmin = wave_umin(live ? key : 0xFFFFFFFFu);
+        const uint32_t imax = wave_umax(live && key == kmin ? idx : 0u);
+        live = live && !(key == kmin && idx == imax);
+      }
+      v = live ? ~idx : 0u;
+    } else {
+      if (total <= 32) wave_sort_pairs<32>(key, idx);
+      else wave_sort_pairs<64>(key, idx);
+      v = lane < keep ? ~idx : 0u;
+      width = keep;
+    }
+    if (width <= 16) wave_sort_desc<16>(v);
+    else if (width <= 32) wave_sort_desc<32>(v);
     else wave_sort_desc<64>(v);
     if (lane < keep) out_sel[lane] = (int)~v;
     if (lane == 0) out_sel[keep] = own;
