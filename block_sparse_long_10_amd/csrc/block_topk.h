@@ -316,8 +316,11 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 }
 
 // Fast path; returns false (leaving out_sel untouched) when more than 64
-// keys reach the bound.  Requires 1 <= keep < own.
-template <int MAXV>
+// keys reach the bound.  Requires 1 <= keep < own.  Without ORDERED the
+// kept blocks before the own one come in a fixed order of the path's own
+// (gather or score order) instead of ascending: for callers that only need
+// the same set in the same order in every workgroup.
+template <int MAXV, bool ORDERED>
 __device__ __forceinline__ bool topk_fast(const RegKeys<MAXV>& src, int own, int keep, int k,
                                           int* out_sel, TopkShared& sh) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -422,17 +425,28 @@ __device__ __forceinline__ bool topk_fast(const RegKeys<MAXV>& src, int own, int
         const uint32_t imax = wave_umax(live && key == kmin ? idx : 0u);
         live = live && !(key == kmin && idx == imax);
       }
+      if constexpr (!ORDERED) {  // the winners in gather order
+        const uint64_t lm = __ballot(live);
+        const int r = __builtin_amdgcn_mbcnt_hi((uint32_t)(lm >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)lm, 0u));
+        if (live) out_sel[r] = (int)idx;
+      }
       v = live ? ~idx : 0u;
     } else {
       if (total <= 32) wave_sort_pairs<32>(key, idx);
       else wave_sort_pairs<64>(key, idx);
+      if constexpr (!ORDERED) {  // the winners in score order
+        if (lane < keep) out_sel[lane] = (int)idx;
+      }
       v = lane < keep ? ~idx : 0u;
       width = keep;
     }
-    if (width <= 16) wave_sort_desc<16>(v);
-    else if (width <= 32) wave_sort_desc<32>(v);
-    else wave_sort_desc<64>(v);
-    if (lane < keep) out_sel[lane] = (int)~v;
+    if constexpr (ORDERED) {
+      if (width <= 16) wave_sort_desc<16>(v);
+      else if (width <= 32) wave_sort_desc<32>(v);
+      else wave_sort_desc<64>(v);
+      if (lane < keep) out_sel[lane] = (int)~v;
+    }
     if (lane == 0) out_sel[keep] = own;
     for (int i = keep + 1 + lane; i < k; i += kWave) out_sel[i] = -1;
   }
@@ -565,7 +579,7 @@ __device__ __forceinline__ void topk_select(const Src& src, int own, int k, int*
 // (64 per thread), otherwise longer rows are re-read from memory.  Each
 // register variant is a separate copy of the selection code, so kernels on a
 // latency-critical path keep only the one they need.
-template <bool WIDE>
+template <bool WIDE, bool ORDERED = true>
 __device__ __forceinline__ void block_topk(const float* __restrict__ scores, int own, int k,
                                            int* out_sel, TopkShared& sh) {
   const int keep = min(k - 1, own);
@@ -575,12 +589,12 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ scores, int
   } else if (own <= kTopkThreads * 32) {
     RegKeys<32> src;
     src.load(scores, own);
-    if (!topk_fast(src, own, keep, k, out_sel, sh))
+    if (!topk_fast<32, ORDERED>(src, own, keep, k, out_sel, sh))
       topk_select(GlobalKeys{scores, own}, own, k, out_sel, sh);
   } else if (WIDE && own <= kTopkThreads * 64) {
     RegKeys<64> src;
     src.load(scores, own);
-    if (!topk_fast(src, own, keep, k, out_sel, sh))
+    if (!topk_fast<64, ORDERED>(src, own, keep, k, out_sel, sh))
       topk_select(GlobalKeys{scores, own}, own, k, out_sel, sh);
   } else {
     GlobalKeys src{scores, own};
@@ -594,9 +608,9 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ scores, int
 // if hi were the own block with a budget of k - (number forced).  Without
 // forced blocks that is the plain selection, written straight to out_sel (one
 // copy of the selection code either way).  tmp is an LDS array of kMaxTopK
-// entries.  Result as block_topk's (ascending, own block included, -1
-// padded).
-template <bool WIDE>
+// entries.  Result as block_topk's (ascending, or as ORDERED allows; own
+// block included, -1 padded).
+template <bool WIDE, bool ORDERED = true>
 __device__ __forceinline__ void block_topk_forced(const float* __restrict__ scores, int own, int k,
                                                   int n_sink, int n_local, int* out_sel,
                                                   int* tmp, TopkShared& sh) {
@@ -604,7 +618,7 @@ __device__ __forceinline__ void block_topk_forced(const float* __restrict__ scor
   const int hi = max(own - n_local, lo);
   const int forced = lo + (own - hi);
   const int kr = k - forced;  // >= 1: the host checks sink + local <= k - 1
-  block_topk<WIDE>(scores + lo, hi - lo, kr, forced == 0 ? out_sel : tmp, sh);
+  block_topk<WIDE, ORDERED>(scores + lo, hi - lo, kr, forced == 0 ? out_sel : tmp, sh);
   if (forced == 0) return;  // uniform
   const int chosen = min(kr - 1, hi - lo);  // tmp[0 .. chosen) are relative block ids
   for (int i = threadIdx.x; i < k; i += kTopkThreads) {

@@ -71,7 +71,9 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(const float* __restric
 // per head combined across the waves in LDS; the last of the top_k slot
 // workgroups of (s, g) merges the partials by log-sum-exp.  With FUSED_TOPK
 // every slot workgroup first derives the selection from the pooled scores
-// (identical in all slots) and slot 0 stores it; otherwise it reads sel.
+// (the same blocks in the same slots in all of them, not necessarily
+// ascending), and slot 0 stores it in ascending order once its own part is
+// done; otherwise it reads sel.
 template <int B, bool FUSED_TOPK>
 __global__ __launch_bounds__(256) void decode_attn_kernel(
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
@@ -102,10 +104,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
   const size_t sg = (size_t)s * num_kv_heads + g;
   int blk;
   if constexpr (FUSED_TOPK) {
-    block_topk_forced<false>(pooled + sg * max_blocks, (L - 1) / B, top_k, n_sink, n_local, sel_s, tmp_s,
-                      tsh);
-    if (slot == 0)
-      for (int i = tid; i < top_k; i += 256) sel[sg * top_k + i] = sel_s[i];
+    block_topk_forced<false, false>(pooled + sg * max_blocks, (L - 1) / B, top_k, n_sink, n_local,
+                                    sel_s, tmp_s, tsh);
     blk = sel_s[slot];
   } else {
     blk = sel[sg * top_k + slot];
@@ -129,8 +129,21 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
     is_last = __hip_atomic_fetch_add(&counters[sg], 1u, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(top_k - 1);
   __syncthreads();
-  if (!is_last) return;
+  // the selection output, ascending and -1 padded (wave 0 of slot 0, after
+  // its partial is counted in: off the merge's path)
+  auto store_selection = [&]() {
+    if (tid >= kWave) return;
+    const int b = tid < top_k ? sel_s[tid] : -1;
+    uint32_t v = b >= 0 ? ~(uint32_t)b : 0u;
+    wave_sort_desc<64>(v);
+    if (tid < top_k) sel[sg * top_k + tid] = v != 0u ? (int)~v : -1;
+  };
+  if (!is_last) {
+    if (FUSED_TOPK && slot == 0) store_selection();
+    return;
+  }
   merge_partials(ro, rml, top_k, group, out + ((size_t)s * Hq + (size_t)g * group) * 128, msh);
+  if (FUSED_TOPK && slot == 0) store_selection();
 }
 
 // Slot workgroups beyond which TopK runs in its own launch instead of being
