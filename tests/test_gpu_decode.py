@@ -155,6 +155,35 @@ def test_decode_constructed_exact_ties():
     np.testing.assert_array_equal(g["sel"], ref["sel"])
 
 
+@pytest.mark.parametrize("extra", [1, 2, 4, 6])
+def test_decode_ties_across_the_cut(extra):
+    """keep + extra blocks with bit-identical index keys are the clear best of
+    each sequence: only keep of them fit, so the cut falls inside the tie and
+    the lowest block indices must win (reading: score descending, then block
+    index ascending).  extra <= 4 is settled by dropping the worst candidates
+    one at a time, 6 by sorting them; both against the oracle bit for bit."""
+    _announce("ties across the cut, %d extra" % extra)
+    keep = SMALL.top_k - 1
+    case = make_decode_case(SMALL, [5000, 2300], 110 + extra, device=DEV)
+    ik = case.cache.idx_k
+    bt = case.cache.block_table
+    rng = np.random.default_rng(extra)
+    for s, L in enumerate(case.lengths):
+        own = (L - 1) // SMALL.block_size
+        tied = sorted(rng.choice(own, size=keep + extra, replace=False).tolist())
+        src = int(bt[s, tied[0]])
+        ik[src] = (ik[src].float() * 0.5 + 1.5).to(torch.bfloat16)
+        for b in tied[1:]:
+            ik[int(bt[s, b])] = ik[src]
+    case.idx_q[:] = case.idx_q.abs()
+    g, ref, _, _ = _full_check(case, exact_sel=True)
+    for s, L in enumerate(case.lengths):
+        own = (L - 1) // SMALL.block_size
+        for gi in range(SMALL.num_kv_heads):
+            assert g["sel"][s, gi].tolist()[-1] == own
+    np.testing.assert_array_equal(g["sel"], ref["sel"])
+
+
 def test_decode_tie_fallback_paths():
     _announce("all-equal and heavily tied scores")
     # every pooled score equal: the lowest indices win
