@@ -131,7 +131,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
   __syncthreads();
   // the selection output, ascending and -1 padded (wave 0 of slot 0, after
   // its partial is counted in: off the merge's path)
-  auto store_selection = [&]() {
+  auto store_selection = [&]() __attribute__((always_inline)) {
     if (tid >= kWave) return;
     const int b = tid < top_k ? sel_s[tid] : -1;
     uint32_t v = b >= 0 ? ~(uint32_t)b : 0u;
