@@ -574,22 +574,24 @@ __device__ __forceinline__ void topk_select(const Src& src, int own, int k, int*
   topk_write_sorted(sh, min(sh.n_chosen, keep), own, k, out_sel);
 }
 
-// TopK of scores[0 .. own) held in global memory.  Up to 8192 candidates
-// live in registers (32 per thread); WIDE kernels also keep up to 16384 there
-// (64 per thread), otherwise longer rows are re-read from memory.  Each
-// register variant is a separate copy of the selection code, so kernels on a
-// latency-critical path keep only the one they need.
-template <bool WIDE, bool ORDERED = true>
+// TopK of scores[0 .. own) held in global memory.  Up to 256 * REGS
+// candidates live in registers (REGS per thread: 32, or 4 for kernels that
+// only meet rows of at most 1024 blocks, which then do an eighth of the
+// work); WIDE kernels also keep up to 16384 there (64 per thread), otherwise
+// longer rows are re-read from memory.  Each register variant is a separate
+// copy of the selection code, so kernels on a latency-critical path keep only
+// the one they need.
+template <bool WIDE, bool ORDERED = true, int REGS = 32>
 __device__ __forceinline__ void block_topk(const float* __restrict__ scores, int own, int k,
                                            int* out_sel, TopkShared& sh) {
   const int keep = min(k - 1, own);
   if (keep >= own || keep == 0) {
     GlobalKeys src{scores, own};  // nothing to rank
     topk_select(src, own, k, out_sel, sh);
-  } else if (own <= kTopkThreads * 32) {
-    RegKeys<32> src;
+  } else if (own <= kTopkThreads * REGS) {
+    RegKeys<REGS> src;
     src.load(scores, own);
-    if (!topk_fast<32, ORDERED>(src, own, keep, k, out_sel, sh))
+    if (!topk_fast<REGS, ORDERED>(src, own, keep, k, out_sel, sh))
       topk_select(GlobalKeys{scores, own}, own, k, out_sel, sh);
   } else if (WIDE && own <= kTopkThreads * 64) {
     RegKeys<64> src;
@@ -610,7 +612,7 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ scores, int
 // copy of the selection code either way).  tmp is an LDS array of kMaxTopK
 // entries.  Result as block_topk's (ascending, or as ORDERED allows; own
 // block included, -1 padded).
-template <bool WIDE, bool ORDERED = true>
+template <bool WIDE, bool ORDERED = true, int REGS = 32>
 __device__ __forceinline__ void block_topk_forced(const float* __restrict__ scores, int own, int k,
                                                   int n_sink, int n_local, int* out_sel,
                                                   int* tmp, TopkShared& sh) {
@@ -618,7 +620,7 @@ __device__ __forceinline__ void block_topk_forced(const float* __restrict__ scor
   const int hi = max(own - n_local, lo);
   const int forced = lo + (own - hi);
   const int kr = k - forced;  // >= 1: the host checks sink + local <= k - 1
-  block_topk<WIDE, ORDERED>(scores + lo, hi - lo, kr, forced == 0 ? out_sel : tmp, sh);
+  block_topk<WIDE, ORDERED, REGS>(scores + lo, hi - lo, kr, forced == 0 ? out_sel : tmp, sh);
   if (forced == 0) return;  // uniform
   const int chosen = min(kr - 1, hi - lo);  // tmp[0 .. chosen) are relative block ids
   for (int i = threadIdx.x; i < k; i += kTopkThreads) {

@@ -358,7 +358,8 @@ msa_status msa::decode_impl(const msa_params* params, const msa_paged_kv* kv, co
                   "index score launch");
   if (st != MSA_OK) return st;
   return hip_status(
-      msa::launch_decode_attn(d, c, static_cast<const uint16_t*>(q), seq_lens, batch, pooled,
+      msa::launch_decode_attn(d, c, static_cast<const uint16_t*>(q), seq_lens, batch, max_seq_len,
+                              pooled,
                               reinterpret_cast<float*>(ws + w.part_o),
                               reinterpret_cast<float*>(ws + w.part_ml), counters,
                               sel != nullptr ? sel : reinterpret_cast<int32_t*>(ws + w.sel), out, s),

@@ -61,9 +61,9 @@ hipError_t launch_cache_append(const Dims& d, const CacheW& c, const uint16_t* k
 // TopK, Step 2 over the kept blocks (one partial per block) and the merge of
 // the partials, decode.  counters must be zero on entry.
 hipError_t launch_decode_attn(const Dims& d, const Cache& c, const uint16_t* q,
-                              const int32_t* seq_lens, int32_t batch, const float* pooled,
-                              float* part_o, float* part_ml, uint32_t* counters, int32_t* sel,
-                              float* out, hipStream_t stream);
+                              const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                              const float* pooled, float* part_o, float* part_ml,
+                              uint32_t* counters, int32_t* sel, float* out, hipStream_t stream);
 
 // Prefill chunks of one or several sequences.  Tiles are numbered sequence
 // after sequence; tile u of the call is local tile t of sequence s, whose

@@ -73,8 +73,9 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(const float* __restric
 // every slot workgroup first derives the selection from the pooled scores
 // (the same blocks in the same slots in all of them, not necessarily
 // ascending), and slot 0 stores it in ascending order once its own part is
-// done; otherwise it reads sel.
-template <int B, bool FUSED_TOPK>
+// done; otherwise it reads sel.  REGS: the selection's scores per thread in
+// registers (4 when no row is longer than 1024 blocks).
+template <int B, bool FUSED_TOPK, int REGS = 32>
 __global__ __launch_bounds__(256) void decode_attn_kernel(
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ block_table, int32_t max_blocks, const uint16_t* __restrict__ q,
@@ -104,8 +105,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
   const size_t sg = (size_t)s * num_kv_heads + g;
   int blk;
   if constexpr (FUSED_TOPK) {
-    block_topk_forced<false, false>(pooled + sg * max_blocks, (L - 1) / B, top_k, n_sink, n_local,
-                                    sel_s, tmp_s, tsh);
+    block_topk_forced<false, false, REGS>(pooled + sg * max_blocks, (L - 1) / B, top_k, n_sink,
+                                          n_local, sel_s, tmp_s, tsh);
     blk = sel_s[slot];
   } else {
     blk = sel[sg * top_k + slot];
@@ -151,20 +152,24 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
 constexpr int kFusedTopkMaxWorkgroups = 1024;
 
 hipError_t launch_decode_attn(const Dims& d, const Cache& c, const uint16_t* q,
-                              const int32_t* seq_lens, int32_t batch, const float* pooled,
-                              float* part_o, float* part_ml, uint32_t* counters, int32_t* sel,
-                              float* out, hipStream_t stream) {
+                              const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                              const float* pooled, float* part_o, float* part_ml,
+                              uint32_t* counters, int32_t* sel, float* out, hipStream_t stream) {
   const int G = d.num_q_heads / d.num_kv_heads;
   const float sl2 = d.softmax_scale * kLog2e;
   const dim3 grid_sg(d.num_kv_heads, batch);
   const dim3 grid_attn(d.top_k, d.num_kv_heads, batch);
   const bool fused = (size_t)d.top_k * d.num_kv_heads * batch <= kFusedTopkMaxWorkgroups;
+  // rows of at most 1024 blocks: the selection with 4 scores per thread
+  const bool short_rows = (max_seq_len - 1) / d.block_size <= kTopkThreads * 4;
   // the dynamic LDS (staged V, block outputs, then merge scratch)
   const size_t dyn = std::max(std::max(attend_wo_bytes(G), sizeof(MergeShared)), kAttendVStageBytes);
 #define MSA_ATTN_ARGS c.k, c.v, c.block_table, c.max_blocks, q, seq_lens, pooled, sel, \
     d.num_kv_heads, G, d.top_k, d.sink_blocks, d.local_blocks, sl2, part_o, part_ml, counters, out
   if (d.block_size == 64) {
-    if (fused) {
+    if (fused && short_rows) {
+      hipLaunchKernelGGL((decode_attn_kernel<64, true, 4>), grid_attn, dim3(256), dyn, stream, MSA_ATTN_ARGS);
+    } else if (fused) {
       hipLaunchKernelGGL((decode_attn_kernel<64, true>), grid_attn, dim3(256), dyn, stream, MSA_ATTN_ARGS);
     } else {
       hipLaunchKernelGGL(decode_topk_kernel<64>, grid_sg, dim3(256), 0, stream, pooled, seq_lens,
@@ -172,7 +177,9 @@ hipError_t launch_decode_attn(const Dims& d, const Cache& c, const uint16_t* q,
       hipLaunchKernelGGL((decode_attn_kernel<64, false>), grid_attn, dim3(256), dyn, stream, MSA_ATTN_ARGS);
     }
   } else {
-    if (fused) {
+    if (fused && short_rows) {
+      hipLaunchKernelGGL((decode_attn_kernel<128, true, 4>), grid_attn, dim3(256), dyn, stream, MSA_ATTN_ARGS);
+    } else if (fused) {
       hipLaunchKernelGGL((decode_attn_kernel<128, true>), grid_attn, dim3(256), dyn, stream, MSA_ATTN_ARGS);
     } else {
       hipLaunchKernelGGL(decode_topk_kernel<128>, grid_sg, dim3(256), 0, stream, pooled, seq_lens,
