@@ -50,8 +50,9 @@
 namespace msa {
 
 // ---------------------------------------------------------------- decode
-// TopK of every (sequence, group): one workgroup each (large batches).
-template <int B>
+// TopK of every (sequence, group): one workgroup each (large batches); REGS
+// as in decode_attn_kernel.
+template <int B, int REGS = 32>
 __global__ __launch_bounds__(256) void decode_topk_kernel(const float* __restrict__ pooled,
                                                           const int32_t* __restrict__ seq_lens,
                                                           int32_t num_kv_heads, int32_t max_blocks,
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(const float* __restric
   __shared__ int sel_s[kMaxTopK], tmp_s[kMaxTopK];
   const int g = blockIdx.x, s = blockIdx.y;
   const size_t sg = (size_t)s * num_kv_heads + g;
-  block_topk_forced<false>(pooled + sg * max_blocks, (seq_lens[s] - 1) / B, top_k, n_sink, n_local, sel_s,
+  block_topk_forced<false, true, REGS>(pooled + sg * max_blocks, (seq_lens[s] - 1) / B, top_k, n_sink, n_local, sel_s,
                     tmp_s, sh);
   for (int i = threadIdx.x; i < top_k; i += 256) sel[sg * top_k + i] = sel_s[i];
 }
@@ -160,8 +161,11 @@ hipError_t launch_decode_attn(const Dims& d, const Cache& c, const uint16_t* q,
   const dim3 grid_sg(d.num_kv_heads, batch);
   const dim3 grid_attn(d.top_k, d.num_kv_heads, batch);
   const bool fused = (size_t)d.top_k * d.num_kv_heads * batch <= kFusedTopkMaxWorkgroups;
-  // rows of at most 1024 blocks: the selection with 4 scores per thread
-  const bool short_rows = (max_seq_len - 1) / d.block_size <= kTopkThreads * 4;
+  // rows of at most 1024 (4096) blocks: the selection with 4 (16) scores
+  // per thread
+  const int max_own = (max_seq_len - 1) / d.block_size;
+  const bool short_rows = max_own <= kTopkThreads * 4;
+  const bool mid_rows = max_own <= kTopkThreads * 16;
   // the dynamic LDS (staged V, block outputs, then merge scratch)
   const size_t dyn = std::max(std::max(attend_wo_bytes(G), sizeof(MergeShared)), kAttendVStageBytes);
 #define MSA_ATTN_ARGS c.k, c.v, c.block_table, c.max_blocks, q, seq_lens, pooled, sel, \
@@ -172,8 +176,13 @@ hipError_t launch_decode_attn(const Dims& d, const Cache& c, const uint16_t* q,
     } else if (fused) {
       hipLaunchKernelGGL((decode_attn_kernel<64, true>), grid_attn, dim3(256), dyn, stream, MSA_ATTN_ARGS);
     } else {
-      hipLaunchKernelGGL(decode_topk_kernel<64>, grid_sg, dim3(256), 0, stream, pooled, seq_lens,
-                         d.num_kv_heads, c.max_blocks, d.top_k, d.sink_blocks, d.local_blocks, sel);
+      if (mid_rows)
+        hipLaunchKernelGGL((decode_topk_kernel<64, 16>), grid_sg, dim3(256), 0, stream, pooled,
+                           seq_lens, d.num_kv_heads, c.max_blocks, d.top_k, d.sink_blocks,
+                           d.local_blocks, sel);
+      else
+        hipLaunchKernelGGL(decode_topk_kernel<64>, grid_sg, dim3(256), 0, stream, pooled, seq_lens,
+                           d.num_kv_heads, c.max_blocks, d.top_k, d.sink_blocks, d.local_blocks, sel);
       hipLaunchKernelGGL((decode_attn_kernel<64, false>), grid_attn, dim3(256), dyn, stream, MSA_ATTN_ARGS);
     }
   } else {
@@ -182,8 +191,13 @@ hipError_t launch_decode_attn(const Dims& d, const Cache& c, const uint16_t* q,
     } else if (fused) {
       hipLaunchKernelGGL((decode_attn_kernel<128, true>), grid_attn, dim3(256), dyn, stream, MSA_ATTN_ARGS);
     } else {
-      hipLaunchKernelGGL(decode_topk_kernel<128>, grid_sg, dim3(256), 0, stream, pooled, seq_lens,
-                         d.num_kv_heads, c.max_blocks, d.top_k, d.sink_blocks, d.local_blocks, sel);
+      if (mid_rows)
+        hipLaunchKernelGGL((decode_topk_kernel<128, 16>), grid_sg, dim3(256), 0, stream, pooled,
+                           seq_lens, d.num_kv_heads, c.max_blocks, d.top_k, d.sink_blocks,
+                           d.local_blocks, sel);
+      else
+        hipLaunchKernelGGL(decode_topk_kernel<128>, grid_sg, dim3(256), 0, stream, pooled, seq_lens,
+                           d.num_kv_heads, c.max_blocks, d.top_k, d.sink_blocks, d.local_blocks, sel);
       hipLaunchKernelGGL((decode_attn_kernel<128, false>), grid_attn, dim3(256), dyn, stream, MSA_ATTN_ARGS);
     }
   }
