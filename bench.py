@@ -741,6 +741,91 @@ def traffic_probe(args, torch, msa, mi, gu):
     log("[bench] traffic probe done; kernel source hash %s" % kernel_source_hash())
 
 
+TIMELINE_WORKLOADS = ["decode_b1_L1M", "decode_b8_L128k", "decode_b1_L4k"]
+TIMELINE_LABELS = {
+    "index_end": "last decode index workgroup ends",
+    "start": "watched attention workgroup starts",
+    "scores_in": "selection: length, pooled scores in, thread maxima",
+    "range": "selection: range of the maxima (barrier)",
+    "bin": "selection: bin of the bound (2 barriers)",
+    "counted": "selection: candidates counted (barrier)",
+    "gathered": "selection: candidates gathered (barrier)",
+    "selected": "selection: worst dropped / sorted, written",
+    "block_known": "kept block of the slot known (barrier)",
+    "kv_in": "block: page id, K, Q, staged V in",
+    "scores": "block: scores and row maxima",
+    "softmax": "block: exponentials and row sums",
+    "pv": "block: P.V products issued",
+    "waves_done": "block: all waves done with V (barrier)",
+    "combined": "block: wave outputs in LDS (barrier)",
+    "stored": "partial stored (before the store wait)",
+    "counted_in": "store wait, hand-off counter back (barrier)",
+    "merged": "group 0 merged (its last slot workgroup)",
+}
+
+
+def timeline(args, torch, msa, mi, gu, out_txt, command):
+    """Wall-clock marks of one decode attention workgroup (libmsa_timeline.so,
+    include/msa_timeline.h): for each workload, warmup + steps msa_decode
+    calls on rotated buffer sets, each between a clear and a read of the
+    marks (so every call starts on an idle GPU); the table gives the median of
+    each mark relative to the watched workgroup's start."""
+    import statistics
+    lines = ["Decode attention launch: per-workgroup timeline (wall-clock marks)", "",
+             "command:", "  " + command, "",
+             "Timeline build of the library (libmsa_timeline.so, -DMSA_TIMELINE): thread 0",
+             "of the slot-1 workgroup of group 0 of sequence 0 stores the 100 MHz",
+             "constant clock (s_memrealtime, 10 ns ticks) at each mark; 'merged' comes",
+             "from the workgroup that merges group 0, 'last decode index workgroup ends'",
+             "is the latest end over the index launch.  Each call runs on an idle GPU",
+             "(the marks are cleared and read around it).  Medians over the timed calls,",
+             "in microseconds from the watched workgroup's start; 'step' is the time",
+             "since the mark above it.", ""]
+    for name in TIMELINE_WORKLOADS:
+        base = mi.make_workload(name, "cuda")
+        sets = [base] + [clone_decode_case(base) for _ in range(max(0, args.rotate - 1))]
+        sh = base.shape
+        p = gu.params_of(sh)
+        kvs = [gu.kv_of(c) for c in sets]
+        batch, maxL, mb = base.batch, max(base.lengths), base.cache.max_blocks
+        out = torch.empty(batch, sh.num_q_heads, sh.head_dim, device="cuda")
+        sel = torch.empty(batch, sh.num_kv_heads, sh.top_k, dtype=torch.int32, device="cuda")
+        ws = torch.zeros(msa.msa_decode_workspace_bytes(p, batch, mb), dtype=torch.uint8,
+                         device="cuda")
+        rows = []
+        for i in range(args.warmup + args.steps):
+            c = sets[i % len(sets)]
+            msa.msa_timeline_clear()
+            msa.msa_decode(p, kvs[i % len(sets)], c.q, c.idx_q, c.seq_lens, batch, maxL, out,
+                           sel, ws)
+            m = msa.msa_timeline_read()
+            if i >= args.warmup:
+                rows.append(m)
+        del sets, kvs
+        torch.cuda.empty_cache()
+        log("[bench] timeline %s: %d calls" % (name, len(rows)))
+        slots = batch * sh.num_kv_heads * sh.top_k
+        lines.append("%s: batch %d, longest row %d blocks, %d slot workgroups, %d timed calls"
+                     % (name, batch, (maxL - 1) // sh.block_size, slots, len(rows)))
+        lines.append("  %-52s %10s %8s %7s" % ("mark", "since start", "step", "reached"))
+        med = {}
+        for k in TIMELINE_LABELS:
+            d = [(r[k] - r["start"]) / 100.0 for r in rows if r[k] and r["start"]]
+            if d:
+                med[k] = (statistics.median(d), len(d))
+        prev = None
+        for k in sorted(med, key=lambda k: med[k][0]):
+            t, n = med[k]
+            step = "" if prev is None else "%8.2f" % (t - prev)
+            lines.append("  %-52s %10.2f %8s %4d/%d" % (TIMELINE_LABELS[k], t, step, n, len(rows)))
+            prev = t
+        lines.append("")
+    if out_txt:
+        with open(out_txt, "w") as f:
+            f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 MFMA_PROBE_ITERS, MFMA_PROBE_WORKGROUPS = 1024, 1024
 
 
@@ -951,6 +1036,10 @@ def main():
     ap.add_argument("--mfma-probe", action="store_true",
                     help="for rocprofv3 counter runs: the MFMA issue loop (calibration), then "
                          "one index, TopK and attention launch of the 1M prefill; no timing")
+    ap.add_argument("--timeline", metavar="OUT_TXT", nargs="?", const="",
+                    help="with libmsa_timeline.so: per-workgroup wall-clock marks of the decode "
+                         "attention launch (medians over --steps calls after --warmup), "
+                         "printed and, given a path, written there; no JSON line")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for rocprofv3 counter runs: one 128 MiB device copy (the "
                          "calibration), then 8 decode index-kernel launches; no timing")
@@ -979,7 +1068,13 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.timeline is not None:
+        msa.use_timeline_library()
     msa.lib()
+    if args.timeline is not None:
+        timeline(args, torch, msa, mi, gu, args.timeline,
+                 "python bench.py " + " ".join(sys.argv[1:]))
+        return
     if args.traffic_probe:
         traffic_probe(args, torch, msa, mi, gu)
         return

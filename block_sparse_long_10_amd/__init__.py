@@ -22,11 +22,13 @@ __all__ = [
     "msa_block_topk_prefill", "msa_sparse_attn_prefill", "msa_last_error", "msa_version",
     "PagedKVMut", "make_kv_mut", "msa_cache_append", "msa_decode_append",
     "msa_prefill_varlen_workspace_bytes", "msa_prefill_varlen", "msa_probe_read_stream",
-    "msa_probe_mfma_bf16", "msa_probe_latency_chain",
+    "msa_probe_mfma_bf16", "msa_probe_latency_chain", "use_timeline_library", "msa_timeline_clear",
+    "msa_timeline_read", "TIMELINE_MARKS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmsa.so")
+_TIMELINE_LIB_PATH = os.path.join(_HERE, "libmsa_timeline.so")
 
 MSA_OK = 0
 STATUS_NAMES = {0: "MSA_OK", -1: "MSA_ERR_INVALID_ARGUMENT", -2: "MSA_ERR_UNSUPPORTED",
@@ -67,6 +69,16 @@ def library_path() -> str:
     return _LIB_PATH
 
 
+def use_timeline_library() -> None:
+    """Load libmsa_timeline.so (include/msa_timeline.h: the same entry points
+    plus the wall-clock marks) instead of libmsa.so.  Must come before the
+    first call into the library."""
+    global _LIB_PATH
+    if _lib is not None:
+        raise RuntimeError("the library is already loaded from %s" % _LIB_PATH)
+    _LIB_PATH = _TIMELINE_LIB_PATH
+
+
 def lib():
     """The loaded libmsa.so; raises if it has not been built."""
     global _lib
@@ -100,6 +112,9 @@ def lib():
             "msa_probe_mfma_bf16": (ctypes.c_int, [i32, i32, vp, vp]),
             "msa_probe_latency_chain": (ctypes.c_int, [vp, i32, i32, i32, vp, vp]),
         }
+        if hasattr(L, "msa_timeline_read"):  # the timeline build only
+            sigs["msa_timeline_clear"] = (ctypes.c_int, [])
+            sigs["msa_timeline_read"] = (ctypes.c_int, [vp, i32])
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
             fn.restype, fn.argtypes = res, args
@@ -316,3 +331,29 @@ def msa_probe_latency_chain(next_: torch.Tensor, steps: int, start: int, sink: t
     """steps dependent loads p = next_[p] from p = start (next_: int32 GPU table)."""
     _check(lib().msa_probe_latency_chain(_dev(next_, torch.int32, "next"), next_.numel(), steps,
                                          start, _dev(sink, torch.int32, "sink"), _stream(stream)))
+
+
+# Mark numbers of include/msa_timeline.h, in order.
+TIMELINE_MARKS = ["start", "scores_in", "range", "bin", "counted", "gathered", "selected",
+                  "block_known", "kv_in", "scores", "softmax", "pv", "waves_done", "combined",
+                  "stored", "counted_in", "merged", "index_end"]
+
+
+def _timeline_lib():
+    L = lib()
+    if not hasattr(L, "msa_timeline_read"):
+        raise RuntimeError("%s has no timeline marks; call use_timeline_library() first" % _LIB_PATH)
+    return L
+
+
+def msa_timeline_clear() -> None:
+    """Sets every mark to 0 (synchronises the device)."""
+    _check(_timeline_lib().msa_timeline_clear())
+
+
+def msa_timeline_read() -> dict:
+    """The marks, {name: 10 ns clock ticks, 0 if not reached} (synchronises
+    the device)."""
+    buf = (ctypes.c_uint64 * len(TIMELINE_MARKS))()
+    _check(_timeline_lib().msa_timeline_read(ctypes.cast(buf, ctypes.c_void_p), len(buf)))
+    return dict(zip(TIMELINE_MARKS, list(buf)))

@@ -37,6 +37,7 @@
 #pragma once
 
 #include "msa_device.h"
+#include "timeline_marks.h"
 
 namespace msa {
 
@@ -320,6 +321,11 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // kept blocks before the own one come in a fixed order of the path's own
 // (gather or score order) instead of ascending: for callers that only need
 // the same set in the same order in every workgroup.
+// (timeline marks: the unordered form runs only in the decode attention kernel)
+#define MSA_TOPK_MARK(m)                \
+  do {                                  \
+    if constexpr (!ORDERED) MSA_MARK(m); \
+  } while (0)
 template <int MAXV, bool ORDERED>
 __device__ __forceinline__ bool topk_fast(const RegKeys<MAXV>& src, int own, int keep, int k,
                                           int* out_sel, TopkShared& sh) {
@@ -337,6 +343,7 @@ __device__ __forceinline__ bool topk_fast(const RegKeys<MAXV>& src, int own, int
   // range and the histogram, so that a short row keeps fine bins; at least
   // keep < own threads hold a score)
   const uint32_t m = order_key(mx[0]);
+  MSA_TOPK_MARK(MSA_MARK_SCORES_IN);
   const bool has = m >= kKeyMinFinite;
   const uint32_t wmax = wave_umax(m), wmin = wave_umin(has ? m : 0xFFFFFFFFu);
   if (lane == 0) {
@@ -345,6 +352,7 @@ __device__ __forceinline__ bool topk_fast(const RegKeys<MAXV>& src, int own, int
   }
   for (int i = tid; i < kTopkBins; i += kTopkThreads) sh.hist[i] = 0u;
   __syncthreads();
+  MSA_TOPK_MARK(MSA_MARK_RANGE);
   uint32_t hi = sh.red_a[0], lo = sh.red_b[0];
 #pragma unroll
   for (int w = 1; w < kTopkThreads / kWave; ++w) {
@@ -375,6 +383,7 @@ __device__ __forceinline__ bool topk_fast(const RegKeys<MAXV>& src, int own, int
     }
   }
   __syncthreads();
+  MSA_TOPK_MARK(MSA_MARK_BIN);
   const uint32_t edge = ((uint32_t)(sh.bstar + 1) << shift) - 1u;  // hi - key <= edge
   // the bound as a float (at least -FLT_MAX, so the -inf of empty slots
   // never reaches it): key >= t  <=>  score >= tf for finite scores
@@ -387,6 +396,7 @@ __device__ __forceinline__ bool topk_fast(const RegKeys<MAXV>& src, int own, int
   const int incl = wave_incl_scan(cnt);
   if (lane == kWave - 1) sh.wave_cnt[wave] = incl;
   __syncthreads();
+  MSA_TOPK_MARK(MSA_MARK_COUNTED);
   int base = incl - cnt, total = 0;
 #pragma unroll
   for (int w = 0; w < kTopkThreads / kWave; ++w) {
@@ -406,6 +416,7 @@ __device__ __forceinline__ bool topk_fast(const RegKeys<MAXV>& src, int own, int
     base += c ? 1 : 0;
   }
   __syncthreads();
+  MSA_TOPK_MARK(MSA_MARK_GATHERED);
   if (wave == 0) {
     // total >= keep candidates (T bounds the keep-th best score).  A few
     // too many: the worst are dropped one at a time (lowest key, then
@@ -449,10 +460,12 @@ __device__ __forceinline__ bool topk_fast(const RegKeys<MAXV>& src, int own, int
     }
     if (lane == 0) out_sel[keep] = own;
     for (int i = keep + 1 + lane; i < k; i += kWave) out_sel[i] = -1;
+    MSA_TOPK_MARK(MSA_MARK_SELECTED);
   }
   __syncthreads();
   return true;
 }
+#undef MSA_TOPK_MARK
 
 // Sort keep+1 kept blocks (chosen[0..found) and own) ascending into out_sel.
 __device__ __forceinline__ void topk_write_sorted(const TopkShared& sh, int found, int own, int k,

@@ -6,6 +6,7 @@
 #pragma once
 
 #include "msa_device.h"
+#include "timeline_marks.h"
 
 namespace msa {
 
@@ -126,6 +127,7 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ kc,
       }
     }
     wait_vmem();  // K, Q and the staged V rows are in place (one wave: no barrier)
+    MSA_MARK(MSA_MARK_KV_IN);
     if (t0 + 32 > n_valid) {  // rows past the last token: zero (uniform)
       for (int x = lane + 16 * (n_valid - t0); x < 32 * 16; x += kWave)
         *reinterpret_cast<u32x4*>(vs + x * 16) = u32x4{0u, 0u, 0u, 0u};
@@ -164,6 +166,7 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ kc,
     for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
     mx = fmaxf(mx, xor_lane(mx, 16));
     mx = fmaxf(mx, xor_lane(mx, 32));
+    MSA_MARK(MSA_MARK_SCORES);
     float p[8], sum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -174,6 +177,7 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ kc,
     sum += xor_lane(sum, 32);
     m_w = mx;
     l_w = sum;
+    MSA_MARK(MSA_MARK_SOFTMAX);
     // P^T as the B operand (keys 8*q4 + j of head r16), hi + lo bf16 parts
     uint32_t hi[8], lo[8];
 #pragma unroll
@@ -187,6 +191,7 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ kc,
       o[mt] = mfma16(vf[mt], phi, o[mt]);
       o[mt] = mfma16(vf[mt], plo, o[mt]);
     }
+    MSA_MARK(MSA_MARK_PV);
   }
   // o[mt][j] = O^T[dim 16*mt + 4*q4 + j][head r16]
   if (lane < 16) {
@@ -194,6 +199,7 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ kc,
     sh.w_l[wave][lane] = l_w;
   }
   __syncthreads();  // every wave's V reads are done before w_o (aliasing vstage) is written
+  MSA_MARK(MSA_MARK_WAVES_DONE);
   if (r16 < group) {
     float* row = w_o + (wave * group + r16) * kWoStride;
 #pragma unroll
@@ -202,6 +208,7 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ kc,
       for (int j = 0; j < 4; ++j) row[16 * mt + 4 * q4 + j] = o[mt][j];
   }
   __syncthreads();
+  MSA_MARK(MSA_MARK_COMBINED);
   // combine the waves: thread -> (head h, dims 4*d4 .. +3)
   for (int idx = tid; idx < group * 32; idx += 256) {
     const int h = idx >> 5, d4 = idx & 31;

@@ -14,6 +14,7 @@
 #include "index_block.h"
 #include "msa_device.h"
 #include "msa_launch.h"
+#include "timeline_marks.h"
 
 namespace msa {
 
@@ -87,6 +88,7 @@ __global__ __launch_bounds__(64) void index_score_decode_kernel(
                                   num_kv_heads, stage,
                                   [&](int g, float v) { out[(size_t)g * max_blocks] = v; });
   }
+  MSA_MARK_LATEST(MSA_MARK_INDEX_END);
 }
 
 // Batches whose full (block, sequence) grid is mostly empty (lengths far
@@ -154,6 +156,7 @@ __global__ __launch_bounds__(64) void index_score_decode_compact_kernel(
     i = in;
     page = page_n;
   }
+  MSA_MARK_LATEST(MSA_MARK_INDEX_END);
 }
 
 template <int B, int NI>
@@ -266,5 +269,9 @@ hipError_t launch_index_score_decode(const Dims& d, const Cache& c, const uint16
                               c.max_blocks, idx_q, seq_lens, d.num_kv_heads, d.idx_k_heads, pooled,
                               counters, ap);
 }
+
+#ifdef MSA_TIMELINE
+MSA_TIMELINE_ACCESSORS(index)
+#endif
 
 }  // namespace msa

@@ -16,6 +16,7 @@
 #include "msa.h"
 #include "msa_launch.h"
 #include "msa_probes.h"
+#include "msa_timeline.h"
 #include "msa_api_internal.h"
 
 namespace {
@@ -601,3 +602,33 @@ extern "C" msa_status msa_probe_latency_chain(const int32_t* next, int32_t n, in
     return fail(MSA_ERR_HIP, "unexpected internal error");
   }
 }
+
+#ifdef MSA_TIMELINE
+// Timeline build only: the marks of msa_timeline.h.
+extern "C" msa_status msa_timeline_clear(void) {
+  try {
+    const hipError_t e = msa::timeline_clear_attn();
+    if (e != hipSuccess) return hip_status(e, "timeline clear");
+    return hip_status(msa::timeline_clear_index(), "timeline clear");
+  } catch (...) {
+    return fail(MSA_ERR_HIP, "unexpected internal error");
+  }
+}
+
+extern "C" msa_status msa_timeline_read(uint64_t* marks, int32_t n) {
+  try {
+    if (marks == nullptr) return fail(MSA_ERR_INVALID_ARGUMENT, "marks must not be NULL");
+    if (n < MSA_NUM_MARKS) return fail(MSA_ERR_INVALID_ARGUMENT, "n must be >= MSA_NUM_MARKS");
+    unsigned long long attn[MSA_NUM_MARKS], index[MSA_NUM_MARKS];
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = msa::timeline_read_attn(attn);
+    if (e == hipSuccess) e = msa::timeline_read_index(index);
+    if (e != hipSuccess) return hip_status(e, "timeline read");
+    for (int i = 0; i < MSA_NUM_MARKS; ++i) marks[i] = attn[i];
+    marks[MSA_MARK_INDEX_END] = index[MSA_MARK_INDEX_END];
+    return MSA_OK;
+  } catch (...) {
+    return fail(MSA_ERR_HIP, "unexpected internal error");
+  }
+}
+#endif

@@ -109,4 +109,13 @@ hipError_t launch_sparse_attn_prefill(const Dims& d, const Cache& c, const uint1
                                       const ChunkMap& m, int32_t num_tiles, const int32_t* sel,
                                       float* out, hipStream_t stream);
 
+#ifdef MSA_TIMELINE
+// Timeline build: copy out / clear the marks of the attention and index
+// translation units (synchronous).
+hipError_t timeline_read_attn(unsigned long long* out);
+hipError_t timeline_clear_attn();
+hipError_t timeline_read_index(unsigned long long* out);
+hipError_t timeline_clear_index();
+#endif
+
 }  // namespace msa

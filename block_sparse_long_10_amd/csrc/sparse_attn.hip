@@ -46,6 +46,7 @@
 #include "decode_attend.h"
 #include "msa_device.h"
 #include "msa_launch.h"
+#include "timeline_marks.h"
 
 namespace msa {
 
@@ -101,6 +102,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
   const int lin = blockIdx.x + blockIdx.y * gridDim.x;
   const int g = lin % num_kv_heads, slot = lin / num_kv_heads, s = blockIdx.z;
   const int tid = threadIdx.x;
+  MSA_MARK(MSA_MARK_START);
   const int Hq = num_kv_heads * group;
   const int L = seq_lens[s];
   const size_t sg = (size_t)s * num_kv_heads + g;
@@ -112,6 +114,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
   } else {
     blk = sel[sg * top_k + slot];
   }
+  MSA_MARK(MSA_MARK_BLOCK_KNOWN);
 
   // partials of (s, g): o [top_k][group][128] and (m, l, -, -) [top_k][group]
   const uint32_t o_bytes = (uint32_t)top_k * group * 128 * 4, ml_bytes = (uint32_t)top_k * group * 16;
@@ -122,6 +125,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
                   num_kv_heads, g, group, scale_log2, slot, ro, rml, ash, dyn_lds,
                   reinterpret_cast<uint8_t*>(dyn_lds));
 
+  MSA_MARK(MSA_MARK_STORED);
   // hand-off: stores complete, then count this slot in; the last slot
   // workgroup reads the partials with agent-scope loads issued after its
   // increment returned
@@ -131,6 +135,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
     is_last = __hip_atomic_fetch_add(&counters[sg], 1u, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(top_k - 1);
   __syncthreads();
+  MSA_MARK(MSA_MARK_COUNTED_IN);
   // the selection output, ascending and -1 padded (wave 0 of slot 0, after
   // its partial is counted in: off the merge's path)
   auto store_selection = [&]() __attribute__((always_inline)) {
@@ -145,6 +150,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
     return;
   }
   merge_partials(ro, rml, top_k, group, out + ((size_t)s * Hq + (size_t)g * group) * 128, msh);
+  MSA_MARK_IF(s == 0 && g == 0, MSA_MARK_MERGED);
   if (FUSED_TOPK && slot == 0) store_selection();
 }
 
@@ -793,5 +799,9 @@ hipError_t launch_sparse_attn_prefill(const Dims& d, const Cache& c, const uint1
 #undef MSA_PREFILL_ATTN
   return hipGetLastError();
 }
+
+#ifdef MSA_TIMELINE
+MSA_TIMELINE_ACCESSORS(attn)
+#endif
 
 }  // namespace msa

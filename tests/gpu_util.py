@@ -44,7 +44,7 @@ def run_decode(case, with_pooled=True, ws=None):
     batch, maxL, mb = case.batch, max(case.lengths), case.cache.max_blocks
     out = torch.full((batch, sh.num_q_heads, sh.head_dim), float("nan"), device=dev)
     sel = torch.full((batch, sh.num_kv_heads, sh.top_k), -7, dtype=torch.int32, device=dev)
-    if ws is None:  # zero-filled: the selection reads the chunk maxima
+    if ws is None:  # (contents on entry do not matter; test_gpu_decode checks that)
         ws = torch.zeros(msa.msa_decode_workspace_bytes(p, batch, mb), dtype=torch.uint8,
                          device=dev)
     msa.msa_decode(p, kv, case.q, case.idx_q, case.seq_lens, batch, maxL, out, sel, ws)

@@ -14,14 +14,16 @@ from block_sparse_long_10_amd import Params, PagedKV
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "msa.h")
 HEADERS = [HEADER, os.path.join(ROOT, "include", "msa_probes.h")]
+TIMELINE_HEADER = os.path.join(ROOT, "include", "msa_timeline.h")
+TIMELINE_LIB = os.path.join(os.path.dirname(msa.library_path()), "libmsa_timeline.so")
 
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
 FAKE = 0x10000  # a non-null address; never dereferenced by a rejected call
 
 
-def declared_functions():
+def declared_functions(headers=HEADERS):
     names = set()
-    for h in HEADERS:
+    for h in headers:
         text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
         names.update(re.findall(r"\b(msa_[a-z_0-9]+)\s*\(", text))
     return sorted(names)
@@ -43,6 +45,49 @@ def test_library_loads_and_exports_every_declared_symbol():
     for n in declared_functions():
         assert hasattr(L, n), n
     assert msa.msa_version().startswith("msa-mi355x")
+
+
+def _timeline_lib():
+    if not os.path.exists(TIMELINE_LIB):
+        pytest.skip("libmsa_timeline.so is not built (block_sparse_long_10_amd/build.py builds it)")
+    return ctypes.CDLL(TIMELINE_LIB)
+
+
+def test_timeline_library_exports_the_same_entry_points_and_the_marks():
+    """libmsa_timeline.so (the -DMSA_TIMELINE build) exports every entry point
+    of msa.h and msa_probes.h plus those of msa_timeline.h; libmsa.so exports
+    none of the latter."""
+    T = _timeline_lib()
+    extra = declared_functions([TIMELINE_HEADER])
+    assert extra == ["msa_timeline_clear", "msa_timeline_read"]
+    for n in declared_functions() + extra:
+        assert hasattr(T, n), n
+    L = ctypes.CDLL(msa.library_path())
+    for n in extra:
+        assert not hasattr(L, n), n
+
+
+def test_timeline_mark_numbers_match_the_binding():
+    """The MSA_MARK_* numbers of msa_timeline.h are 0 .. MSA_NUM_MARKS-1 in
+    the order of the binding's TIMELINE_MARKS names."""
+    text = open(TIMELINE_HEADER).read()
+    marks = {m.group(1).lower(): int(m.group(2))
+             for m in re.finditer(r"#define MSA_MARK_([A-Z_]+) (\d+)", text)}
+    num = int(re.search(r"#define MSA_NUM_MARKS (\d+)", text).group(1))
+    assert sorted(marks.values()) == list(range(num))
+    assert [k for k, _ in sorted(marks.items(), key=lambda kv: kv[1])] == msa.TIMELINE_MARKS
+
+
+def test_timeline_read_rejects_bad_arguments():
+    T = _timeline_lib()
+    T.msa_timeline_read.restype = ctypes.c_int
+    T.msa_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+    T.msa_last_error.restype = ctypes.c_char_p
+    assert T.msa_timeline_read(None, 64) == INVALID
+    assert b"NULL" in T.msa_last_error()
+    buf = (ctypes.c_uint64 * 4)()
+    assert T.msa_timeline_read(ctypes.cast(buf, ctypes.c_void_p), 4) == INVALID
+    assert b"MSA_NUM_MARKS" in T.msa_last_error()
 
 
 def good_params(**kw):

@@ -111,6 +111,30 @@ def test_decode_shape_variants(shape):
     print("worst row err %.3g" % worst)
 
 
+
+# The selection's register tiers switch on the longest row of the batch
+# (max_seq_len): the fused TopK keeps 4 scores per thread up to 1024 ranked
+# blocks and 32 above; the separate TopK launch (more than 1024 slot
+# workgroups) keeps 16 up to 4096 blocks and 32 above.  Each edge from both
+# sides, beside short rows of the same batch.
+EDGE_FUSED = Shape(num_q_heads=8, num_kv_heads=2, num_idx_heads=4, block_size=64, top_k=8)
+EDGE_SPLIT = Shape(num_q_heads=8, num_kv_heads=2, num_idx_heads=2, block_size=64, top_k=64)
+
+
+@pytest.mark.parametrize("shape,own,others,seed", [
+    (EDGE_FUSED, 1024, [3000, 1], 111),
+    (EDGE_FUSED, 1025, [3000, 65], 112),
+    (EDGE_SPLIT, 4096, [1, 64, 65, 5000, 30000, 65600, 9000, 129], 113),
+    (EDGE_SPLIT, 4097, [1, 64, 65, 5000, 30000, 65600, 9000, 129], 114),
+])
+def test_decode_selection_tier_edges(shape, own, others, seed):
+    lengths = [own * shape.block_size + 1] + others
+    _announce("selection tier edge: %d ranked blocks, %d slot workgroups"
+              % (own, len(lengths) * shape.num_kv_heads * shape.top_k))
+    case = make_decode_case(shape, lengths, seed, device=DEV, shuffle_pages=True, poison_frac=0.02)
+    g, worst, kinds = _big_check(case)
+    print("worst row err %.3g, selections %s" % (worst, {k: kinds.count(k) for k in set(kinds)}))
+
 def test_decode_workload_b1_L4k():
     _announce("decode_b1_L4k")
     case = make_workload("decode_b1_L4k", DEV)
