@@ -242,6 +242,22 @@ struct MergeShared {
   float w[16][kMaxSlots];
 };
 
+// Weights of up to 16 slots: lane (h, k) of a DPP row of 16 (h = tid/16,
+// k = tid%16) takes the (max, sum) record v of slot k, head h.
+__device__ __forceinline__ void row_weights(f32x4 v, int top_k, int group, MergeShared& ms) {
+  const int tid = threadIdx.x, hh = tid >> 4, k = tid & 15;
+  const bool live = hh < group && k < top_k;
+  const float m = live ? v[0] : -INFINITY;
+  const float M = row16_max(m);
+  const float e = live ? exp2f(m - M) : 0.f;  // 0 for an empty slot
+  float den = e * v[1];
+  den += row_ror<8>(den);
+  den += row_ror<4>(den);
+  den += row_ror<2>(den);
+  den += row_ror<1>(den);
+  if (live) ms.w[hh][k] = e / den;
+}
+
 __device__ __forceinline__ void merge_partials(__amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rml,
                                                int top_k, int group, float* __restrict__ out_sg,
                                                MergeShared& ms) {
@@ -249,32 +265,36 @@ __device__ __forceinline__ void merge_partials(__amdgpu_buffer_rsrc_t ro, __amdg
   const int tid = threadIdx.x;
   // item = (head h, dims 4*d4 .. +3): group*32 of them, one or two per thread
   const int items = group * 32;
-  // one item and one chunk per thread (uniform): the thread's partials are
-  // loaded while the weights are formed (slots past top_k read beyond the
-  // buffer range: zeros); otherwise they are loaded chunk by chunk after
-  // (so that only one chunk of registers is ever live)
-  const bool single = items <= 256 && top_k <= kChunk;
-  f32x4 o[kChunk];
-  if (single) {
+  if (items <= 256 && top_k <= kChunk) {  // uniform
+    // one item and one chunk per thread, in straight-line code: the weight
+    // lane's (max, sum) record is loaded first and the item's partials after
+    // it, so that the weights, which wait for the record only (loads complete
+    // in order), are formed while the partials stream in.  Slots past top_k
+    // and rows past the group read beyond the buffer range: zeros.
+    const f32x4 v = load_shared4(rml, ((tid & 15) * group + (tid >> 4)) * 16);
     const int h = tid >> 5, d4 = tid & 31;
+    f32x4 o[kChunk];
 #pragma unroll
     for (int k = 0; k < kChunk; ++k)
       o[k] = load_shared4(ro, ((k * group + h) * 128 + 4 * d4) * 4);
+    row_weights(v, top_k, group, ms);
+    __syncthreads();
+    if (tid >= items) return;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) {
+      const float w = k < top_k ? ms.w[h][k] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = fmaf(w, o[k][j], acc[j]);
+    }
+    *reinterpret_cast<f32x4*>(out_sg + (size_t)h * 128 + 4 * d4) = acc;
+    return;
   }
-  if (top_k <= 16) {  // uniform: lane (h, k) of a DPP row of 16 forms weight (h, k)
-    const int hh = tid >> 4, k = tid & 15;
-    const bool live = hh < group && k < top_k;
-    // (rows past the group or slots past top_k read beyond the range: zeros)
-    const f32x4 v = load_shared4(rml, (k * group + hh) * 16);
-    const float m = live ? v[0] : -INFINITY;
-    const float M = row16_max(m);
-    const float e = live ? exp2f(m - M) : 0.f;  // 0 for an empty slot
-    float den = e * v[1];
-    den += row_ror<8>(den);
-    den += row_ror<4>(den);
-    den += row_ror<2>(den);
-    den += row_ror<1>(den);
-    if (live) ms.w[hh][k] = e / den;
+  // general case (group 16, or more than 16 slots): the weights first, then
+  // the partials in small chunks (so that only one chunk of registers is
+  // ever live)
+  if (top_k <= 16) {  // uniform
+    row_weights(load_shared4(rml, ((tid & 15) * group + (tid >> 4)) * 16), top_k, group, ms);
   } else {
     for (int x = tid; x < group * top_k; x += 256) {
       const int hh = x / top_k, k = x - hh * top_k;
@@ -297,20 +317,6 @@ __device__ __forceinline__ void merge_partials(__amdgpu_buffer_rsrc_t ro, __amdg
     }
   }
   __syncthreads();
-  if (single) {
-    if (tid >= items) return;
-    const int h = tid >> 5, d4 = tid & 31;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < kChunk; ++k) {
-      const float w = k < top_k ? ms.w[h][k] : 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = fmaf(w, o[k][j], acc[j]);
-    }
-    *reinterpret_cast<f32x4*>(out_sg + (size_t)h * 128 + 4 * d4) = acc;
-    return;
-  }
-  // general case (group 16, or more than 16 slots): small chunks
   constexpr int kLoopChunk = 4;
   for (int it = tid; it < items; it += 256) {
     const int h = it >> 5, d4 = it & 31;
