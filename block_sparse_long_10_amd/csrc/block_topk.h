@@ -123,13 +123,18 @@ template <int MAXV>
 struct RegKeys {
   float val[MAXV];
   int n;
+  // (every load is issued: slots past the row read its last score, or the
+  // row's first entry when it is empty, and are then set to -inf; a load
+  // under a branch per slot made the loads trickle out one by one)
   __device__ __forceinline__ void load(const float* __restrict__ s, int n_) {
     n = n_;
     const int tid = threadIdx.x;
+    const int last = n > 0 ? n - 1 : 0;
 #pragma unroll
     for (int j = 0; j < MAXV; ++j) {
       const int i = j * kTopkThreads + tid;
-      val[j] = i < n ? s[i] : -INFINITY;
+      const float v = s[min(i, last)];
+      val[j] = i < n ? v : -INFINITY;
     }
   }
 };
