@@ -115,8 +115,9 @@ def test_decode_shape_variants(shape):
 # The selection's register tiers switch on the longest row of the batch
 # (max_seq_len): the fused TopK keeps 4 scores per thread up to 1024 ranked
 # blocks and 32 above; the separate TopK launch (more than 1024 slot
-# workgroups) keeps 16 up to 4096 blocks and 32 above.  Each edge from both
-# sides, beside short rows of the same batch.
+# workgroups) keeps 16 up to 4096 blocks and 32 above; past 8192 blocks
+# both re-read the scores from memory (the general path).  Each edge from
+# both sides, beside short rows of the same batch.
 EDGE_FUSED = Shape(num_q_heads=8, num_kv_heads=2, num_idx_heads=4, block_size=64, top_k=8)
 EDGE_SPLIT = Shape(num_q_heads=8, num_kv_heads=2, num_idx_heads=2, block_size=64, top_k=64)
 
@@ -126,6 +127,9 @@ EDGE_SPLIT = Shape(num_q_heads=8, num_kv_heads=2, num_idx_heads=2, block_size=64
     (EDGE_FUSED, 1025, [3000, 65], 112),
     (EDGE_SPLIT, 4096, [1, 64, 65, 5000, 30000, 65600, 9000, 129], 113),
     (EDGE_SPLIT, 4097, [1, 64, 65, 5000, 30000, 65600, 9000, 129], 114),
+    (EDGE_FUSED, 8192, [3000, 1], 115),
+    (EDGE_FUSED, 8193, [3000, 65], 116),
+    (EDGE_SPLIT, 8193, [1, 64, 65, 5000, 30000, 65600, 9000, 129], 117),
 ])
 def test_decode_selection_tier_edges(shape, own, others, seed):
     lengths = [own * shape.block_size + 1] + others
