@@ -916,6 +916,57 @@ def summarize_mfma(counter_csv, out_txt, command):
     print("\n".join(lines))
 
 
+def summarize_instruction_mix(csv_a, csv_b, out_txt, command):
+    """Per-wave instruction mix of the MSA kernels of --mfma-probe from two
+    rocprofv3 counter passes (SQ counters; one dispatch each): waves, vector
+    instructions other than MFMA, MFMA, transcendental (fp32) and LDS
+    instructions per wave and per MFMA, LDS bank-conflict cycles per LDS
+    active cycle, and the MFMA busy fraction.  SQ_INSTS_VALU counts the MFMA
+    instructions too (the issue loop reads them one for one), so they are
+    subtracted."""
+    import csv
+    n_xcc, n_simd = 8, 1024
+    agent_csv = os.path.join(os.path.dirname(csv_a), "run_agent_info.csv")
+    if os.path.exists(agent_csv):
+        for r in csv.DictReader(open(agent_csv)):
+            if r.get("Name", "").startswith("gfx"):
+                n_xcc, n_simd = int(r["Num_Xcc"]), int(r["Simd_Count"])
+    rows = {}
+    for path in (csv_a, csv_b):
+        for r in csv.DictReader(open(path)):
+            if "msa::" not in r["Kernel_Name"]:
+                continue
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("msa::", "")
+            d = rows.setdefault(name, {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    lines = ["rocprofv3 SQ counters: instruction mix per wave (one dispatch of each kernel)", "",
+             "commands (two counter passes of the same program):", "  " + command, "",
+             "valu = SQ_INSTS_VALU - SQ_INSTS_MFMA (vector instructions other than MFMA); "
+             "trans = SQ_INSTS_VALU_TRANS_F32; lds = SQ_INSTS_LDS;",
+             "conflict = SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS; MFMA busy = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / %d XCDs x %d SIMDs)" % (n_xcc, n_simd),
+             "",
+             "%-36s %8s %9s %8s %8s %8s %8s %9s %9s %7s" % (
+                 "kernel", "waves", "valu/wv", "mfma/wv", "valu/mf", "trans/mf", "lds/mf",
+                 "salu/wv", "conflict", "busy %")]
+    for name, d in sorted(rows.items()):
+        waves = max(1.0, d.get("SQ_WAVES", 0.0))
+        mfma = d.get("SQ_INSTS_MFMA", 0.0)
+        valu = d.get("SQ_INSTS_VALU", 0.0) - mfma
+        per_mf = (lambda x: "%8.2f" % (x / mfma)) if mfma > 0 else (lambda x: "%8s" % "-")
+        lds_act = d.get("SQ_ACTIVE_INST_LDS", 0.0)
+        conflict = d.get("SQ_LDS_BANK_CONFLICT", 0.0) / lds_act if lds_act > 0 else 0.0
+        active = d.get("GRBM_GUI_ACTIVE", 0.0) / n_xcc
+        busy = 100.0 * d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / max(1.0, active * n_simd)
+        lines.append("%-36s %8d %9.0f %8.0f %s %s %s %9.0f %9.3f %7.1f" % (
+            name[:36], waves, valu / waves, mfma / waves, per_mf(valu),
+            per_mf(d.get("SQ_INSTS_VALU_TRANS_F32", 0.0)), per_mf(d.get("SQ_INSTS_LDS", 0.0)),
+            d.get("SQ_INSTS_SALU", 0.0) / waves, conflict, busy))
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_kernel_trace(trace_csv, out_txt, command):
     """Write a short text summary of a rocprofv3 --kernel-trace run: per MSA
     kernel and launch grid (workgroups x, y, z), the dispatch count and the
@@ -1033,6 +1084,9 @@ def main():
                     help="write the profiles/ summary of a rocprofv3 --stats run")
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("COUNTER_CSV", "OUT_TXT", "CMD"),
                     help="write the profiles/ summary of an MFMA counter run")
+    ap.add_argument("--summarize-instruction-mix", nargs=4,
+                    metavar=("COUNTER_CSV_A", "COUNTER_CSV_B", "OUT_TXT", "CMD"),
+                    help="write the profiles/ instruction-mix summary of two SQ counter runs")
     ap.add_argument("--mfma-probe", action="store_true",
                     help="for rocprofv3 counter runs: the MFMA issue loop (calibration), then "
                          "one index, TopK and attention launch of the 1M prefill; no timing")
@@ -1052,6 +1106,9 @@ def main():
         return
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma)
+        return
+    if args.summarize_instruction_mix:
+        summarize_instruction_mix(*args.summarize_instruction_mix)
         return
     if args.summarize_kernel_stats:
         summarize_kernel_stats(*args.summarize_kernel_stats)

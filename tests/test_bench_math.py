@@ -115,6 +115,27 @@ def test_traffic_summary_scales_by_the_copy(tmp_path):
     assert t["kernel_source_hash"] == bench.kernel_source_hash()
 
 
+def test_instruction_mix_summary_subtracts_mfma_from_valu(tmp_path):
+    a, b, out = tmp_path / "a.csv", tmp_path / "b.csv", tmp_path / "mix.txt"
+    k = "void msa::prefill_attn_kernel<128, true>(...)"
+    # two waves: 100 vector instructions of which 20 MFMA; 10 transcendental,
+    # 30 LDS; 5 conflict cycles over 50 LDS active cycles
+    with open(a, "w") as f:
+        f.write('"Kernel_Name","Counter_Name","Counter_Value"\n')
+        for c, v in [("SQ_INSTS_VALU", 100.0), ("SQ_INSTS_LDS", 30.0),
+                     ("SQ_LDS_BANK_CONFLICT", 5.0), ("SQ_ACTIVE_INST_LDS", 50.0)]:
+            f.write('"%s","%s",%r\n' % (k, c, v))
+    with open(b, "w") as f:
+        f.write('"Kernel_Name","Counter_Name","Counter_Value"\n')
+        for c, v in [("SQ_INSTS_MFMA", 20.0), ("SQ_INSTS_VALU_TRANS_F32", 10.0),
+                     ("SQ_WAVES", 2.0), ("SQ_INSTS_SALU", 8.0)]:
+            f.write('"%s","%s",%r\n' % (k, c, v))
+    bench.summarize_instruction_mix(str(a), str(b), str(out), "cmd")
+    row = [l for l in open(out) if l.startswith("prefill_attn_kernel<128, true>")][0].split()
+    # waves, valu/wave, mfma/wave, valu/mfma, trans/mfma, lds/mfma, salu/wave, conflict, busy
+    assert row[-9:] == ["2", "40", "10", "4.00", "0.50", "1.50", "4", "0.100", "0.0"]
+
+
 def test_traffic_figure_is_dropped_when_the_kernel_source_changed(tmp_path, monkeypatch):
     f = tmp_path / "t.json"
     json.dump({"kernel_source_hash": bench.kernel_source_hash(), "hbm_bytes_per_launch": 5}, open(f, "w"))
