@@ -58,6 +58,44 @@ def test_decode_noalloc_matches_decode_twice_shrinking():
         check_out(out, oracle.attend_decode(case, sel, prepared=P))
 
 
+def test_decode_noalloc_replays_in_a_graph():
+    """Captured in a HIP graph (the callers it is for), then replayed three
+    times; between the replays, eager work and an eager msa_decode_noalloc
+    on another input, which leaves its own contents in the shared scratch.
+    Every replay equals the eager call bit for bit."""
+    print("\n[gpu noalloc] graph capture and replays", flush=True)
+    sys.stdout.flush()
+    shape = Shape(num_q_heads=16, num_kv_heads=2, num_idx_heads=4, block_size=64, top_k=8)
+    case = make_decode_case(shape, [9000, 777, 1, 4097], 154, device=DEV, shuffle_pages=True,
+                            poison_frac=0.02)
+    other = make_decode_case(GQA64, [70001, 3000], 155, device=DEV, shuffle_pages=True)
+    ref_out, ref_sel = _noalloc(case)
+    sh = case.shape
+    out = torch.full((case.batch, sh.num_q_heads, sh.head_dim), float("nan"), device=DEV)
+    sel = torch.full((case.batch, sh.num_kv_heads, sh.top_k), -7, dtype=torch.int32, device=DEV)
+    p, kv = params_of(sh), kv_of(case)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            msa.msa_decode_noalloc(p, kv, case.q, case.idx_q, case.seq_lens, case.batch,
+                                   max(case.lengths), out, sel)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        sel.fill_(-7)
+        _noalloc(other)  # the scratch now holds another call's contents
+        junk = torch.randn(1 << 20, device=DEV).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(sel.cpu().numpy(), ref_sel, err_msg="replay %d" % rep)
+        assert np.array_equal(out.cpu().numpy().astype(np.float64), ref_out), "replay %d" % rep
+        assert torch.isfinite(junk)
+
+
 def test_decode_noalloc_rejects_beyond_the_static_scratch():
     sh = GQA64
     case = make_decode_case(sh, [300], 153, device=DEV)
