@@ -1060,8 +1060,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--rotate", type=int, default=4, help="decode buffer sets")
-    ap.add_argument("--prefill-steps", type=int, default=5)
-    ap.add_argument("--prefill-warmup", type=int, default=2)
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--prefill-warmup", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--layers", type=int, default=60,
                     help="layers of the multi-layer decode leg (0 = skip)")
