@@ -641,17 +641,23 @@ def practical_peaks(torch):
 
 
 def cpu_model():
-    """The host CPU's model name and logical core count."""
-    name = "unknown"
+    """The host CPU's model name, family/model numbers (which identify the
+    generation where the name is generic) and logical core count."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    name = line.split(":", 1)[1].strip()
-                    break
+                if not line.strip():
+                    break  # the first processor's entry is enough
+                key, _, val = line.partition(":")
+                info.setdefault(key.strip(), val.strip())
     except OSError:
         pass
-    return "%s (%d logical cores on the host)" % (name, os.cpu_count() or 0)
+    name = info.get("model name", "unknown")
+    fam = ("family %s model %s" % (info["cpu family"], info["model"])
+           if "cpu family" in info and "model" in info else None)
+    return "%s (%s%d logical cores on the host)" % (name, fam + ", " if fam else "",
+                                                    os.cpu_count() or 0)
 
 
 def cpu_baseline(case, budget_s, workload=None):
