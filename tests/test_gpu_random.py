@@ -1,7 +1,8 @@
 """Seeded random configurations of the whole path on the GPU, each against the
 oracle through the C ABI: group sizes, index heads, block size, k, forced sink
-and local blocks, shared or per-group index keys, ragged lengths (decode) and
-prior / chunk positions (prefill), paged and poisoned caches.  The draws are
+and local blocks, shared or per-group index keys, ragged lengths (decode),
+prior / chunk positions (prefill) and batches of them (batched prefill), paged
+and poisoned caches.  The draws are
 fixed by the seeds, so every run checks the same configurations.  Marked gpu."""
 import random
 import sys
@@ -9,8 +10,9 @@ import sys
 import pytest
 
 import oracle
-from msa_inputs import Shape, make_decode_case, make_prefill_case
+from msa_inputs import Shape, make_decode_case, make_prefill_case, make_varlen_prefill_case
 from tests.gpu_util import check_out, check_pooled, check_selection, run_decode, run_prefill
+from tests.test_gpu_varlen import run_varlen
 
 pytestmark = pytest.mark.gpu
 
@@ -80,4 +82,40 @@ def test_random_prefill(seed):
             check_selection(g["sel"][t, gi], ref["pooled"][t, gi], own, shape.top_k,
                             sink=shape.sink_blocks, local=shape.local_blocks)
     worst = check_out(g["out"], oracle.attend_prefill(case, g["sel"], prepared=P))
+    print("worst row err %.3g" % worst)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_varlen(seed):
+    """msa_prefill_varlen over 1-6 sequences of random prior and chunk
+    lengths (empty priors and one-token chunks among them), each sequence's
+    selections and outputs against the oracle run on that sequence alone."""
+    rng = random.Random(3000 + seed)
+    shape = random_shape(rng, prefill=True)
+    n = rng.randint(1, 6)
+    priors = [rng.choice([0, rng.randint(1, 600), rng.randint(600, 7000)]) for _ in range(n)]
+    chunks = [rng.choice([1, rng.randint(2, 150), rng.randint(150, 500)]) for _ in range(n)]
+    _announce("varlen seed %d %s priors %s chunks %s" % (seed, shape, priors, chunks))
+    case = make_varlen_prefill_case(shape, priors, chunks, 7000 + seed, device=DEV,
+                                    shuffle_pages=True, poison_frac=0.05)
+    out, sel = run_varlen(case)
+    out, sel = out.cpu().numpy().astype("float64"), sel.cpu().numpy()
+    B = shape.block_size
+    worst, t0 = 0.0, 0
+    for s in range(n):
+        one = case.sequence(s)
+        P = oracle.prepare(one)
+        ref = oracle.prefill(one, prepared=P)
+        nt = one.num_tiles
+        my_sel = sel[t0:t0 + nt]
+        t0 += nt
+        for t in range(nt):
+            own = one.prior_len // B + t
+            for gi in range(shape.num_kv_heads):
+                check_selection(my_sel[t, gi], ref["pooled"][t, gi], own, shape.top_k,
+                                sink=shape.sink_blocks, local=shape.local_blocks)
+        q0 = case.q_start[s]
+        worst = max(worst, check_out(out[q0:q0 + one.chunk_len],
+                                     oracle.attend_prefill(one, my_sel, prepared=P),
+                                     "sequence %d" % s))
     print("worst row err %.3g" % worst)
