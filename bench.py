@@ -747,7 +747,7 @@ def traffic_probe(args, torch, msa, mi, gu):
     log("[bench] traffic probe done; kernel source hash %s" % kernel_source_hash())
 
 
-TIMELINE_WORKLOADS = ["decode_b1_L1M", "decode_b8_L128k", "decode_b1_L4k"]
+TIMELINE_WORKLOADS = ["decode_b1_L1M", "decode_b8_L128k", "decode_b1_L4k", "decode_paged_b32"]
 TIMELINE_LABELS = {
     "index_end": "last decode index workgroup ends",
     "start": "watched attention workgroup starts",
